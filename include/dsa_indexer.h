@@ -1,0 +1,189 @@
+/*
+ * dsa_indexer.h -- C ABI of the DeepSeek Sparse Attention (DSA) indexer hot path on MI355X
+ * (gfx950): store compressed index keys into a paged cache, score queries against every causally
+ * visible key, select the top-k keys per query.
+ *
+ * The operation is the indexer the four DSA-indexer blog pages describe:
+ *  - "When the Fused Kernel Isn't Enough", Input Knowledge Required: a store path writes compressed
+ *    keys, a read path loads them and computes logits; an fp8 key is 128 B of codes + a 4 B scale
+ *    (132 B/token), a bf16 key is 256 B/token.
+ *  - "The Moment of Validation", Input Knowledge Required: the fused store normalises, applies RoPE
+ *    and writes the cache; fp8 keys share one scale per group (here: per key).
+ *  - "The Crash That Changed Direction", Experiment and Assumptions: the scores are a batched q.k
+ *    product followed by ReLU over the head dimension, then top-k; fp8 keys are e4m3 and widen
+ *    exactly to bf16 before the product.
+ *  - "The Fused Kernel Decision", Message and Assumptions: the cache is paged, 64 keys per page,
+ *    [npages, 64*128]; a key maps to (page, offset); q and k share one element order.
+ *  - "When the Fused Kernel Isn't Enough", Message and Why This Message Matters: materialising the
+ *    full per-head logits tensor is what ran out of memory at 22K tokens; this library never does.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" are device (HBM) memory the caller owns; the library never allocates
+ *    or frees device memory and keeps no state between calls.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream) without a host
+ *    synchronisation.  The return value reports host-side argument validation and launch errors;
+ *    a fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - Integers inside device arrays are read as given; out-of-range values never cause an
+ *    out-of-bounds access (see each entry point for what they do instead).
+ *  - head_dim is 128, n_heads is 64, 64 keys per page, 4 tokens per compressed key.
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IDX_ABI_VERSION 1
+#define IDX_HEAD_DIM 128
+#define IDX_N_HEADS 64
+#define IDX_PAGE_KEYS 64
+#define IDX_COMPRESS_RATIO 4
+#define IDX_MAX_TOPK 2048
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_EINVAL = 1,        /* a null pointer, negative size or out-of-range scalar argument */
+  IDX_EUNSUPPORTED = 2,  /* a valid but unsupported configuration (n_heads != 64, dtype) */
+  IDX_EWORKSPACE = 3,    /* the workspace is smaller than one query row needs */
+  IDX_EHIP = 4           /* a HIP launch returned an error */
+} idx_status;
+
+typedef enum {
+  IDX_KV_FP8_E4M3 = 0,   /* page = 64 x 128 e4m3fn codes, then 64 fp32 scales: 8448 B */
+  IDX_KV_BF16 = 1        /* page = 64 x 128 bf16: 16384 B */
+} idx_kv_dtype;
+
+/* IDX_ABI_VERSION of the built library. */
+int idx_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* idx_status_string(int status);
+
+/* Bytes of one cache page for `dtype` (8448 for fp8, 16384 for bf16), 0 for an unknown dtype.
+ * Per key: 128 code bytes + a 4 B fp32 scale, or 256 bf16 bytes ("When the Fused Kernel Isn't
+ * Enough", Input Knowledge Required).  Inside an fp8 page the 64 code rows come first (16 B
+ * aligned for vector loads), then the 64 scales. */
+size_t idx_page_bytes(int dtype);
+
+/*
+ * S1 -- fused RMSNorm + RoPE + quantise + paged store of compressed index keys ("The Moment of
+ * Validation", Input Knowledge Required; "The Fused Kernel Decision", Message).
+ *
+ * For each input row n (key s = key_idx[n] of sequence b = key_seq[n]):
+ *   y   = x[n] / sqrt(mean(x[n]^2) + eps) * gamma           (fp64 inside the kernel)
+ *   rotate dims (64+2j, 65+2j), j = 0..31, by angle 4*s * inv_freq_j,
+ *       inv_freq_j = fp32(10000^(-2j/64))                    (RoPE position = first token, 4s)
+ *   k32 = y rounded once to fp32
+ *   bf16: code_i = RNE bf16 of k32_i
+ *   fp8:  scale = fp32(max_i |k32_i| / 448); code_i = e4m3fn RNE, saturating, of fp32(k32_i/scale);
+ *         an all-zero key stores scale 0 and codes 0
+ * and writes the key to slot s % 64 of page page_table[b * max_pages + s / 64] of `kcache`.
+ *
+ * x          device fp32 [n_keys, 128], row-major
+ * gamma      device fp32 [128]
+ * eps        RMSNorm epsilon (added to the mean square)
+ * key_idx    device int32 [n_keys]
+ * key_seq    device int32 [n_keys], or NULL: every key belongs to sequence 0
+ * page_table device int32 [n_seq, max_pages]; -1 = no page
+ * kcache     device, n_pages_pool * idx_page_bytes(dtype) bytes; only the addressed slots (and, for
+ *            fp8, their scale words) are written
+ * Rows whose sequence, key index (>= max_pages * 64) or page id (outside [0, n_pages_pool)) is out
+ * of range are skipped.  Two rows that address the same slot race.  n_keys == 0 is a no-op.
+ * Errors: IDX_EINVAL (null pointer with n_keys > 0, n_keys/n_seq/max_pages/n_pages_pool < 0 or
+ * eps < 0), IDX_EUNSUPPORTED (unknown dtype), IDX_EHIP.
+ */
+int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t* key_idx,
+                   const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
+                   int32_t n_seq, int32_t max_pages, int dtype, void* kcache,
+                   int64_t n_pages_pool, void* stream);
+
+/*
+ * Bytes of workspace idx_logits_topk uses for a call of this shape when the caller wants all
+ * queries scored in one pass.  Any workspace of at least idx_logits_topk_min_workspace() bytes
+ * works: the call then processes the queries in chunks that fit.  The bound never depends on
+ * n_heads: per-head logits are never materialised.
+ */
+size_t idx_logits_topk_workspace_size(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t k);
+size_t idx_logits_topk_min_workspace(int32_t n_seq, int32_t max_pages, int32_t k);
+
+/*
+ * S2 + S3 -- score every query against every causally visible key and select the top-k
+ * ("The Crash That Changed Direction", Input Knowledge Required and Pivot; top-k 512 and 1024,
+ * "The Crash That Changed Direction", Context).
+ *
+ * Queries of sequence b are its last q_len_b = cu_q[b+1] - cu_q[b] tokens: row i of q with
+ * cu_q[b] <= i < cu_q[b+1] sits at token t = seq_lens[b] - q_len_b + (i - cu_q[b]) and sees keys
+ * s < n_vis = min(floor((t+1)/4), max_pages*64) (key s covers tokens 4s..4s+3; t < 0 sees none).
+ *   logit(i, s) = sum_h w[i,h] * max(0, sum_d q[i,h,d] * k[s,d])
+ * with k the stored key (bf16, or e4m3 code * scale), computed with fp32 accumulation.
+ * out_idx[i, :] receives the k keys s with the largest logits (ties to the lower s) in increasing
+ * s order, then -1 padding when n_vis < k; out_val (optional) their logits, -inf for padding.
+ * Keys whose page id lies outside [0, n_pages_pool) score -inf.
+ *
+ * q          device bf16 [n_q, 64, 128]
+ * w          device fp32 [n_q, 64]
+ * kcache     device pool as written by idx_store_keys with the same dtype
+ * page_table device int32 [n_seq, max_pages]
+ * seq_lens   device int32 [n_seq]
+ * cu_q       device int32 [n_seq + 1], non-decreasing, cu_q[0] = 0, cu_q[n_seq] = n_q
+ *            (a row outside every [cu_q[b], cu_q[b+1]) sees no key)
+ * out_idx    device int32 [n_q, k];  out_val device fp32 [n_q, k] or NULL
+ * workspace  device, workspace_bytes >= idx_logits_topk_min_workspace(...)
+ * Errors: IDX_EINVAL (null pointer, n_q/n_seq/max_pages/n_pages_pool < 0, k < 1 or
+ * k > IDX_MAX_TOPK), IDX_EUNSUPPORTED (n_heads != 64, unknown dtype), IDX_EWORKSPACE, IDX_EHIP.
+ */
+int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype,
+                    int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                    int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                    int32_t n_heads, int32_t k, int32_t* out_idx, float* out_val,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * idx_logits_topk with instrumentation: `ev_score_begin` / `ev_score_end` (hipEvent_t, either may
+ * be NULL) are recorded on `stream` right before the first and right after the last launch of the
+ * scoring kernel, so a caller can time that kernel alone.  Results are identical.
+ */
+int idx_logits_topk_timed(const void* q, const float* w, const void* kcache, int dtype,
+                          int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                          int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q,
+                          int64_t n_q, int32_t n_heads, int32_t k, int32_t* out_idx,
+                          float* out_val, void* workspace, size_t workspace_bytes,
+                          void* ev_score_begin, void* ev_score_end, void* stream);
+
+/*
+ * S2 alone, for checking: out_logits[i, s] (device fp32 [n_q, max_keys], row stride max_keys)
+ * receives logit(i, s) for visible s < max_keys and -inf for every other s < max_keys.  Uses the
+ * same scoring kernel as idx_logits_topk, so its values are bit-identical to the ones top-k
+ * selects from.  Materialises the head-reduced [n_q, max_keys] matrix; never the per-head one.
+ * Arguments and errors as idx_logits_topk; max_keys < 1 is IDX_EINVAL.
+ */
+int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtype,
+                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                     int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                     int32_t n_heads, float* out_logits, int32_t max_keys, void* stream);
+
+/*
+ * S3 alone: top-k of each row of a score matrix ("The Crash That Changed Direction", Context and
+ * Pivot: the top-k op over indexer logits, k = 512 or 1024).
+ *
+ * scores   device fp32 [n_rows, row_stride]; row r holds row_len[r] candidates (clamped to
+ *          [0, row_stride]; row_len NULL = row_stride each).  Values must not be NaN; -0 and +0
+ *          compare equal.
+ * out_idx  device int32 [n_rows, k]: the column indices of the k largest values (ties to the lower
+ *          index) in increasing index order, then -1; out_val (optional) device fp32 [n_rows, k]
+ *          their values, then -inf.
+ * Errors: IDX_EINVAL (null pointer, n_rows < 0, row_stride < 1, k < 1 or k > IDX_MAX_TOPK),
+ * IDX_EHIP.
+ */
+int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const int32_t* row_len,
+                  int32_t k, int32_t* out_idx, float* out_val, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_H */

@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Each pin raises AssertionError on failure.  They use closed forms, library routines (torch's CPU
+float8_e4m3fn / bfloat16 casts, numpy complex arithmetic, matrix products, stable argsort) on
+special cases that reduce to them, invariants of the method (scale invariance of RMSNorm, rotation
+by RoPE, ReLU(d) + ReLU(-d) = |d|), brute force on tiny inputs, and the sizes the DSA indexer pages
+print (tests/golden/layout.txt).  ``ALL_PINS`` is also run with planted mistakes in the oracle to
+show that each mistake trips at least one pin.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+D, H, PAGE = 128, 64, 64
+FP8, BF16 = oracle.FP8, oracle.BF16
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(i):
+    return np.random.default_rng([7777, i])
+
+
+def _torch_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def _torch_bf16_bits(v: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_to_f64(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _store_rows(x, s, gamma=None, eps=1e-6, dtype=BF16):
+    """Store rows of x at logical positions s of one sequence; return (pool, k32, page_table)."""
+    x = np.asarray(x, np.float32)
+    s = np.asarray(s, np.int32)
+    gamma = np.ones(D, np.float32) if gamma is None else np.asarray(gamma, np.float32)
+    max_pages = int(s.max()) // PAGE + 1
+    pt = np.arange(max_pages, dtype=np.int32)[None, :]
+    pool = oracle.new_pool(max_pages, dtype)
+    skipped, k32 = oracle.store_keys(x, gamma, eps, s, None, pt, dtype, pool, want_k32=True)
+    assert skipped == 0
+    return pool, k32, pt
+
+
+def _pool_keys(pool, pt, dtype, b, n):
+    """Decode keys 0..n-1 of sequence b from a pool with torch's casts (an independent decoder)."""
+    pb = oracle.page_bytes(dtype)
+    out = np.zeros((n, D))
+    for s in range(n):
+        page = pt[b, s // PAGE]
+        base = page * pb
+        slot = s % PAGE
+        if dtype == BF16:
+            raw = pool[base + slot * 256: base + slot * 256 + 256].view(np.uint16)
+            out[s] = _bf16_to_f64(raw)
+        else:
+            codes = pool[base + slot * D: base + slot * D + D]
+            scale = pool[base + PAGE * D + 4 * slot: base + PAGE * D + 4 * slot + 4].view(np.float32)[0]
+            out[s] = _torch_e4m3_to_f64(codes) * float(scale)
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# Layout sizes printed on the pages
+# ------------------------------------------------------------------------------------------------
+
+def pin_layout_sizes():
+    vals = {}
+    with open(os.path.join(GOLDEN, "layout.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = int(v)
+    assert oracle.page_bytes(FP8) == vals["page_keys"] * vals["fp8_bytes_per_token"] == 8448
+    assert oracle.page_bytes(BF16) == vals["page_keys"] * vals["bf16_bytes_per_token"] == 16384
+    assert vals["bf16_bytes_per_token"] == 2 * vals["head_dim"]
+    assert vals["fp8_bytes_per_token"] == vals["head_dim"] + 4
+
+
+# ------------------------------------------------------------------------------------------------
+# Number formats
+# ------------------------------------------------------------------------------------------------
+
+def pin_e4m3_decode_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = _torch_e4m3_to_f64(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+
+
+def pin_e4m3_roundtrip_and_midpoints():
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    dec = oracle.e4m3_decode(np.array(finite, np.uint8)).astype(np.float32)
+    enc = oracle.e4m3_encode(dec)
+    # -0.0 decodes to -0.0 and must come back as 0x80; everything else round-trips
+    assert np.array_equal(enc, np.array(finite, np.uint8))
+    mags = oracle.e4m3_decode(np.arange(127, dtype=np.uint8))
+    assert np.all(np.diff(mags) > 0)
+    mid = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)        # exact: <= 5 significant bits
+    assert np.array_equal(mid.astype(np.float64), (mags[:-1] + mags[1:]) / 2)
+    got = oracle.e4m3_encode(mid)
+    lo = np.arange(126)
+    want = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    assert np.array_equal(got, want), "midpoints must round to the even code"
+    got_neg = oracle.e4m3_encode(-mid)
+    assert np.array_equal(got_neg, want | 0x80)
+    # just off the midpoints the nearest value wins
+    up = np.nextafter(mid, np.float32(np.inf))
+    dn = np.nextafter(mid, np.float32(0))
+    assert np.array_equal(oracle.e4m3_encode(up), (lo + 1).astype(np.uint8))
+    assert np.array_equal(oracle.e4m3_encode(dn), lo.astype(np.uint8))
+
+
+def pin_e4m3_vs_torch_sweep():
+    r = _rng(1)
+    v = np.concatenate([
+        r.uniform(-448, 448, 4000),
+        r.standard_normal(4000) * 10.0,
+        np.exp(r.uniform(np.log(1e-4), np.log(448), 4000)) * r.choice([-1, 1], 4000),
+        np.linspace(-0.02, 0.02, 2001),                  # subnormal region, exact ties included
+    ]).astype(np.float32)
+    ours = oracle.e4m3_encode(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def pin_e4m3_saturation_and_zero():
+    big = np.array([448.0, 448.001, 463.9, 464.0, 500.0, 1e6, 3.4e38], np.float32)
+    assert np.all(oracle.e4m3_encode(big) == 0x7E)
+    assert np.all(oracle.e4m3_encode(-big) == 0xFE)
+    tiny = np.array([2.0 ** -11, 1e-10, 0.0], np.float32)    # round to zero
+    assert np.all(oracle.e4m3_encode(tiny) == 0x00)
+    assert np.all(oracle.e4m3_encode(-tiny) == 0x80)
+    assert oracle.e4m3_encode(np.array([2.0 ** -9], np.float32))[0] == 0x01
+    assert oracle.e4m3_encode(np.array([2.0 ** -6], np.float32))[0] == 0x08
+
+
+def pin_bf16_vs_torch():
+    r = _rng(2)
+    v = np.concatenate([
+        r.standard_normal(20000),
+        np.exp(r.uniform(-80, 80, 20000)) * r.choice([-1, 1], 20000),
+    ]).astype(np.float32)
+    # exact ties: fp32 patterns whose low 16 bits are 0x8000
+    ties = (r.integers(0, 2 ** 15, 4000, dtype=np.uint32) << 16 | 0x8000
+            | (r.integers(0, 2, 4000, dtype=np.uint32) << 31)) & 0xFE7FFFFF
+    v = np.concatenate([v, ties.astype(np.uint32).view(np.float32)])
+    v = v[np.isfinite(v)]
+    assert np.array_equal(oracle.bf16_encode(v), _torch_bf16_bits(v))
+
+
+# ------------------------------------------------------------------------------------------------
+# S1: RMSNorm, RoPE, quantisation
+# ------------------------------------------------------------------------------------------------
+
+def pin_rmsnorm_unit_rms():
+    x = _rng(3).standard_normal((16, D)).astype(np.float32)
+    _, k32, _ = _store_rows(x, np.zeros(16), eps=0.0)
+    rms = np.sqrt(np.mean(k32.astype(np.float64) ** 2, axis=1))
+    assert np.all(np.abs(rms - 1.0) < 2e-7), rms
+
+
+def pin_rmsnorm_scale_and_gamma():
+    r = _rng(4)
+    x = r.standard_normal((8, D)).astype(np.float32)
+    g = (1 + 0.1 * r.standard_normal(D)).astype(np.float32)
+    s = np.array([0, 1, 5, 100, 999, 4000, 20000, 32767])
+    _, a, _ = _store_rows(x, s, gamma=g, eps=0.0)
+    _, b, _ = _store_rows(2 * x, s, gamma=g, eps=0.0)
+    _, c, _ = _store_rows(x, s, gamma=2 * g, eps=0.0)
+    assert np.array_equal(a, b), "RMSNorm output must not depend on the scale of x"
+    assert np.array_equal(c, 2 * a), "the output must be linear in gamma"
+
+
+def _inv_freq_np():
+    return np.power(10000.0, -np.arange(0, 64, 2) / 64.0).astype(np.float32)
+
+
+def pin_rope_inv_freq():
+    assert np.array_equal(oracle.rope_inv_freq(), _inv_freq_np())
+
+
+def pin_rope_complex_rotation():
+    r = _rng(5)
+    x = np.repeat(r.standard_normal((1, D)).astype(np.float32), 6, axis=0)
+    s = np.array([0, 1, 7, 1000, 20000, 32767])
+    _, k32, _ = _store_rows(x, s)
+    k = k32.astype(np.float64)
+    assert np.array_equal(k32[1:, :64], np.repeat(k32[:1, :64], 5, axis=0)), \
+        "dims 0..63 are not rotated"
+    z0 = k[0, 64::2] + 1j * k[0, 65::2]
+    for row, pos in enumerate(s):
+        ang = 4.0 * pos * _inv_freq_np().astype(np.float64)
+        z = z0 * np.exp(1j * ang)
+        got = k[row, 64::2] + 1j * k[row, 65::2]
+        assert np.all(np.abs(got - z) <= 4e-7 * np.abs(z0) + 1e-12), (pos, np.abs(got - z).max())
+
+
+def pin_rope_relative_position():
+    """<R_m a, R_n b> depends only on m - n (rotated halves)."""
+    r = _rng(6)
+    a = r.standard_normal(D).astype(np.float32)
+    b = r.standard_normal(D).astype(np.float32)
+    x = np.stack([a, b, a, b])
+    s = np.array([10, 3, 1010, 1003])
+    _, k32, _ = _store_rows(x, s, eps=0.0)
+    k = k32.astype(np.float64)
+    d1 = k[0, 64:] @ k[1, 64:]
+    d2 = k[2, 64:] @ k[3, 64:]
+    assert abs(d1 - d2) < 2e-5 * (1 + abs(d1)), (d1, d2)
+
+
+def pin_bf16_store_vs_torch():
+    x = _rng(7).standard_normal((40, D)).astype(np.float32)
+    s = np.arange(40) * 3
+    pool, k32, pt = _store_rows(x, s, dtype=BF16)
+    pb = oracle.page_bytes(BF16)
+    for i, si in enumerate(s):
+        base = pt[0, si // PAGE] * pb + (si % PAGE) * 256
+        assert np.array_equal(pool[base:base + 256].view(np.uint16), _torch_bf16_bits(k32[i]))
+
+
+def pin_fp8_store_scale_and_bound():
+    x = _rng(8).standard_normal((40, D)).astype(np.float32)
+    s = np.arange(40) * 2 + 1
+    pool, k32, pt = _store_rows(x, s, dtype=FP8)
+    pb = oracle.page_bytes(FP8)
+    for i, si in enumerate(s):
+        base = pt[0, si // PAGE] * pb
+        codes = pool[base + (si % PAGE) * D: base + (si % PAGE) * D + D]
+        scale = float(pool[base + PAGE * D + 4 * (si % PAGE):][:4].view(np.float32)[0])
+        amax = float(np.abs(k32[i]).max())
+        assert abs(scale * 448.0 - amax) <= amax * 2 ** -23
+        assert np.max(codes & 0x7F) == 0x7E, "the largest element must map to +-448"
+        deq = _torch_e4m3_to_f64(codes) * scale
+        err = np.abs(deq - k32[i].astype(np.float64))
+        bound = 2.0 ** -4 * np.abs(k32[i]) + 2.0 ** -10 * scale + 1e-7 * amax
+        assert np.all(err <= bound)
+        assert np.array_equal(np.signbit(deq) | (deq == 0), np.signbit(k32[i]) | (deq == 0))
+
+
+def pin_paging_invariance():
+    r = _rng(9)
+    n = 150
+    x = r.standard_normal((n, D)).astype(np.float32)
+    s = np.arange(n, dtype=np.int32)
+    for dtype in (FP8, BF16):
+        pt_id = np.arange(3, dtype=np.int32)[None, :]
+        pt_perm = np.array([[4, 0, 2]], dtype=np.int32)
+        p1 = oracle.new_pool(3, dtype)
+        p2 = oracle.new_pool(5, dtype)
+        oracle.store_keys(x, np.ones(D, np.float32), 1e-6, s, None, pt_id, dtype, p1)
+        oracle.store_keys(x, np.ones(D, np.float32), 1e-6, s, None, pt_perm, dtype, p2)
+        k1 = _pool_keys(p1, pt_id, dtype, 0, n)
+        k2 = _pool_keys(p2, pt_perm, dtype, 0, n)
+        assert np.array_equal(k1, k2)
+        pb = oracle.page_bytes(dtype)
+        assert np.all(p2[1 * pb:2 * pb] == 0xA5) and np.all(p2[3 * pb:4 * pb] == 0xA5), \
+            "pages outside the table stay untouched"
+
+
+# ------------------------------------------------------------------------------------------------
+# S2: visibility and scores
+# ------------------------------------------------------------------------------------------------
+
+def pin_visibility_brute_force():
+    for t in range(-5, 600):
+        n = sum(1 for s in range(0, 200) if 4 * s + 3 <= t)
+        assert oracle.n_visible(t, 100) == n, t
+    assert oracle.n_visible(10 ** 6, 2) == 128, "visibility is capped by the page-table width"
+
+
+def _tiny_pool(dtype, n_keys=140, seed=10):
+    r = _rng(seed)
+    x = r.standard_normal((n_keys, D)).astype(np.float32)
+    g = (1 + 0.1 * r.standard_normal(D)).astype(np.float32)
+    s = np.arange(n_keys, dtype=np.int32)
+    max_pages = (n_keys + PAGE - 1) // PAGE
+    pt = r.permutation(max_pages + 1)[:max_pages].astype(np.int32)[None, :]
+    pool = oracle.new_pool(max_pages + 1, dtype)
+    oracle.store_keys(x, g, 1e-6, s, None, pt, dtype, pool)
+    return pool, pt
+
+
+def _q_bits(n_q, seed):
+    q = _rng(seed).standard_normal((n_q, H, D)).astype(np.float32)
+    return _torch_bf16_bits(q.ravel()).reshape(n_q, H, D)
+
+
+def pin_visibility_in_logits():
+    pool, pt = _tiny_pool(BF16)
+    L, q_len = 4 * 140, 40
+    qb = _q_bits(q_len, 11)
+    w = np.full((q_len, H), 1.0 / 64, np.float32)
+    out, nv = oracle.logits(qb, w, pool, BF16, pt, [L], [0, q_len])
+    for i in range(q_len):
+        t = L - q_len + i
+        vis = np.array([4 * s + 3 <= t for s in range(out.shape[1])])
+        assert np.array_equal(np.isfinite(out[i]), vis), i
+        assert nv[i] == vis.sum()
+
+
+def pin_scores_onehot_head():
+    for dtype in (FP8, BF16):
+        pool, pt = _tiny_pool(dtype, seed=12)
+        n_q, L = 6, 4 * 140
+        qb = _q_bits(n_q, 13)
+        keys = _pool_keys(pool, pt, dtype, 0, 140)
+        for h0 in (0, 17, 63):
+            w = np.zeros((n_q, H), np.float32)
+            w[:, h0] = 1.0
+            out, nv = oracle.logits(qb, w, pool, dtype, pt, [L], [0, n_q])
+            qf = _bf16_to_f64(qb)
+            for i in range(n_q):
+                ref = np.maximum(0.0, keys[:nv[i]] @ qf[i, h0])
+                assert np.allclose(out[i, :nv[i]], ref, rtol=1e-12, atol=1e-12), (dtype, h0, i)
+
+
+def pin_scores_relu_pairs():
+    pool, pt = _tiny_pool(BF16, seed=14)
+    n_q, L = 4, 4 * 140
+    half = _q_bits(n_q, 15)[:, :32]
+    qb = np.concatenate([half, half ^ np.uint16(0x8000)], axis=1)       # q[h+32] = -q[h]
+    wh = (_rng(16).standard_normal((n_q, 32)) / 8).astype(np.float32)
+    w = np.concatenate([wh, wh], axis=1)
+    out, nv = oracle.logits(qb, w, pool, BF16, pt, [L], [0, n_q])
+    keys = _pool_keys(pool, pt, BF16, 0, 140)
+    qf = _bf16_to_f64(half)
+    for i in range(n_q):
+        d = keys[:nv[i]] @ qf[i].T                                       # [n, 32]
+        ref = np.abs(d) @ wh[i].astype(np.float64)
+        assert np.allclose(out[i, :nv[i]], ref, rtol=1e-10, atol=1e-10)
+
+
+def pin_scores_positive_linear():
+    r = _rng(17)
+    n_q, n_keys, L = 3, 60, 4 * 60
+    keys = np.abs(r.standard_normal((1, n_keys, D))).astype(np.float32)
+    qb = _torch_bf16_bits(np.abs(r.standard_normal(n_q * H * D)).astype(np.float32)).reshape(n_q, H, D)
+    w = (r.standard_normal((n_q, H)) / 8).astype(np.float32)
+    pt = np.zeros((1, 1), np.int32)
+    out, nv = oracle.logits(qb, w, None, BF16, pt, [L], [0, n_q], keys_ref=keys, ref_stride=n_keys)
+    qf = _bf16_to_f64(qb)
+    for i in range(n_q):
+        v = w[i].astype(np.float64) @ qf[i]                              # sum_h w_h q_h
+        ref = keys[0, :nv[i]].astype(np.float64) @ v
+        assert np.allclose(out[i, :nv[i]], ref, rtol=1e-10, atol=1e-10)
+
+
+# ------------------------------------------------------------------------------------------------
+# S3: top-k
+# ------------------------------------------------------------------------------------------------
+
+def pin_topk_brute_force():
+    r = _rng(18)
+    for trial in range(60):
+        n = int(r.integers(1, 50))
+        k = int(r.choice([1, 2, 5, 16, 64]))
+        v = r.integers(0, 6, size=(3, n)).astype(np.float64)            # many ties
+        v[0, ::3] = -0.0
+        idx, val = oracle.topk(v, k)
+        for row in range(3):
+            vr = np.where(v[row] == 0, 0.0, v[row])
+            sel = [i for i in range(n)
+                   if sum(1 for j in range(n) if vr[j] > vr[i] or (vr[j] == vr[i] and j < i)) < k]
+            got = [i for i in idx[row] if i >= 0]
+            assert sorted(got) == sel, (trial, row)
+            assert list(idx[row, :len(sel)]) == list(np.argsort(-vr, kind="stable")[:len(sel)])
+            assert np.all(idx[row, len(sel):] == -1) and np.all(np.isneginf(val[row, len(sel):]))
+
+
+def pin_topk_row_len():
+    v = np.array([[5.0, 4.0, 3.0, 9.0, 9.0, 1.0]])
+    idx, _ = oracle.topk(v, 3, row_len=np.array([3]))
+    assert list(idx[0]) == [0, 1, 2]
+    idx, _ = oracle.topk(v, 2, row_len=np.array([6]))
+    assert list(idx[0]) == [3, 4]
+
+
+# ------------------------------------------------------------------------------------------------
+# Needle planting (harness helper built on the oracle's RoPE)
+# ------------------------------------------------------------------------------------------------
+
+def pin_needle_planting():
+    r = _rng(19)
+    kstar = r.standard_normal((5, D))
+    s = np.array([0, 3, 77, 900, 32000], np.int32)
+    g = (1 + 0.1 * r.standard_normal(D)).astype(np.float32)
+    xo = np.empty((5, D), np.float32)
+    oracle.lib().oracle_plant_keys(oracle._ptr(kstar), oracle._ptr(s), 5, oracle._ptr(g),
+                                   oracle._ptr(xo))
+    _, k32, _ = _store_rows(xo, s, gamma=g)
+    for i in range(5):
+        c = k32[i].astype(np.float64) @ kstar[i] / (np.linalg.norm(k32[i]) * np.linalg.norm(kstar[i]))
+        assert c > 1 - 1e-6, c
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
