@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA indexer hot path on one MI355X.
+
+One step = the whole path over one batch: store the step's keys (RMSNorm + RoPE + quantise +
+paged store), then score every query against its visible keys and select the top-k.
+
+Default workload: the long prefill chunk -- the last 8192 queries of a 22528-token context (5632
+compressed keys, 37,746,688 visible (query, key) pairs), bf16 keys, top-512, with the chunk's 2048
+keys stored inside the step and keys 0..3583 stored beforehand.  Other shapes are selectable with
+--workload for the design notes; they are not the headline line.
+
+Prints one JSON line: keys scored per second (whole job), top-k queries per second, the scoring
+kernel's roofline figures (HIP events around that kernel, on the stream it runs on) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+WORKLOADS = {
+    # name: (config id, kv dtype)
+    "prefill-22k-chunk8192-bf16": (3, 1),
+    "prefill-4k-fp8": (0, 0),
+    "prefill-4k-bf16-needles": (1, 1),
+    "decode-64x4k-22k-fp8": (2, 0),
+    "decode-64x4k-22k-bf16": (2, 1),
+    "decode-32x128k-fp8": (4, 0),
+    "decode-32x128k-bf16": (4, 1),
+}
+DEFAULT = "prefill-22k-chunk8192-bf16"
+
+
+def _pairs(wl) -> int:
+    t = wl.query_positions()
+    nv = np.minimum((t + 1) // 4, wl.max_keys)
+    nv[t < 0] = 0
+    return int(nv.sum()), nv
+
+
+def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int) -> dict:
+    """The oracle as it stands, on every (n_q / n_sample_rows)-th query row of the same batch,
+    plus the store of the step's keys scaled to the same fraction of the batch."""
+    import oracle  # noqa: PLC0415  (test infrastructure; only this leg uses it)
+    oracle.lib()
+    stride = max(1, wl.n_q // n_sample_rows)
+    rows = np.arange(0, wl.n_q, stride, dtype=np.int64)
+    frac = rows.size / wl.n_q
+    pool = oracle.new_pool(wl.n_pages_pool, dtype)
+    if x_step_mask is not None:
+        oracle.store_workload(wl, dtype, pool=pool, mask=~x_step_mask)
+    t0 = time.perf_counter()
+    oracle.store_workload(wl, dtype, pool=pool, mask=x_step_mask)
+    t_store = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    lg, nv = oracle.logits(wl.q_bits, wl.w, pool, dtype, wl.page_table, wl.seq_lens, wl.cu_q,
+                           rows=rows)
+    oracle.topk(lg, wl.k, row_len=nv)
+    t_read = time.perf_counter() - t0
+    secs = t_store * frac + t_read
+    return {"value": float(nv.sum() / secs), "unit": "keys/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows.size} of {wl.n_q} query rows (every {stride}th) scored and "
+                      f"selected, plus the step's store scaled by {frac:.4f}; "
+                      f"{secs:.2f} s of wall time"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the indexer path "
+              "shards by sequence or query chunk with no collective on the hot path, and this "
+              "build runs one GPU.", file=sys.stderr)
+        return 2
+
+    import torch  # noqa: PLC0415
+    import sparse_attention_indexer_rmsnorm_amd as ix  # noqa: PLC0415
+    from sparse_attention_indexer_rmsnorm_amd import workloads as W  # noqa: PLC0415
+
+    ix.lib()
+    cfg, dtype = WORKLOADS[args.workload]
+    wl = W.CONFIGS[cfg]() if cfg != 4 else W.cfg4(needles=False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {
+        "x": torch.from_numpy(wl.x).to(dev), "gamma": torch.from_numpy(wl.gamma).to(dev),
+        "key_idx": torch.from_numpy(wl.key_idx).to(dev),
+        "key_seq": torch.from_numpy(wl.key_seq).to(dev),
+        "page_table": torch.from_numpy(wl.page_table).to(dev),
+        "seq_lens": torch.from_numpy(wl.seq_lens).to(dev),
+        "cu_q": torch.from_numpy(wl.cu_q).to(dev), "q": wl.q_torch().to(dev),
+        "w": torch.from_numpy(wl.w).to(dev),
+    }
+    pool = ix.new_cache(wl.n_pages_pool, dtype, device=dev)
+    step_mask = wl.step_keys if wl.step_keys is not None else np.ones(wl.n_keys, bool)
+    pre = np.nonzero(~step_mask)[0]
+    stp = np.nonzero(step_mask)[0]
+    if pre.size:
+        ix.store_keys(d["x"][pre].contiguous(), d["gamma"], d["key_idx"][pre].contiguous(),
+                      d["page_table"], pool, dtype, eps=wl.eps,
+                      key_seq=d["key_seq"][pre].contiguous())
+    sx = d["x"][stp].contiguous()
+    sidx = d["key_idx"][stp].contiguous()
+    sseq = d["key_seq"][stp].contiguous()
+    ws = torch.empty(ix.workspace_size(wl.n_q, wl.n_seq, wl.max_pages, wl.k), dtype=torch.uint8,
+                     device=dev)
+    out_idx = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:            # materialise the underlying hipEvent_t handles
+        a.record(stream)
+        b.record(stream)
+
+    def step(events=None):
+        ix.store_keys(sx, d["gamma"], sidx, d["page_table"], pool, dtype, eps=wl.eps,
+                      key_seq=sseq)
+        ix.logits_topk(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"], d["cu_q"],
+                       wl.k, out_idx=out_idx, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    pairs, nv = _pairs(wl)
+    score_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    key_bytes = 132 if dtype == 0 else 256
+    if cfg in (2, 4):   # decode: one pass over the visible keys of every sequence
+        algo_bytes = float(nv.sum()) * key_bytes + wl.n_q * (64 * 128 * 2 + 64 * 4)
+        achieved = algo_bytes / (score_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        flops = 2.0 * 64 * 128 * pairs
+        achieved = flops / (score_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "score_kernel"
+    roof["kernel_ms"] = round(score_ms, 4)
+
+    line = {
+        "metric": "indexer keys scored/s (top-k queries/s alongside)",
+        "value": pairs / (ms * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "queries": wl.n_q, "keys": int(wl.max_keys),
+                   "visible_pairs": pairs, "k": wl.k, "kv_dtype": "fp8" if dtype == 0 else "bf16",
+                   "keys_stored_in_step": int(stp.size), "heads": 64, "head_dim": 128,
+                   "workspace_bytes": int(ws.numel())},
+        "topk_queries_per_s": wl.n_q / (ms * 1e-3),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, dtype, wl.step_keys, args.cpu_sample_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -61,6 +61,8 @@ def lib():
         L.oracle_topk.argtypes = [_p, _i64, _i64, _p, _i32, _p, _p]
         L.oracle_plant_keys.restype = None
         L.oracle_plant_keys.argtypes = [_p, _p, _i64, _p, _p]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
         L.oracle_set_mutation.restype = None
         L.oracle_set_mutation.argtypes = [ctypes.c_int]
         _lib = L
@@ -73,6 +75,10 @@ def _ptr(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 def set_mutation(m: int) -> None:

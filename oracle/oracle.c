@@ -36,6 +36,7 @@
  *    sequence, index or page are not stored.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -51,6 +52,9 @@
 static int g_mutation = 0;
 void oracle_set_mutation(int m) { g_mutation = m; }
 int oracle_get_mutation(void) { return g_mutation; }
+
+/* Threads the OpenMP loops below run on. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 int64_t oracle_page_bytes(int dtype) {
     return dtype == OR_FP8 ? (int64_t)OR_PAGE * (OR_D + 4) : (int64_t)OR_PAGE * OR_D * 2;

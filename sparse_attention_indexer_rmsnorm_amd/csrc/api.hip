@@ -1,0 +1,279 @@
+// C ABI of the indexer library (include/dsa_indexer.h): argument validation, workspace planning
+// and kernel launches.  Host code only; validation returns before any HIP call.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/dsa_indexer.h"
+#include "internal.h"
+
+namespace {
+
+using namespace dsa;
+
+constexpr size_t kAlign = 256;
+// Recommended workspace cap: query chunks are sized so that one chunk's head-reduced scores
+// stay within this bound, whatever the batch (the 8192 x 5632 long-prefill chunk needs 185 MB).
+constexpr size_t kWorkspaceCap = size_t(256) << 20;
+// Target number of waves per scoring launch; key chunks shrink until the launch has about this
+// many (row, chunk) work items, but never below kMinChunkKeys keys per wave.
+constexpr int64_t kTargetWaves = 8192;
+constexpr int32_t kMinChunkKeys = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+RopeFreq rope_table() {
+  RopeFreq t;
+  for (int j = 0; j < 32; ++j) t.f[j] = static_cast<float>(std::pow(10000.0, -(2.0 * j) / 64.0));
+  return t;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_EHIP; }
+
+bool dtype_ok(int dtype) { return dtype == IDX_KV_FP8_E4M3 || dtype == IDX_KV_BF16; }
+
+// Workspace layout for `rows` query rows: [row_nvis int32 x rows | pad][scores fp32 rows x cols].
+size_t workspace_for_rows(int64_t rows, int32_t max_pages) {
+  const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
+  return align_up(static_cast<size_t>(rows) * sizeof(int32_t)) +
+         static_cast<size_t>(rows) * cols * sizeof(float);
+}
+
+int64_t rows_fitting(size_t bytes, int32_t max_pages, int64_t n_q) {
+  // largest R <= n_q with workspace_for_rows(R) <= bytes
+  int64_t lo = 0, hi = n_q;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (workspace_for_rows(mid, max_pages) <= bytes) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+void plan_chunks(int64_t n_rows, int32_t n_cols, int32_t* chunk_keys, int32_t* n_chunks) {
+  const int64_t cols32 = (static_cast<int64_t>(n_cols) + 31) / 32 * 32;
+  int64_t ck = (static_cast<int64_t>(n_cols) * n_rows + kTargetWaves - 1) / kTargetWaves;
+  ck = (ck + 31) / 32 * 32;
+  if (ck < kMinChunkKeys) ck = kMinChunkKeys;
+  if (ck > cols32) ck = cols32;
+  if (ck < 32) ck = 32;
+  *chunk_keys = static_cast<int32_t>(ck);
+  *n_chunks = static_cast<int32_t>((cols32 + ck - 1) / ck);
+}
+
+int validate_logits_common(const void* q, const float* w, const void* kcache, int dtype,
+                           int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                           int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q,
+                           int64_t n_q, int32_t n_heads) {
+  if (n_q < 0 || n_seq < 0 || max_pages < 0 || n_pages_pool < 0) return IDX_EINVAL;
+  if (!dtype_ok(dtype)) return IDX_EUNSUPPORTED;
+  if (n_heads != IDX_N_HEADS) return IDX_EUNSUPPORTED;
+  if (n_q > INT32_MAX || static_cast<int64_t>(max_pages) * IDX_PAGE_KEYS > INT32_MAX / 2)
+    return IDX_EINVAL;
+  if (n_q > 0 && (!q || !w || !cu_q || (n_seq > 0 && (!seq_lens || !page_table))))
+    return IDX_EINVAL;
+  if (n_q > 0 && n_seq > 0 && max_pages > 0 && n_pages_pool > 0 && !kcache) return IDX_EINVAL;
+  return IDX_OK;
+}
+
+ScoreArgs score_args(const void* q, const float* w, const void* kcache, int64_t n_pages_pool,
+                     const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                     const int32_t* seq_lens, const int32_t* cu_q) {
+  ScoreArgs s{};
+  s.q = static_cast<const uint16_t*>(q);
+  s.w = w;
+  s.kcache = static_cast<const uint8_t*>(kcache);
+  s.n_pages_pool = n_pages_pool;
+  s.page_table = page_table;
+  s.n_seq = n_seq;
+  s.max_pages = max_pages;
+  s.seq_lens = seq_lens;
+  s.cu_q = cu_q;
+  return s;
+}
+
+int logits_topk_impl(const void* q, const float* w, const void* kcache, int dtype,
+                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                     int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                     int32_t n_heads, int32_t k, int32_t* out_idx, float* out_val,
+                     void* workspace, size_t workspace_bytes, void* ev_begin, void* ev_end,
+                     void* stream) {
+  int st = validate_logits_common(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
+                                  seq_lens, cu_q, n_q, n_heads);
+  if (st != IDX_OK) return st;
+  if (k < 1 || k > IDX_MAX_TOPK) return IDX_EINVAL;
+  if (n_q > 0 && !out_idx) return IDX_EINVAL;
+  if (n_q == 0) return IDX_OK;
+  if (!workspace) return IDX_EWORKSPACE;
+  const int64_t rows_per_chunk = rows_fitting(workspace_bytes, max_pages, n_q);
+  if (rows_per_chunk < 1) return IDX_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t cols = max_pages * IDX_PAGE_KEYS;
+  int32_t* nvis = static_cast<int32_t*>(workspace);
+  float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align_up(rows_per_chunk * sizeof(int32_t)));
+  ScoreArgs sa = score_args(q, w, kcache, n_pages_pool, page_table, n_seq, max_pages, seq_lens,
+                            cu_q);
+  sa.n_cols = cols;
+  sa.out = scores;
+  sa.out_stride = cols;
+  sa.fill_invisible = 0;
+  sa.row_nvis = nvis;
+
+  for (int64_t q0 = 0; q0 < n_q; q0 += rows_per_chunk) {
+    const int64_t rows = (n_q - q0 < rows_per_chunk) ? n_q - q0 : rows_per_chunk;
+    sa.q_begin = q0;
+    sa.n_rows = rows;
+    if (cols > 0) {
+      plan_chunks(rows, cols, &sa.chunk_keys, &sa.n_chunks);
+    } else {
+      sa.chunk_keys = 32;
+      sa.n_chunks = 1;
+    }
+    if (ev_begin && q0 == 0 && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
+      return IDX_EHIP;
+    if (launch_score(sa, dtype, s) != hipSuccess) return IDX_EHIP;
+    if (ev_end && q0 + rows >= n_q &&
+        hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
+      return IDX_EHIP;
+    TopkArgs ta{};
+    ta.scores = scores;
+    ta.row_stride = cols > 0 ? cols : 1;
+    ta.row_len = nvis;
+    ta.n_rows = rows;
+    ta.k = k;
+    ta.out_idx = out_idx + q0 * k;
+    ta.out_val = out_val ? out_val + q0 * k : nullptr;
+    ta.max_row_len = cols;
+    if (launch_topk(ta, s) != hipSuccess) return IDX_EHIP;
+  }
+  return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int idx_abi_version(void) { return IDX_ABI_VERSION; }
+
+const char* idx_status_string(int status) {
+  switch (status) {
+    case IDX_OK: return "ok";
+    case IDX_EINVAL: return "invalid argument";
+    case IDX_EUNSUPPORTED: return "unsupported configuration";
+    case IDX_EWORKSPACE: return "workspace too small";
+    case IDX_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t idx_page_bytes(int dtype) {
+  if (dtype == IDX_KV_FP8_E4M3) return static_cast<size_t>(kFp8PageBytes);
+  if (dtype == IDX_KV_BF16) return static_cast<size_t>(kBf16PageBytes);
+  return 0;
+}
+
+int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t* key_idx,
+                   const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
+                   int32_t n_seq, int32_t max_pages, int dtype, void* kcache,
+                   int64_t n_pages_pool, void* stream) {
+  if (n_keys < 0 || n_seq < 0 || max_pages < 0 || n_pages_pool < 0) return IDX_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return IDX_EINVAL;
+  if (!dtype_ok(dtype)) return IDX_EUNSUPPORTED;
+  if (n_keys == 0) return IDX_OK;
+  if (!x || !gamma || !key_idx || !page_table || !kcache) return IDX_EINVAL;
+  if (n_keys > (static_cast<int64_t>(INT32_MAX) - 255) / 8 * 8) return IDX_EINVAL;
+  StoreArgs a{};
+  a.x = x;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.key_idx = key_idx;
+  a.key_seq = key_seq;
+  a.n_keys = n_keys;
+  a.page_table = page_table;
+  a.n_seq = n_seq;
+  a.max_pages = max_pages;
+  a.kcache = static_cast<uint8_t*>(kcache);
+  a.n_pages_pool = n_pages_pool;
+  a.rope = rope_table();
+  return hip_status(launch_store(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t idx_logits_topk_workspace_size(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t k) {
+  (void)n_seq;
+  (void)k;
+  if (n_q <= 0 || max_pages < 0) return align_up(sizeof(int32_t));
+  const int64_t cap_rows = rows_fitting(kWorkspaceCap, max_pages, n_q);
+  const int64_t rows = cap_rows < 1 ? 1 : cap_rows;
+  return workspace_for_rows(rows, max_pages);
+}
+
+size_t idx_logits_topk_min_workspace(int32_t n_seq, int32_t max_pages, int32_t k) {
+  (void)n_seq;
+  (void)k;
+  return workspace_for_rows(1, max_pages < 0 ? 0 : max_pages);
+}
+
+int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype,
+                    int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                    int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                    int32_t n_heads, int32_t k, int32_t* out_idx, float* out_val,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return logits_topk_impl(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
+                          seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, workspace,
+                          workspace_bytes, nullptr, nullptr, stream);
+}
+
+int idx_logits_topk_timed(const void* q, const float* w, const void* kcache, int dtype,
+                          int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                          int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q,
+                          int64_t n_q, int32_t n_heads, int32_t k, int32_t* out_idx,
+                          float* out_val, void* workspace, size_t workspace_bytes,
+                          void* ev_score_begin, void* ev_score_end, void* stream) {
+  return logits_topk_impl(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
+                          seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, workspace,
+                          workspace_bytes, ev_score_begin, ev_score_end, stream);
+}
+
+int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtype,
+                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                     int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                     int32_t n_heads, float* out_logits, int32_t max_keys, void* stream) {
+  int st = validate_logits_common(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
+                                  seq_lens, cu_q, n_q, n_heads);
+  if (st != IDX_OK) return st;
+  if (max_keys < 1) return IDX_EINVAL;
+  if (n_q > 0 && !out_logits) return IDX_EINVAL;
+  if (n_q == 0) return IDX_OK;
+  ScoreArgs sa = score_args(q, w, kcache, n_pages_pool, page_table, n_seq, max_pages, seq_lens,
+                            cu_q);
+  sa.q_begin = 0;
+  sa.n_rows = n_q;
+  sa.n_cols = max_keys;
+  plan_chunks(n_q, max_keys, &sa.chunk_keys, &sa.n_chunks);
+  sa.out = out_logits;
+  sa.out_stride = max_keys;
+  sa.fill_invisible = 1;
+  sa.row_nvis = nullptr;
+  return hip_status(launch_score(sa, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const int32_t* row_len,
+                  int32_t k, int32_t* out_idx, float* out_val, void* stream) {
+  if (n_rows < 0 || row_stride < 1 || k < 1 || k > IDX_MAX_TOPK) return IDX_EINVAL;
+  if (n_rows > INT32_MAX || row_stride > INT32_MAX) return IDX_EINVAL;
+  if (n_rows == 0) return IDX_OK;
+  if (!scores || !out_idx) return IDX_EINVAL;
+  TopkArgs ta{};
+  ta.scores = scores;
+  ta.row_stride = row_stride;
+  ta.row_len = row_len;
+  ta.n_rows = n_rows;
+  ta.k = k;
+  ta.out_idx = out_idx;
+  ta.out_val = out_val;
+  ta.max_row_len = static_cast<int32_t>(row_stride);
+  return hip_status(launch_topk(ta, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

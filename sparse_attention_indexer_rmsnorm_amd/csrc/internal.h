@@ -1,0 +1,80 @@
+// Internal declarations shared by the HIP translation units of the indexer library.
+// The exported C ABI is include/dsa_indexer.h; nothing here crosses it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kHeadDim = 128;        // index-key head dim
+constexpr int kHeads = 64;           // indexer heads
+constexpr int kPageKeys = 64;        // keys per cache page
+constexpr int kRatio = 4;            // tokens per compressed key
+constexpr int kFp8 = 0;
+constexpr int kBf16 = 1;
+constexpr int64_t kFp8PageBytes = kPageKeys * (kHeadDim + 4);   // 8448: codes, then scales
+constexpr int64_t kBf16PageBytes = kPageKeys * kHeadDim * 2;    // 16384
+constexpr int kFp8ScaleOffset = kPageKeys * kHeadDim;           // 8192
+
+// RoPE inverse frequencies, rounded to fp32 on the host and passed by value.
+struct RopeFreq {
+  float f[32];
+};
+
+struct StoreArgs {
+  const float* x;
+  const float* gamma;
+  float eps;
+  const int32_t* key_idx;
+  const int32_t* key_seq;   // may be null
+  int64_t n_keys;
+  const int32_t* page_table;
+  int32_t n_seq;
+  int32_t max_pages;
+  uint8_t* kcache;
+  int64_t n_pages_pool;
+  RopeFreq rope;
+};
+
+hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t stream);
+
+// One launch scores rows [q_begin, q_begin + n_rows) of the query batch against key columns
+// [0, n_cols).  Each wave owns one (row, chunk of chunk_keys columns) work item.
+struct ScoreArgs {
+  const uint16_t* q;         // [n_q, 64, 128] bf16 bit patterns
+  const float* w;            // [n_q, 64]
+  const uint8_t* kcache;
+  int64_t n_pages_pool;
+  const int32_t* page_table; // [n_seq, max_pages]
+  int32_t n_seq;
+  int32_t max_pages;
+  const int32_t* seq_lens;   // [n_seq]
+  const int32_t* cu_q;       // [n_seq + 1]
+  int64_t q_begin;
+  int64_t n_rows;
+  int32_t n_cols;            // columns covered by the chunks
+  int32_t chunk_keys;        // multiple of 32
+  int32_t n_chunks;
+  float* out;                // [n_rows, out_stride]
+  int64_t out_stride;
+  int32_t fill_invisible;    // 1: write -inf to invisible columns < n_cols
+  int32_t* row_nvis;         // [n_rows] visible-key count per row, or null
+};
+
+hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
+
+struct TopkArgs {
+  const float* scores;       // [n_rows, row_stride]
+  int64_t row_stride;
+  const int32_t* row_len;    // [n_rows] or null (= row_stride)
+  int64_t n_rows;
+  int32_t k;
+  int32_t* out_idx;          // [n_rows, k]
+  float* out_val;            // [n_rows, k] or null
+  int32_t max_row_len;       // upper bound on row lengths (sizes the LDS row cache)
+};
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,131 @@
+"""The C-ABI library loads, exports every declared symbol, and validates arguments on the host.
+
+No GPU is needed: every call here returns from host-side validation before any HIP call.
+"""
+import ctypes
+
+import pytest
+
+import sparse_attention_indexer_rmsnorm_amd as ix
+from tests.helpers import header_functions
+
+E_OK, E_INVAL, E_UNSUP, E_WS, E_HIP = 0, 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ix.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(L, n), f"missing export {n}"
+    assert sorted(n for n, _, _ in ix.SIGNATURES) == names
+
+
+def test_version_and_strings(L):
+    assert L.idx_abi_version() == 1
+    for s in range(5):
+        assert L.idx_status_string(s)
+    assert L.idx_status_string(99) == b"unknown status"
+
+
+def test_page_bytes(L):
+    assert L.idx_page_bytes(0) == 8448      # 64 keys x (128 codes + 4 B scale)
+    assert L.idx_page_bytes(1) == 16384     # 64 keys x 256 B
+    assert L.idx_page_bytes(2) == 0
+
+
+def test_workspace_sizes(L):
+    # decode batch of 32 queries over 512 pages: one row of 32768 fp32 scores each + counts
+    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == 256 + 32 * 32768 * 4
+    # long prefill chunk: 8192 queries x 5632 keys fits the 256 MiB cap in one pass
+    ws = L.idx_logits_topk_workspace_size(8192, 1, 88, 512)
+    assert ws == 8192 * 4 + 8192 * 5632 * 4 and ws <= 256 << 20
+    # a 128K-token prefill of 8192 queries is chunked to stay under the cap
+    big = L.idx_logits_topk_workspace_size(8192, 1, 2048, 512)
+    assert big <= 256 << 20 and big >= 131072 * 4
+    assert L.idx_logits_topk_min_workspace(1, 88, 512) == 256 + 5632 * 4
+    # never depends on the head count: the per-head tensor is never formed
+    assert L.idx_logits_topk_workspace_size(8192, 1, 88, 512) < 8192 * 5632 * 64 * 4 / 50
+
+
+def _store(L, **kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, key_idx=FAKE, key_seq=None, n=10, pt=FAKE, n_seq=1,
+             max_pages=1, dtype=0, kc=FAKE, pool=1)
+    a.update(kw)
+    return L.idx_store_keys(a["x"], a["gamma"], a["eps"], a["key_idx"], a["key_seq"], a["n"],
+                            a["pt"], a["n_seq"], a["max_pages"], a["dtype"], a["kc"], a["pool"],
+                            None)
+
+
+def test_store_validation(L):
+    assert _store(L, n=-1) == E_INVAL
+    assert _store(L, dtype=5) == E_UNSUP
+    assert _store(L, x=None) == E_INVAL
+    assert _store(L, kc=None) == E_INVAL
+    assert _store(L, pt=None) == E_INVAL
+    assert _store(L, eps=-1.0) == E_INVAL
+    assert _store(L, eps=float("nan")) == E_INVAL
+    assert _store(L, n_seq=-2) == E_INVAL
+    assert _store(L, n=0, x=None, kc=None) == E_OK        # empty store is a no-op
+
+
+def _topk(L, fn="idx_logits_topk", **kw):
+    a = dict(q=FAKE, w=FAKE, kc=FAKE, dtype=1, pool=4, pt=FAKE, n_seq=1, max_pages=2,
+             seq_lens=FAKE, cu_q=FAKE, n_q=3, n_heads=64, k=512, oi=FAKE, ov=None, ws=FAKE,
+             ws_bytes=1)
+    a.update(kw)
+    return getattr(L, fn)(a["q"], a["w"], a["kc"], a["dtype"], a["pool"], a["pt"], a["n_seq"],
+                          a["max_pages"], a["seq_lens"], a["cu_q"], a["n_q"], a["n_heads"], a["k"],
+                          a["oi"], a["ov"], a["ws"], a["ws_bytes"], None)
+
+
+def test_logits_topk_validation(L):
+    assert _topk(L, n_heads=32) == E_UNSUP
+    assert _topk(L, dtype=3) == E_UNSUP
+    assert _topk(L, k=0) == E_INVAL
+    assert _topk(L, k=2049) == E_INVAL
+    assert _topk(L, n_q=-1) == E_INVAL
+    assert _topk(L, q=None) == E_INVAL
+    assert _topk(L, cu_q=None) == E_INVAL
+    assert _topk(L, oi=None) == E_INVAL
+    assert _topk(L, ws=None, ws_bytes=10 ** 9) == E_WS
+    assert _topk(L, ws_bytes=100) == E_WS                    # < one row (256 + 128 * 4)
+    assert _topk(L, n_q=0, q=None, w=None, oi=None, ws=None) == E_OK
+
+
+def test_logits_dense_validation(L):
+    def dense(**kw):
+        a = dict(q=FAKE, w=FAKE, kc=FAKE, dtype=0, pool=4, pt=FAKE, n_seq=1, max_pages=2,
+                 seq_lens=FAKE, cu_q=FAKE, n_q=3, n_heads=64, out=FAKE, max_keys=128)
+        a.update(kw)
+        return L.idx_logits_dense(a["q"], a["w"], a["kc"], a["dtype"], a["pool"], a["pt"],
+                                  a["n_seq"], a["max_pages"], a["seq_lens"], a["cu_q"], a["n_q"],
+                                  a["n_heads"], a["out"], a["max_keys"], None)
+    assert dense(max_keys=0) == E_INVAL
+    assert dense(out=None) == E_INVAL
+    assert dense(n_heads=128) == E_UNSUP
+    assert dense(n_q=0, out=None) == E_OK
+
+
+def test_topk_rows_validation(L):
+    f = L.idx_topk_rows
+    assert f(FAKE, 4, 0, None, 10, FAKE, None, None) == E_INVAL     # row_stride < 1
+    assert f(FAKE, 4, 100, None, 0, FAKE, None, None) == E_INVAL
+    assert f(FAKE, 4, 100, None, 4096, FAKE, None, None) == E_INVAL
+    assert f(None, 4, 100, None, 10, FAKE, None, None) == E_INVAL
+    assert f(FAKE, -1, 100, None, 10, FAKE, None, None) == E_INVAL
+    assert f(None, 0, 100, None, 10, None, None, None) == E_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 128)
+    with pytest.raises(ValueError):
+        ix.store_keys(x, torch.ones(128), torch.zeros(4, dtype=torch.int32),
+                      torch.zeros(1, 1, dtype=torch.int32), torch.zeros(8448, dtype=torch.uint8),
+                      ix.FP8)

@@ -1,0 +1,146 @@
+"""S3 parity.
+
+1. The selection kernel alone against the oracle's full sort on identical fp32 inputs: indices
+   and values must match exactly (ties broken toward the lower index, -0 == +0), for rows with
+   heavy ties, short rows, rows longer than the LDS cache and every k the API allows.
+2. The whole read path (score + select) against fp64 oracle logits: exact sets wherever the
+   oracle's k-th / (k+1)-th gap exceeds the logit tolerance, near-tie validity everywhere and
+   mean overlap >= 0.999.
+3. GPU self-consistency: idx_logits_topk equals idx_topk_rows applied to idx_logits_dense, and
+   chunking the queries through a small workspace changes nothing.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_indexer_rmsnorm_amd as ix
+from sparse_attention_indexer_rmsnorm_amd import workloads as W
+from tests.helpers import check_topk_sets, dev_inputs, gpu_store, oracle_rows, workload
+
+pytestmark = pytest.mark.gpu
+FP8, BF16 = W.FP8, W.BF16
+
+
+def _rows(seed, n_rows, stride, kind):
+    r = np.random.default_rng(seed)
+    if kind == "ties":
+        v = r.integers(-3, 4, (n_rows, stride)).astype(np.float32)
+        v[v == 0] = np.where(r.random((v == 0).sum()) < 0.5, -0.0, 0.0)
+    elif kind == "normal":
+        v = r.standard_normal((n_rows, stride)).astype(np.float32)
+    else:   # few distinct values with -inf mixed in
+        v = r.choice(np.array([-np.inf, -1.5, 0.25, 7.0], np.float32), (n_rows, stride))
+    return v
+
+
+@pytest.mark.parametrize("n_rows,stride,k,kind", [
+    (64, 1024, 512, "ties"), (64, 1024, 512, "normal"), (8, 5632, 512, "mixed"),
+    (4, 32768, 1024, "normal"), (3, 32768, 2048, "ties"), (2, 40000, 1024, "normal"),
+    (2, 40000, 700, "ties"), (16, 100, 1, "ties"), (16, 100, 2048, "normal"),
+    (5, 513, 512, "ties"), (5, 512, 512, "normal"),
+])
+def test_topk_rows_bit_exact(oracle_mod, n_rows, stride, k, kind):
+    v = _rows(n_rows * 1000003 + stride * 31 + k + 7 * len(kind), n_rows, stride, kind)
+    row_len = np.random.default_rng(5).integers(0, stride + 1, n_rows).astype(np.int32)
+    row_len[0] = stride
+    row_len[-1] = min(k, stride)
+    gi, gv = ix.topk_rows(torch.from_numpy(v).cuda(), k, torch.from_numpy(row_len).cuda())
+    oi, ov = oracle_mod.topk(v, k, row_len=row_len)
+    gi, gv = gi.cpu().numpy(), gv.cpu().numpy()
+    for r in range(n_rows):
+        m = min(k, int(row_len[r]))
+        # the GPU returns the selected set in index order; the oracle in value order
+        assert np.array_equal(gi[r, :m], np.sort(oi[r, :m])), f"row {r}"
+        assert np.all(gi[r, m:] == -1)
+        order = np.argsort(oi[r, :m])
+        assert np.array_equal(gv[r, :m].view(np.uint32),
+                              ov[r, :m][order].astype(np.float32).view(np.uint32))
+        assert np.all(np.isneginf(gv[r, m:]))
+
+
+def _gpu_topk(wl, d, pool, dtype, workspace=None, want_values=False):
+    return ix.logits_topk(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"], d["cu_q"],
+                          wl.k, workspace=workspace, want_values=want_values)
+
+
+@pytest.mark.parametrize("cfg,dtype,n_rows", [(0, FP8, None), (1, BF16, None), (2, FP8, None),
+                                              (2, BF16, None), (3, BF16, 48), (4, FP8, None),
+                                              (4, BF16, None)])
+def test_logits_topk_vs_oracle(oracle_mod, cfg, dtype, n_rows):
+    """The full path as measured: keys stored by the GPU, then score + select on the GPU."""
+    wl = workload(cfg)
+    print(f"topk cfg{cfg} dtype={dtype}", flush=True)
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, dtype, d)
+    gi, _ = _gpu_topk(wl, d, pool, dtype)
+    gi = gi.cpu().numpy()
+    if n_rows is None:
+        rows = np.arange(wl.n_q)
+    else:
+        rows = np.unique(np.concatenate([[0, wl.n_q - 1], np.random.default_rng(cfg).choice(
+            wl.n_q, n_rows - 2, replace=False)]))
+    pool_o, _ = oracle_mod.store_workload(wl, dtype)
+    o, nv = oracle_rows(oracle_mod, wl, pool_o, dtype, rows)
+    mean, exact = check_topk_sets(gi[rows], o, nv, wl.k, f"cfg{cfg}")
+    print(f"  rows={rows.size} overlap={mean:.6f} exact-gap rows={exact}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", [FP8, BF16])
+def test_logits_topk_ragged(oracle_mod, dtype):
+    wl = W.make_workload("ragged", 31 + dtype, [0, 3, 4, 130, 700, 1500, 2100],
+                         [0, 2, 1, 7, 33, 70, 3], 64, permute_pages=True, extra_pages=2)
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, dtype, d)
+    gi, gv = _gpu_topk(wl, d, pool, dtype, want_values=True)
+    pool_o, _ = oracle_mod.store_workload(wl, dtype)
+    o, nv = oracle_rows(oracle_mod, wl, pool_o, dtype, None)
+    check_topk_sets(gi.cpu().numpy(), o, nv, wl.k, "ragged")
+    gv = gv.cpu().numpy()
+    gi = gi.cpu().numpy()
+    for r in range(wl.n_q):
+        m = min(wl.k, int(nv[r]))
+        assert np.all(np.isneginf(gv[r, m:]))
+        assert np.allclose(gv[r, :m], o[r, gi[r, :m]], rtol=2e-3, atol=1e-3)
+
+
+@pytest.mark.parametrize("cfg,dtype", [(2, FP8), (2, BF16), (0, FP8)])
+def test_topk_matches_dense_then_select(cfg, dtype):
+    wl = workload(cfg)
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, dtype, d)
+    gi, gv = _gpu_topk(wl, d, pool, dtype, want_values=True)
+    dense = ix.logits_dense(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
+                            d["cu_q"], wl.max_keys)
+    nvis = torch.isfinite(dense).sum(dim=1).to(torch.int32)
+    si, sv = ix.topk_rows(dense, wl.k, nvis)
+    assert torch.equal(gi, si)
+    assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
+
+
+def test_small_workspace_chunks_queries():
+    wl = workload(0)
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, FP8, d)
+    full, _ = _gpu_topk(wl, d, pool, FP8)
+    ws = torch.empty(ix.min_workspace(wl.n_seq, wl.max_pages, wl.k) * 3 + 100, dtype=torch.uint8,
+                     device="cuda")
+    part, _ = _gpu_topk(wl, d, pool, FP8, workspace=ws)
+    assert torch.equal(full, part)
+
+
+def test_too_small_workspace_raises():
+    wl = workload(0)
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, FP8, d)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ix.IndexerError):
+        _gpu_topk(wl, d, pool, FP8, workspace=ws)
+
+
+def test_logits_topk_repeatable():
+    wl = workload(4)
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, FP8, d)
+    a, _ = _gpu_topk(wl, d, pool, FP8)
+    b, _ = _gpu_topk(wl, d, pool, FP8)
+    assert torch.equal(a, b)
