@@ -22,6 +22,18 @@ constexpr int32_t kMinChunkKeys = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Batches with several queries per sequence on average (prefill chunks) use the kernel whose
+// workgroups share key pages between 4 query rows; decode-shaped batches (about one query per
+// sequence) split each row's keys over many waves instead.
+bool prefill_shaped(int64_t n_rows, int32_t n_seq) {
+  return n_rows >= 64 && n_rows >= 4 * static_cast<int64_t>(n_seq > 0 ? n_seq : 1);
+}
+
+hipError_t score_launch(const ScoreArgs& a, int dtype, hipStream_t s) {
+  return prefill_shaped(a.n_rows, a.n_seq) ? launch_score_rows(a, dtype, s)
+                                           : launch_score(a, dtype, s);
+}
+
 RopeFreq rope_table() {
   RopeFreq t;
   for (int j = 0; j < 32; ++j) t.f[j] = static_cast<float>(std::pow(10000.0, -(2.0 * j) / 64.0));
@@ -132,7 +144,7 @@ int logits_topk_impl(const void* q, const float* w, const void* kcache, int dtyp
     }
     if (ev_begin && q0 == 0 && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
       return IDX_EHIP;
-    if (launch_score(sa, dtype, s) != hipSuccess) return IDX_EHIP;
+    if (score_launch(sa, dtype, s) != hipSuccess) return IDX_EHIP;
     if (ev_end && q0 + rows >= n_q &&
         hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
       return IDX_EHIP;
@@ -255,7 +267,7 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
   sa.out_stride = max_keys;
   sa.fill_invisible = 1;
   sa.row_nvis = nullptr;
-  return hip_status(launch_score(sa, dtype, static_cast<hipStream_t>(stream)));
+  return hip_status(score_launch(sa, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const int32_t* row_len,

@@ -63,6 +63,9 @@ struct ScoreArgs {
 };
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
+// Prefill-shaped variant: 4 query rows per workgroup share LDS-staged key pages; covers all
+// columns [0, n_cols) of each row (chunk_keys / n_chunks unused).
+hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream);
 
 struct TopkArgs {
   const float* scores;       // [n_rows, row_stride]

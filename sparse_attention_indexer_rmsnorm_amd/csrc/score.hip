@@ -162,7 +162,207 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
 }
 
+// Prefill-shaped batches: a workgroup scores 4 consecutive query rows (one per wave) against
+// their sequence's keys, one 64-key page at a time.  The page is staged once per workgroup into
+// LDS (fp8 codes widened to bf16 while staging) and each wave reads its B fragments from there, so
+// the L2 -> CU traffic is shared by 4 queries.  Rows are padded to 272 B in LDS so that the 16 B
+// fragment reads of consecutive lanes (consecutive keys) fall in distinct banks.  The next page is
+// fetched into registers while the current one is being scored (double-buffered LDS).
+constexpr int kTileKeys = 64;
+constexpr int kLdsRow = kHeadDim * 2 + 16;
+
+template <int DT>
+__global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTileKeys * kLdsRow];
+  __shared__ float tscale[2][kTileKeys];
+  __shared__ int32_t seg_b[4];
+  __shared__ int32_t seg_nvis[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int m = lane & 31;
+  const int g = lane >> 5;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+  const bool row_ok = r < a.n_rows;
+  const int64_t i = a.q_begin + (row_ok ? r : a.n_rows - 1);
+
+  int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
+  int64_t n_vis = 0;
+  if (b >= 0) {
+    const int64_t q_len = a.cu_q[b + 1] - a.cu_q[b];
+    const int64_t t = static_cast<int64_t>(a.seq_lens[b]) - q_len + (i - a.cu_q[b]);
+    if (t >= 0) {
+      n_vis = (t + 1) / kRatio;
+      const int64_t cap = static_cast<int64_t>(a.max_pages) * kPageKeys;
+      n_vis = n_vis < cap ? n_vis : cap;
+    }
+  }
+  if (!row_ok) {
+    b = -1;
+    n_vis = 0;
+  }
+  const int32_t nv_own = static_cast<int32_t>(min<int64_t>(n_vis, a.n_cols));
+  float* out_row = a.out + (row_ok ? r : 0) * a.out_stride;
+  if (row_ok) {
+    if (a.row_nvis && lane == 0) a.row_nvis[r] = static_cast<int32_t>(n_vis);
+    if (a.fill_invisible)
+      for (int32_t s = nv_own + lane; s < a.n_cols; s += 64) out_row[s] = -INFINITY;
+  }
+  if (lane == 0) {
+    seg_b[wid] = nv_own > 0 ? b : -1;
+    seg_nvis[wid] = nv_own;
+  }
+
+  // A operand (this wave's query, both 32-head tiles) and the head weights of its rows.
+  Frag qa[2][8];
+  float wv[2][16];
+  if (nv_own > 0) {
+    const uint16_t* qrow = a.q + i * (kHeads * kHeadDim);
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const uint4* src = reinterpret_cast<const uint4*>(qrow + (32 * ht + m) * kHeadDim + 64 * g);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) qa[ht][jj].u = src[jj];
+    }
+    const float* wrow = a.w + i * kHeads;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) wv[ht][rr] = wrow[32 * ht + 8 * (rr >> 2) + 4 * g + (rr & 3)];
+  }
+  __syncthreads();
+
+  // Staging assignment: thread -> (key kk of the page, quarter qq of its 128 dims).
+  const int kk = tid >> 2;
+  const int qq = tid & 3;
+
+  for (int j = 0; j < 4; ++j) {
+    const int32_t bj = seg_b[j];
+    if (bj < 0) continue;
+    bool seen = false;
+    int32_t nmax = 0;
+    for (int jj = 0; jj < 4; ++jj) {
+      if (jj < j && seg_b[jj] == bj) seen = true;
+      if (seg_b[jj] == bj) nmax = max(nmax, seg_nvis[jj]);
+    }
+    if (seen) continue;
+    const bool mine = (b == bj) && nv_own > 0;
+    const int32_t* pt_row = a.page_table + static_cast<int64_t>(bj) * a.max_pages;
+    const int n_tiles = (nmax + kTileKeys - 1) / kTileKeys;
+
+    // Fetch page t into registers.
+    uint4 st[4];
+    float st_scale = 1.0f;
+    bool st_ok = false;
+    auto fetch = [&](int t) {
+      const int32_t s = t * kTileKeys + kk;
+      const int32_t page = pt_row[t];
+      st_ok = page >= 0 && page < a.n_pages_pool;
+      const bool load = st_ok && s < nmax;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) st[c] = make_uint4(0, 0, 0, 0);
+      st_scale = 0.0f;
+      if (load) {
+        if constexpr (DT == kBf16) {
+          const uint4* src = reinterpret_cast<const uint4*>(
+              a.kcache + page * kBf16PageBytes + kk * (kHeadDim * 2) + qq * 64);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) st[c] = src[c];
+        } else {
+          const uint8_t* pg = a.kcache + page * kFp8PageBytes;
+          const uint4* src = reinterpret_cast<const uint4*>(pg + kk * kHeadDim + qq * 32);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) st[c] = src[c];
+          if (qq == 0) st_scale = *reinterpret_cast<const float*>(pg + kFp8ScaleOffset + kk * 4);
+        }
+      }
+    };
+    // Write the fetched page into LDS buffer `buf` (bf16, natural dim order, padded rows).
+    auto commit = [&](int buf) {
+      uint8_t* dst = &tile[buf][kk * kLdsRow + qq * 64];
+      if constexpr (DT == kBf16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) reinterpret_cast<uint4*>(dst)[c] = st[c];
+      } else {
+        // 32 codes -> 32 bf16 (64 B)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t wds[4] = {st[c].x, st[c].y, st[c].z, st[c].w};
+          Frag f0, f1;
+          f0.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[0], 1.0f, false);
+          f0.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[0], 1.0f, true);
+          f0.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[1], 1.0f, false);
+          f0.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[1], 1.0f, true);
+          f1.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2], 1.0f, false);
+          f1.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2], 1.0f, true);
+          f1.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[3], 1.0f, false);
+          f1.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[3], 1.0f, true);
+          reinterpret_cast<uint4*>(dst)[2 * c] = f0.u;
+          reinterpret_cast<uint4*>(dst)[2 * c + 1] = f1.u;
+        }
+        if (qq == 0) tscale[buf][kk] = st_scale;
+      }
+    };
+
+    bool ok_cur = false;
+    fetch(0);
+    commit(0);
+    ok_cur = st_ok;
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int buf = t & 1;
+      const bool more = t + 1 < n_tiles;
+      if (more) fetch(t + 1);
+      const int32_t s_tile = t * kTileKeys;
+      if (mine && s_tile < nv_own) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int32_t s0 = s_tile + 32 * h;
+          if (s0 < nv_own) {
+            Frag kb[8];
+            const uint8_t* srcb = &tile[buf][(32 * h + m) * kLdsRow + 128 * g];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) kb[jj].u = reinterpret_cast<const uint4*>(srcb)[jj];
+            floatx16 acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, kb[jj].v, acc0, 0, 0, 0);
+              acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc1, 0, 0, 0);
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) part += wv[0][rr] * fmaxf(acc0[rr], 0.0f);
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) part += wv[1][rr] * fmaxf(acc1[rr], 0.0f);
+            float tot = part + __shfl_xor(part, 32, 64);
+            const int32_t s = s0 + m;
+            if constexpr (DT == kFp8) tot *= tscale[buf][32 * h + m];
+            if (g == 0 && s < nv_own) out_row[s] = ok_cur ? tot : -INFINITY;
+          }
+        }
+      }
+      if (more) commit(buf ^ 1);
+      const bool ok_next = st_ok;
+      __syncthreads();
+      ok_cur = ok_next;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream) {
+  if (a.n_rows <= 0) return hipSuccess;
+  const int64_t blocks = (a.n_rows + 3) / 4;
+  if (dtype == kBf16)
+    hipLaunchKernelGGL(score_rows_kernel<kBf16>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(score_rows_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
   const int64_t waves = a.n_rows * a.n_chunks;
