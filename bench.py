@@ -84,6 +84,9 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB --steps times (the "
+                         "reference for scaling HBM byte counters); prints its bytes per copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the indexer path "
@@ -94,6 +97,16 @@ def main() -> int:
     import torch  # noqa: PLC0415
     import sparse_attention_indexer_rmsnorm_amd as ix  # noqa: PLC0415
     from sparse_attention_indexer_rmsnorm_amd import workloads as W  # noqa: PLC0415
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": args.steps}))
+        return 0
 
     ix.lib()
     cfg, dtype = WORKLOADS[args.workload]

@@ -20,6 +20,8 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-fp32 instructions anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in arch VGPRs: the epilogue reads them with plain VALU ops
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wall", "-Wno-unused-command-line-argument",
            "-I", os.path.join(ROOT, "include"),
            "-o", LIB + ".tmp"] + sources()

@@ -24,9 +24,10 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Batches with several queries per sequence on average (prefill chunks) use the kernel whose
 // workgroups share key pages between 4 query rows; decode-shaped batches (about one query per
-// sequence) split each row's keys over many waves instead.
+// sequence) and small batches, where 4 rows per workgroup would leave most of the 256 CUs idle,
+// split each row's keys over many waves instead.
 bool prefill_shaped(int64_t n_rows, int32_t n_seq) {
-  return n_rows >= 64 && n_rows >= 4 * static_cast<int64_t>(n_seq > 0 ? n_seq : 1);
+  return n_rows >= 1024 && n_rows >= 4 * static_cast<int64_t>(n_seq > 0 ? n_seq : 1);
 }
 
 hipError_t score_launch(const ScoreArgs& a, int dtype, hipStream_t s) {

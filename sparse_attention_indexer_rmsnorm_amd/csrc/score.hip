@@ -29,12 +29,23 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+// 16-byte moves use a native vector type: HIP's uint4 is a struct whose copies lower to memcpy,
+// which keeps staging arrays from being promoted to registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 union Frag {
   bf16x8 v;
-  uint4 u;
+  u32x4 u;
   bf16x2 p[4];
 };
+
+// Read a wave-uniform int32 through the constant address space: a scalar load whose completion
+// is tracked apart from the vector-memory counter (which also counts outstanding stores).  Only for
+// read-only metadata at addresses that are the same in every lane.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(p));
+}
 
 // Sequence of flattened query row i: the last b with cu_q[b] <= i (binary search), or -1 when i
 // lies outside every [cu_q[b], cu_q[b+1]).
@@ -48,10 +59,95 @@ __device__ __forceinline__ int32_t seq_of_row(const int32_t* cu_q, int32_t n_seq
   return i < cu_q[lo + 1] ? lo : -1;
 }
 
+// ReLU of a finite float as one integer max: a set sign bit makes the pattern a negative int32,
+// which max(., 0) maps to +0; non-negative floats are unchanged.  (A float max would first have
+// to quieten NaNs in IEEE mode, costing a second instruction.)
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Weighted ReLU sum over the 64 heads of one key column.  acc0 / acc1 are the two 32-head MFMA
+// tiles; lane (m, g) holds heads 32*ht + 8*(rr/4) + 4*g + rr%4 of key m in acc_ht[rr].  Four
+// independent fma chains keep the VALU pipeline full.  The summation order is fixed, so every
+// kernel that uses this returns bit-identical logits.
+__device__ __forceinline__ float head_sum(const floatx16& acc0, const floatx16& acc1,
+                                          const float (&wv)[2][16]) {
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr)
+    p[rr & 3] = fmaf(relu(acc0[rr]), wv[0][rr], p[rr & 3]);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr)
+    p[rr & 3] = fmaf(relu(acc1[rr]), wv[1][rr], p[rr & 3]);
+  const float part = (p[0] + p[1]) + (p[2] + p[3]);
+  return part + __shfl_xor(part, 32, 64);
+}
+
+// Load a 32-key column block of B fragments for the split kernel: lane (m, g) reads key s (its
+// column) at dims 64g.. from the pool; zeros when the key is not to be read.
+template <int DT>
+struct KeyBlock;
+
+template <>
+struct KeyBlock<kBf16> {
+  u32x4 raw[8];
+  float scale;
+  __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int slot, int g, bool ok) {
+    if (ok) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          kcache + page * kBf16PageBytes + slot * (kHeadDim * 2) + 128 * g);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) raw[jj] = src[jj];
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) raw[jj] = u32x4{0u, 0u, 0u, 0u};
+    }
+    scale = 1.0f;
+  }
+  __device__ __forceinline__ void frags(Frag (&kb)[8]) const {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) kb[jj].u = raw[jj];
+  }
+};
+
+template <>
+struct KeyBlock<kFp8> {
+  u32x4 raw[4];
+  float scale;
+  __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int slot, int g, bool ok) {
+    if (ok) {
+      const uint8_t* pg = kcache + page * kFp8PageBytes;
+      const u32x4* src = reinterpret_cast<const u32x4*>(pg + slot * kHeadDim + 64 * g);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) raw[c] = src[c];
+      scale = *reinterpret_cast<const float*>(pg + kFp8ScaleOffset + slot * 4);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) raw[c] = u32x4{0u, 0u, 0u, 0u};
+      scale = 0.0f;
+    }
+  }
+  // k-step jj uses code bytes 8jj..8jj+7 of this lane's 64: words 2jj and 2jj+1.
+  __device__ __forceinline__ void frags(Frag (&kb)[8]) const {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint32_t w0 = (jj & 1) ? raw[jj >> 1].z : raw[jj >> 1].x;
+      const uint32_t w1 = (jj & 1) ? raw[jj >> 1].w : raw[jj >> 1].y;
+      kb[jj].p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+      kb[jj].p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+      kb[jj].p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+      kb[jj].p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    }
+  }
+};
+
 template <int DT>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  // the wave index is uniform within a wave; say so, so that everything derived from it
+  // (row, sequence, page-table row) lives in scalar registers
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 +
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t r = wave / a.n_chunks;
   const int32_t chunk = static_cast<int32_t>(wave % a.n_chunks);
   if (r >= a.n_rows) return;
@@ -88,7 +184,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   Frag qa[2][8];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const uint4* src = reinterpret_cast<const uint4*>(qrow + (32 * ht + m) * kHeadDim + 64 * g);
+    const u32x4* src = reinterpret_cast<const u32x4*>(qrow + (32 * ht + m) * kHeadDim + 64 * g);
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) qa[ht][jj].u = src[jj];
   }
@@ -102,65 +198,94 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 
   const int32_t* pt_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
 
+  // Key block s0 .. s0+31 (32-aligned, so inside one page): lane (m, g) holds key s0 + m.  The
+  // next block's keys are fetched while the current one is multiplied; page ids (wave-uniform,
+  // scalar loads) run one more block ahead.
+  auto page_ok = [&](int32_t page) { return page >= 0 && page < a.n_pages_pool; };
+  KeyBlock<DT> cur, nxt;
+  int32_t page = load_uniform(pt_row + c_begin / kPageKeys);
+  int32_t page_n = c_begin + 32 < s_end ? load_uniform(pt_row + (c_begin + 32) / kPageKeys) : -1;
+  bool ok = page_ok(page);
+  cur.load(a.kcache, page, (c_begin + m) % kPageKeys, g, ok && c_begin + m < s_end);
   for (int32_t s0 = c_begin; s0 < s_end; s0 += 32) {
-    const int32_t s = s0 + m;
-    const bool valid = s < s_end;
-    int32_t page = valid ? pt_row[s / kPageKeys] : -1;
-    const bool ok = valid && page >= 0 && page < a.n_pages_pool;
-    const int slot = s % kPageKeys;
-
+    const bool more = s0 + 32 < s_end;
+    const bool ok_n = page_ok(page_n);
+    if (more) nxt.load(a.kcache, page_n, (s0 + 32 + m) % kPageKeys, g, ok_n && s0 + 32 + m < s_end);
+    const int32_t page_nn =
+        s0 + 64 < s_end ? load_uniform(pt_row + (s0 + 64) / kPageKeys) : -1;
     Frag kb[8];
-    float kscale = 1.0f;
-    if constexpr (DT == kBf16) {
-      if (ok) {
-        const uint4* src = reinterpret_cast<const uint4*>(
-            a.kcache + page * kBf16PageBytes + slot * (kHeadDim * 2) + 128 * g);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) kb[jj].u = src[jj];
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) kb[jj].u = make_uint4(0, 0, 0, 0);
-      }
-    } else {
-      uint4 raw[4];
-      if (ok) {
-        const uint8_t* pg = a.kcache + page * kFp8PageBytes;
-        const uint4* src = reinterpret_cast<const uint4*>(pg + slot * kHeadDim + 64 * g);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) raw[c] = src[c];
-        kscale = *reinterpret_cast<const float*>(pg + kFp8ScaleOffset + slot * 4);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) raw[c] = make_uint4(0, 0, 0, 0);
-      }
-      // k-step jj uses code bytes 8jj..8jj+7 of this lane's 64: words 2jj and 2jj+1.
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const uint32_t w0 = (jj & 1) ? raw[jj >> 1].z : raw[jj >> 1].x;
-        const uint32_t w1 = (jj & 1) ? raw[jj >> 1].w : raw[jj >> 1].y;
-        kb[jj].p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-        kb[jj].p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-        kb[jj].p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-        kb[jj].p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-      }
-    }
-
+    cur.frags(kb);
     floatx16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, kb[jj].v, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc1, 0, 0, 0);
     }
-    float part = 0.0f;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) part += wv[0][rr] * fmaxf(acc0[rr], 0.0f);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) part += wv[1][rr] * fmaxf(acc1[rr], 0.0f);
-    float tot = part + __shfl_xor(part, 32, 64);
-    if constexpr (DT == kFp8) tot *= kscale;
-    if (g == 0 && valid) out_row[s] = ok ? tot : -INFINITY;
+    float tot = head_sum(acc0, acc1, wv);
+    if constexpr (DT == kFp8) tot *= cur.scale;
+    const int32_t s = s0 + m;
+    if (g == 0 && s < s_end) out_row[s] = ok ? tot : -INFINITY;
+    if (more) {
+      cur = nxt;
+      ok = ok_n;
+    }
+    page_n = page_nn;
   }
 }
+
+// One thread's share of a 64-key page staged through LDS: key kk, dims 32qq..32qq+31, i.e. 64 B
+// of a bf16 row or 32 code bytes of an fp8 row (plus the key's scale, held by qq == 0).
+template <int DT>
+struct Stage;
+
+template <>
+struct Stage<kBf16> {
+  u32x4 v[4];
+  __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int kk, int qq) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        kcache + page * kBf16PageBytes + kk * (kHeadDim * 2) + qq * 64);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = src[c];
+  }
+  __device__ __forceinline__ void commit(uint8_t* dst, float* scale_slot, int qq) const {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) reinterpret_cast<u32x4*>(dst)[c] = v[c];
+    (void)scale_slot;
+    (void)qq;
+  }
+};
+
+template <>
+struct Stage<kFp8> {
+  u32x4 v[2];
+  float scale;
+  __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int kk, int qq) {
+    const uint8_t* pg = kcache + page * kFp8PageBytes;
+    const u32x4* src = reinterpret_cast<const u32x4*>(pg + kk * kHeadDim + qq * 32);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) v[c] = src[c];
+    scale = qq == 0 ? *reinterpret_cast<const float*>(pg + kFp8ScaleOffset + kk * 4) : 0.0f;
+  }
+  // 32 codes -> 32 bf16 (64 B), natural dim order
+  __device__ __forceinline__ void commit(uint8_t* dst, float* scale_slot, int qq) const {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t wds[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+      Frag f0, f1;
+      f0.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[0], 1.0f, false);
+      f0.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[0], 1.0f, true);
+      f0.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[1], 1.0f, false);
+      f0.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[1], 1.0f, true);
+      f1.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2], 1.0f, false);
+      f1.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2], 1.0f, true);
+      f1.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[3], 1.0f, false);
+      f1.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[3], 1.0f, true);
+      reinterpret_cast<u32x4*>(dst)[2 * c] = f0.u;
+      reinterpret_cast<u32x4*>(dst)[2 * c + 1] = f1.u;
+    }
+    if (qq == 0) *scale_slot = scale;
+  }
+};
 
 // Prefill-shaped batches: a workgroup scores 4 consecutive query rows (one per wave) against
 // their sequence's keys, one 64-key page at a time.  The page is staged once per workgroup into
@@ -221,7 +346,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
     const uint16_t* qrow = a.q + i * (kHeads * kHeadDim);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
-      const uint4* src = reinterpret_cast<const uint4*>(qrow + (32 * ht + m) * kHeadDim + 64 * g);
+      const u32x4* src = reinterpret_cast<const u32x4*>(qrow + (32 * ht + m) * kHeadDim + 64 * g);
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) qa[ht][jj].u = src[jj];
     }
@@ -248,104 +373,86 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
     }
     if (seen) continue;
     const bool mine = (b == bj) && nv_own > 0;
-    const int32_t* pt_row = a.page_table + static_cast<int64_t>(bj) * a.max_pages;
+    // bj comes from LDS: make it visibly wave-uniform so that page-table reads are scalar loads.
+    const int32_t bu = __builtin_amdgcn_readfirstlane(bj);
+    const int32_t* pt_row = a.page_table + static_cast<int64_t>(bu) * a.max_pages;
     const int n_tiles = (nmax + kTileKeys - 1) / kTileKeys;
 
-    // Fetch page t into registers.
-    uint4 st[4];
-    float st_scale = 1.0f;
+    // Page t (id `page`) into this thread's staging registers.  The load is unconditional so that
+    // the staging registers stay registers: an invalid page id reads page 0 instead (its scores
+    // are then replaced by -inf) and key slots past the visible range are inside the page anyway
+    // (their columns are never stored).  An empty pool has no page to read at all.
+    Stage<DT> st;
     bool st_ok = false;
-    auto fetch = [&](int t) {
-      const int32_t s = t * kTileKeys + kk;
-      const int32_t page = pt_row[t];
-      st_ok = page >= 0 && page < a.n_pages_pool;
-      const bool load = st_ok && s < nmax;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) st[c] = make_uint4(0, 0, 0, 0);
-      st_scale = 0.0f;
-      if (load) {
-        if constexpr (DT == kBf16) {
-          const uint4* src = reinterpret_cast<const uint4*>(
-              a.kcache + page * kBf16PageBytes + kk * (kHeadDim * 2) + qq * 64);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) st[c] = src[c];
-        } else {
-          const uint8_t* pg = a.kcache + page * kFp8PageBytes;
-          const uint4* src = reinterpret_cast<const uint4*>(pg + kk * kHeadDim + qq * 32);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) st[c] = src[c];
-          if (qq == 0) st_scale = *reinterpret_cast<const float*>(pg + kFp8ScaleOffset + kk * 4);
-        }
-      }
-    };
-    // Write the fetched page into LDS buffer `buf` (bf16, natural dim order, padded rows).
-    auto commit = [&](int buf) {
-      uint8_t* dst = &tile[buf][kk * kLdsRow + qq * 64];
-      if constexpr (DT == kBf16) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) reinterpret_cast<uint4*>(dst)[c] = st[c];
-      } else {
-        // 32 codes -> 32 bf16 (64 B)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint32_t wds[4] = {st[c].x, st[c].y, st[c].z, st[c].w};
-          Frag f0, f1;
-          f0.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[0], 1.0f, false);
-          f0.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[0], 1.0f, true);
-          f0.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[1], 1.0f, false);
-          f0.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[1], 1.0f, true);
-          f1.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2], 1.0f, false);
-          f1.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[2], 1.0f, true);
-          f1.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[3], 1.0f, false);
-          f1.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[3], 1.0f, true);
-          reinterpret_cast<uint4*>(dst)[2 * c] = f0.u;
-          reinterpret_cast<uint4*>(dst)[2 * c + 1] = f1.u;
-        }
-        if (qq == 0) tscale[buf][kk] = st_scale;
-      }
-    };
+    const bool have_pool = a.n_pages_pool > 0;
+    uint8_t* const lds_dst0 = &tile[0][kk * kLdsRow + qq * 64];
+    uint8_t* const lds_dst1 = &tile[1][kk * kLdsRow + qq * 64];
 
+    int32_t pend_s = -1;        // column of this lane's deferred scores (-1: none)
+    float pend_v[2] = {0.0f, 0.0f};
+    // Page ids run two pages ahead of the data so that no page-table read is waited on.
+    // (Vector loads: a scalar load would share the LDS completion counter and turn every wait
+    // for a B-fragment read into a wait for the page-table read.)
+    int32_t pid_next = n_tiles > 1 ? pt_row[1] : -1;
     bool ok_cur = false;
-    fetch(0);
-    commit(0);
+    {
+      const int32_t page = pt_row[0];
+      st_ok = page >= 0 && page < a.n_pages_pool;
+      if (have_pool) st.load(a.kcache, st_ok ? page : 0, kk, qq);
+      st.commit(lds_dst0, &tscale[0][kk], qq);
+    }
     ok_cur = st_ok;
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
       const int buf = t & 1;
       const bool more = t + 1 < n_tiles;
-      if (more) fetch(t + 1);
+      if (more) {
+        st_ok = pid_next >= 0 && pid_next < a.n_pages_pool;
+        if (have_pool) st.load(a.kcache, st_ok ? pid_next : 0, kk, qq);
+      }
+      if (t + 2 < n_tiles) pid_next = pt_row[t + 2];
       const int32_t s_tile = t * kTileKeys;
+      // Scores of the previous page go out first, so that they retire behind this page's work
+      // instead of stalling the wait for the next page's loads.
+      if (pend_s >= 0) {
+        if (pend_s < nv_own) out_row[pend_s] = pend_v[0];
+        if (pend_s + 32 < nv_own) out_row[pend_s + 32] = pend_v[1];
+        pend_s = -1;
+      }
       if (mine && s_tile < nv_own) {
+        // Both 32-key halves of the page: the second half's MFMAs overlap the first half's
+        // epilogue.  Keys past this row's visible count are computed but not stored.
+        floatx16 acc[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int32_t s0 = s_tile + 32 * h;
-          if (s0 < nv_own) {
-            Frag kb[8];
-            const uint8_t* srcb = &tile[buf][(32 * h + m) * kLdsRow + 128 * g];
+          Frag kb[8];
+          const uint8_t* srcb = &tile[buf][(32 * h + m) * kLdsRow + 128 * g];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) kb[jj].u = reinterpret_cast<const uint4*>(srcb)[jj];
-            floatx16 acc0 = {}, acc1 = {};
+          for (int jj = 0; jj < 8; ++jj) kb[jj].u = reinterpret_cast<const u32x4*>(srcb)[jj];
+          acc[h][0] = floatx16{};
+          acc[h][1] = floatx16{};
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, kb[jj].v, acc0, 0, 0, 0);
-              acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc1, 0, 0, 0);
-            }
-            float part = 0.0f;
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) part += wv[0][rr] * fmaxf(acc0[rr], 0.0f);
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) part += wv[1][rr] * fmaxf(acc1[rr], 0.0f);
-            float tot = part + __shfl_xor(part, 32, 64);
-            const int32_t s = s0 + m;
-            if constexpr (DT == kFp8) tot *= tscale[buf][32 * h + m];
-            if (g == 0 && s < nv_own) out_row[s] = ok_cur ? tot : -INFINITY;
+          for (int jj = 0; jj < 8; ++jj) {
+            acc[h][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, kb[jj].v, acc[h][0], 0, 0, 0);
+            acc[h][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc[h][1], 0, 0, 0);
           }
         }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float tot = head_sum(acc[h][0], acc[h][1], wv);
+          if constexpr (DT == kFp8) tot *= tscale[buf][32 * h + m];
+          pend_v[h] = ok_cur ? tot : -INFINITY;
+        }
+        if (g == 0) pend_s = s_tile + m;
       }
-      if (more) commit(buf ^ 1);
+      if (more) st.commit(buf ? lds_dst0 : lds_dst1, &tscale[buf ^ 1][kk], qq);
       const bool ok_next = st_ok;
       __syncthreads();
       ok_cur = ok_next;
+    }
+    if (pend_s >= 0) {
+      if (pend_s < nv_own) out_row[pend_s] = pend_v[0];
+      if (pend_s + 32 < nv_own) out_row[pend_s + 32] = pend_v[1];
     }
   }
 }
