@@ -176,11 +176,16 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
  * out_idx  device int32 [n_rows, k]: the column indices of the k largest values (ties to the lower
  *          index) in increasing index order, then -1; out_val (optional) device fp32 [n_rows, k]
  *          their values, then -inf.
+ * workspace device, at least idx_topk_rows_workspace_size(n_rows, row_stride, k) bytes (that size
+ *          is 0, and workspace may be NULL, when every row is selected in one pass: rows of at most
+ *          8192 scores in batches large enough to fill the GPU).
  * Errors: IDX_EINVAL (null pointer, n_rows < 0, row_stride < 1, k < 1 or k > IDX_MAX_TOPK),
- * IDX_EHIP.
+ * IDX_EWORKSPACE, IDX_EHIP.
  */
+size_t idx_topk_rows_workspace_size(int64_t n_rows, int64_t row_stride, int32_t k);
 int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const int32_t* row_len,
-                  int32_t k, int32_t* out_idx, float* out_val, void* stream);
+                  int32_t k, int32_t* out_idx, float* out_val, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

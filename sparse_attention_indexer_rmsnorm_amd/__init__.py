@@ -45,7 +45,8 @@ SIGNATURES = [
       _p, _p, _p]),
     ("idx_logits_dense", ctypes.c_int,
      [_p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _p, _i32, _p]),
-    ("idx_topk_rows", ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _p]),
+    ("idx_topk_rows_workspace_size", _sz, [_i64, _i64, _i32]),
+    ("idx_topk_rows", ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p]),
 ]
 
 
@@ -200,9 +201,12 @@ def topk_rows(scores: torch.Tensor, k: int, row_len: Optional[torch.Tensor] = No
     out_idx = torch.empty((n_rows, k), dtype=torch.int32, device=scores.device)
     out_val = torch.empty((n_rows, k), dtype=torch.float32, device=scores.device) \
         if want_values else None
+    ws_bytes = int(lib().idx_topk_rows_workspace_size(n_rows, stride, int(k)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device) if ws_bytes else None
     st = lib().idx_topk_rows(_dev(scores, "scores", torch.float32), n_rows, stride,
                              _dev(row_len, "row_len", torch.int32, n_rows), int(k),
                              _dev(out_idx, "out_idx", torch.int32),
-                             _dev(out_val, "out_val", torch.float32), _stream(stream))
+                             _dev(out_val, "out_val", torch.float32), _dev(ws, "workspace"),
+                             ws_bytes, _stream(stream))
     _check(st, "idx_topk_rows")
     return out_idx, out_val

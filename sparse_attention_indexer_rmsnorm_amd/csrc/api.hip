@@ -45,19 +45,40 @@ int hip_status(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_EHIP; }
 
 bool dtype_ok(int dtype) { return dtype == IDX_KV_FP8_E4M3 || dtype == IDX_KV_BF16; }
 
-// Workspace layout for `rows` query rows: [row_nvis int32 x rows | pad][scores fp32 rows x cols].
-size_t workspace_for_rows(int64_t rows, int32_t max_pages) {
+// Workspace layout for a chunk of `rows` query rows:
+//   [row_nvis int32 x rows | pad][scores fp32 rows x cols | pad][selection candidates]
+struct WsLayout {
+  size_t nvis, scores, topk, total;
+};
+
+WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k) {
+  WsLayout L{};
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
-  return align_up(static_cast<size_t>(rows) * sizeof(int32_t)) +
-         static_cast<size_t>(rows) * cols * sizeof(float);
+  L.nvis = 0;
+  L.scores = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
+  L.topk = align_up(L.scores + static_cast<size_t>(rows) * cols * sizeof(float));
+  L.total = L.topk + topk_workspace_bytes(rows, static_cast<int64_t>(cols), k);
+  return L;
 }
 
-int64_t rows_fitting(size_t bytes, int32_t max_pages, int64_t n_q) {
-  // largest R <= n_q with workspace_for_rows(R) <= bytes
+// A bound on workspace_layout(rows).total that never decreases with `rows` (fewer rows may be
+// selected in more segments, so the exact size is not monotone): every row reserves the
+// candidate space of a single-row chunk.
+size_t workspace_upper(int64_t rows, int32_t max_pages, int32_t k) {
+  const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
+  const size_t cand_row = topk_workspace_bytes(1, static_cast<int64_t>(cols), k);
+  return static_cast<size_t>(rows) * (cols * sizeof(float) + sizeof(int32_t) + cand_row) +
+         3 * kAlign;
+}
+
+// Query rows per chunk for a workspace of `bytes`: all of them if they fit, else the largest
+// count whose upper bound fits.
+int64_t rows_fitting(size_t bytes, int32_t max_pages, int32_t k, int64_t n_q) {
+  if (workspace_layout(n_q, max_pages, k).total <= bytes) return n_q;
   int64_t lo = 0, hi = n_q;
   while (lo < hi) {
     const int64_t mid = lo + (hi - lo + 1) / 2;
-    if (workspace_for_rows(mid, max_pages) <= bytes) lo = mid; else hi = mid - 1;
+    if (workspace_upper(mid, max_pages, k) <= bytes) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -117,26 +138,27 @@ int logits_topk_impl(const void* q, const float* w, const void* kcache, int dtyp
   if (n_q > 0 && !out_idx) return IDX_EINVAL;
   if (n_q == 0) return IDX_OK;
   if (!workspace) return IDX_EWORKSPACE;
-  const int64_t rows_per_chunk = rows_fitting(workspace_bytes, max_pages, n_q);
+  const int64_t rows_per_chunk = rows_fitting(workspace_bytes, max_pages, k, n_q);
   if (rows_per_chunk < 1) return IDX_EWORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t cols = max_pages * IDX_PAGE_KEYS;
-  int32_t* nvis = static_cast<int32_t*>(workspace);
-  float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           align_up(rows_per_chunk * sizeof(int32_t)));
+  char* ws = static_cast<char*>(workspace);
   ScoreArgs sa = score_args(q, w, kcache, n_pages_pool, page_table, n_seq, max_pages, seq_lens,
                             cu_q);
   sa.n_cols = cols;
-  sa.out = scores;
   sa.out_stride = cols;
   sa.fill_invisible = 0;
-  sa.row_nvis = nvis;
 
   for (int64_t q0 = 0; q0 < n_q; q0 += rows_per_chunk) {
     const int64_t rows = (n_q - q0 < rows_per_chunk) ? n_q - q0 : rows_per_chunk;
+    const WsLayout L = workspace_layout(rows, max_pages, k);
+    int32_t* nvis = reinterpret_cast<int32_t*>(ws + L.nvis);
+    float* scores = reinterpret_cast<float*>(ws + L.scores);
     sa.q_begin = q0;
     sa.n_rows = rows;
+    sa.out = scores;
+    sa.row_nvis = nvis;
     if (cols > 0) {
       plan_chunks(rows, cols, &sa.chunk_keys, &sa.n_chunks);
     } else {
@@ -149,16 +171,9 @@ int logits_topk_impl(const void* q, const float* w, const void* kcache, int dtyp
     if (ev_end && q0 + rows >= n_q &&
         hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
       return IDX_EHIP;
-    TopkArgs ta{};
-    ta.scores = scores;
-    ta.row_stride = cols > 0 ? cols : 1;
-    ta.row_len = nvis;
-    ta.n_rows = rows;
-    ta.k = k;
-    ta.out_idx = out_idx + q0 * k;
-    ta.out_val = out_val ? out_val + q0 * k : nullptr;
-    ta.max_row_len = cols;
-    if (launch_topk(ta, s) != hipSuccess) return IDX_EHIP;
+    if (run_topk(scores, cols > 0 ? cols : 1, nvis, rows, k, out_idx + q0 * k,
+                 out_val ? out_val + q0 * k : nullptr, ws + L.topk, s) != hipSuccess)
+      return IDX_EHIP;
   }
   return IDX_OK;
 }
@@ -214,17 +229,18 @@ int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t*
 
 size_t idx_logits_topk_workspace_size(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t k) {
   (void)n_seq;
-  (void)k;
-  if (n_q <= 0 || max_pages < 0) return align_up(sizeof(int32_t));
-  const int64_t cap_rows = rows_fitting(kWorkspaceCap, max_pages, n_q);
-  const int64_t rows = cap_rows < 1 ? 1 : cap_rows;
-  return workspace_for_rows(rows, max_pages);
+  if (k < 1) k = 1;
+  if (max_pages < 0) max_pages = 0;
+  if (n_q <= 0) return align_up(sizeof(int32_t));
+  const size_t all = workspace_layout(n_q, max_pages, k).total;
+  if (all <= kWorkspaceCap) return all;
+  const int64_t cap_rows = rows_fitting(kWorkspaceCap, max_pages, k, n_q);
+  return workspace_upper(cap_rows < 1 ? 1 : cap_rows, max_pages, k);
 }
 
 size_t idx_logits_topk_min_workspace(int32_t n_seq, int32_t max_pages, int32_t k) {
   (void)n_seq;
-  (void)k;
-  return workspace_for_rows(1, max_pages < 0 ? 0 : max_pages);
+  return workspace_upper(1, max_pages < 0 ? 0 : max_pages, k < 1 ? 1 : k);
 }
 
 int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype,
@@ -271,22 +287,22 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
   return hip_status(score_launch(sa, dtype, static_cast<hipStream_t>(stream)));
 }
 
+size_t idx_topk_rows_workspace_size(int64_t n_rows, int64_t row_stride, int32_t k) {
+  if (n_rows <= 0 || row_stride < 1 || k < 1) return 0;
+  return topk_workspace_bytes(n_rows, row_stride, k);
+}
+
 int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const int32_t* row_len,
-                  int32_t k, int32_t* out_idx, float* out_val, void* stream) {
+                  int32_t k, int32_t* out_idx, float* out_val, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   if (n_rows < 0 || row_stride < 1 || k < 1 || k > IDX_MAX_TOPK) return IDX_EINVAL;
   if (n_rows > INT32_MAX || row_stride > INT32_MAX) return IDX_EINVAL;
   if (n_rows == 0) return IDX_OK;
   if (!scores || !out_idx) return IDX_EINVAL;
-  TopkArgs ta{};
-  ta.scores = scores;
-  ta.row_stride = row_stride;
-  ta.row_len = row_len;
-  ta.n_rows = n_rows;
-  ta.k = k;
-  ta.out_idx = out_idx;
-  ta.out_val = out_val;
-  ta.max_row_len = static_cast<int32_t>(row_stride);
-  return hip_status(launch_topk(ta, static_cast<hipStream_t>(stream)));
+  const size_t need = topk_workspace_bytes(n_rows, row_stride, k);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return IDX_EWORKSPACE;
+  return hip_status(run_topk(scores, row_stride, row_len, n_rows, k, out_idx, out_val, workspace,
+                             static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

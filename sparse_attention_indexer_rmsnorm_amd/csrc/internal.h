@@ -73,11 +73,29 @@ struct TopkArgs {
   const int32_t* row_len;    // [n_rows] or null (= row_stride)
   int64_t n_rows;
   int32_t k;
-  int32_t* out_idx;          // [n_rows, k]
-  float* out_val;            // [n_rows, k] or null
-  int32_t max_row_len;       // upper bound on row lengths (sizes the LDS row cache)
+  int32_t* out_idx;          // [n_rows * n_seg, k]
+  float* out_val;            // [n_rows * n_seg, k] or null
+  int32_t n_seg;             // segments per row, each selected by its own wave (1 = whole row)
+  int32_t seg_len;           // elements per segment when n_seg > 1
+  const int32_t* src_idx;    // [n_rows, row_stride] reported indices (< 0: padding), or null
+  int32_t pad_bits;          // 1: pad short outputs with a NaN pattern (intermediate candidate
+                             //    lists, read back by a later pass), 0: with -inf (final output)
 };
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+// Largest row segment one wave selects from (64 lanes x 96 keys in registers).
+constexpr int32_t kMaxSegment = 96 * 64;
+
+struct TopkPlan {
+  int passes;                // selection passes (1: each row in one wave)
+  int64_t cand_elems;        // widest candidate row between passes
+};
+
+TopkPlan topk_plan(int64_t n_rows, int64_t cols, int32_t k);
+// Workspace the selection of n_rows rows of `cols` scores needs (0 for one pass).
+size_t topk_workspace_bytes(int64_t n_rows, int64_t cols, int32_t k);
+// Top-k of every row (ties to the lower index, output sorted by index, -1 / -inf padding).
+hipError_t run_topk(const float* scores, int64_t row_stride, const int32_t* row_len,
+                    int64_t n_rows, int32_t k, int32_t* out_idx, float* out_val, void* ws,
+                    hipStream_t stream);
 
 }  // namespace dsa

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), f"missing export {n}"
     assert sorted(n for n, _, _ in ix.SIGNATURES) == names
@@ -40,17 +40,24 @@ def test_page_bytes(L):
 
 
 def test_workspace_sizes(L):
-    # decode batch of 32 queries over 512 pages: one row of 32768 fp32 scores each + counts
-    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == 256 + 32 * 32768 * 4
-    # long prefill chunk: 8192 queries x 5632 keys fits the 256 MiB cap in one pass
+    # decode batch of 32 queries over 512 pages: a row of 32768 fp32 scores each plus visible
+    # counts, plus two candidate buffers for a two-pass selection (6 segments of <= 6144 scores,
+    # k (index, value) candidates each)
+    scores = 256 + 32 * 32768 * 4
+    cand = 2 * (32 * 6 * 1024 * 8 + 256)
+    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == scores + cand
+    # long prefill chunk: 8192 queries x 5632 keys fits the 256 MiB cap in one pass, one-pass top-k
     ws = L.idx_logits_topk_workspace_size(8192, 1, 88, 512)
     assert ws == 8192 * 4 + 8192 * 5632 * 4 and ws <= 256 << 20
     # a 128K-token prefill of 8192 queries is chunked to stay under the cap
     big = L.idx_logits_topk_workspace_size(8192, 1, 2048, 512)
     assert big <= 256 << 20 and big >= 131072 * 4
-    assert L.idx_logits_topk_min_workspace(1, 88, 512) == 256 + 5632 * 4
+    assert L.idx_logits_topk_min_workspace(1, 88, 512) >= 256 + 5632 * 4
     # never depends on the head count: the per-head tensor is never formed
     assert L.idx_logits_topk_workspace_size(8192, 1, 88, 512) < 8192 * 5632 * 64 * 4 / 50
+    # stand-alone selection: one pass needs none; long rows of a small batch need candidates
+    assert L.idx_topk_rows_workspace_size(8192, 5632, 512) == 0
+    assert L.idx_topk_rows_workspace_size(32, 32768, 1024) > 0
 
 
 def _store(L, **kw):
@@ -114,12 +121,14 @@ def test_logits_dense_validation(L):
 
 def test_topk_rows_validation(L):
     f = L.idx_topk_rows
-    assert f(FAKE, 4, 0, None, 10, FAKE, None, None) == E_INVAL     # row_stride < 1
-    assert f(FAKE, 4, 100, None, 0, FAKE, None, None) == E_INVAL
-    assert f(FAKE, 4, 100, None, 4096, FAKE, None, None) == E_INVAL
-    assert f(None, 4, 100, None, 10, FAKE, None, None) == E_INVAL
-    assert f(FAKE, -1, 100, None, 10, FAKE, None, None) == E_INVAL
-    assert f(None, 0, 100, None, 10, None, None, None) == E_OK
+    assert f(FAKE, 4, 0, None, 10, FAKE, None, None, 0, None) == E_INVAL     # row_stride < 1
+    assert f(FAKE, 4, 100, None, 0, FAKE, None, None, 0, None) == E_INVAL
+    assert f(FAKE, 4, 100, None, 4096, FAKE, None, None, 0, None) == E_INVAL
+    assert f(None, 4, 100, None, 10, FAKE, None, None, 0, None) == E_INVAL
+    assert f(FAKE, -1, 100, None, 10, FAKE, None, None, 0, None) == E_INVAL
+    assert f(None, 0, 100, None, 10, None, None, None, 0, None) == E_OK
+    # a two-pass selection without its workspace
+    assert f(FAKE, 4, 40000, None, 1024, FAKE, None, None, 0, None) == E_WS
 
 
 def test_binding_rejects_host_tensors():

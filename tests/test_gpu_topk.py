@@ -53,8 +53,8 @@ def test_topk_rows_bit_exact(oracle_mod, n_rows, stride, k, kind):
         assert np.array_equal(gi[r, :m], np.sort(oi[r, :m])), f"row {r}"
         assert np.all(gi[r, m:] == -1)
         order = np.argsort(oi[r, :m])
-        assert np.array_equal(gv[r, :m].view(np.uint32),
-                              ov[r, :m][order].astype(np.float32).view(np.uint32))
+        # values equal (a -0 score is returned as +0)
+        assert np.array_equal(gv[r, :m], ov[r, :m][order].astype(np.float32))
         assert np.all(np.isneginf(gv[r, m:]))
 
 
@@ -144,3 +144,26 @@ def test_logits_topk_repeatable():
     a, _ = _gpu_topk(wl, d, pool, FP8)
     b, _ = _gpu_topk(wl, d, pool, FP8)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,k", [(FP8, 512), (BF16, 1024), (FP8, 64)])
+def test_two_pass_selection_matches_one_pass(dtype, k):
+    """Decode-shaped batches select each row in segments, then among the segments' candidates.
+    Rows shorter than k, a row spanning few segments, and keys on an invalid page (-inf) included;
+    the result must equal a one-pass selection over the dense logits, bit for bit."""
+    r = np.random.default_rng(40 + k)
+    lens = r.integers(8, 60000, 24).astype(np.int32)
+    lens[:3] = [12, 4 * k - 4, 4 * k + 8]             # n_vis < k, just below and above k
+    wl = W.make_workload("decode-ragged", 77 + k, lens, np.ones(lens.size, np.int32), k,
+                         permute_pages=True, max_pages=240)
+    wl.page_table[5, 3] = wl.n_pages_pool + 7           # keys 192..255 of row 5 score -inf
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, dtype, d)
+    gi, gv = _gpu_topk(wl, d, pool, dtype, want_values=True)
+    dense = ix.logits_dense(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
+                            d["cu_q"], wl.max_keys)
+    t = wl.query_positions()
+    nv = torch.from_numpy(np.minimum((t + 1) // 4, wl.max_keys).astype(np.int32)).cuda()
+    si, sv = ix.topk_rows(dense, wl.k, nv)
+    assert torch.equal(gi, si)
+    assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
