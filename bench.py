@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,6 +41,36 @@ WORKLOADS = {
     "decode-32x128k-bf16": (4, 1),
 }
 DEFAULT = "prefill-22k-chunk8192-bf16"
+
+
+# Sources that determine each kernel's machine code: a committed counter summary for a kernel is
+# used only while its digest over these files still matches.
+KERNEL_SOURCES = {
+    "score_rows_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
+    "score_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
+}
+
+
+def sources_digest(kernel: str) -> str:
+    import hashlib  # noqa: PLC0415
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(HERE, "sparse_attention_indexer_rmsnorm_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload`, from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary committed under profiles/ (already scaled by the copy-kernel calibration), or None if
+    there is none or the kernel's sources have changed since the counters were taken."""
+    path = os.path.join(HERE, "profiles", f"{kernel}-{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]+)`", open(path).read(), re.M))
+    if fields.get("sources_digest") != sources_digest(kernel) or "traffic_bytes" not in fields:
+        return None
+    return int(fields["traffic_bytes"])
 
 
 def _pairs(wl) -> int:
@@ -172,7 +203,10 @@ def main() -> int:
         achieved = flops / (score_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = "score_kernel"
+    # the prefill-shaped batch runs the LDS-tiled rows kernel, a decode batch the split kernel
+    kernel = "score_kernel" if cfg in (2, 4) else "score_rows_kernel"
+    roof["traffic"] = committed_traffic(kernel, wl.name)
+    roof["kernel"] = kernel
     roof["kernel_ms"] = round(score_ms, 4)
 
     line = {
