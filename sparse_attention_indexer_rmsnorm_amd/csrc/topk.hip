@@ -11,14 +11,16 @@
 //
 // Within a wave (no workgroup barriers anywhere):
 //   1. the segment's scores become order-preserving uint32 keys (-0 folded onto +0) held in
-//      registers, lane-strided (element e = 64 j + lane), all loads in flight together;
-//   2. a 256-bin histogram (wave-private LDS) of the top 8 key bits -- sign and exponent, one
-//      bit-extract and one LDS add per key -- gives the digit D holding the k-th largest key;
-//      every key in a higher digit is selected;
-//   3. the keys of digit D (a small fraction of the row) are gathered into LDS by ballot
-//      compaction, and three more 8-bit passes over them alone yield the k-th largest key T and
-//      how many keys equal to T to take (when digit D is too full for LDS, the passes filter the
-//      registers instead);
+//      registers, lane-strided (element e = 64 j + lane), all loads in flight together; a wave
+//      reduction gives the smallest and largest key;
+//   2. a 4096-bin histogram (wave-private LDS, 16-bit counts packed two to a word) of the keys'
+//      offsets above the smallest key, shifted so that the row's key range fills the bins, gives
+//      the bin B holding the k-th largest key; every key in a higher bin is selected.  Because the
+//      bins follow the row's own range, one wave's LDS adds land on many different addresses;
+//   3. the keys of bin B (a small fraction of the row) are gathered into the same LDS area by
+//      ballot compaction, and 7-bit radix passes over their remaining low bits yield the k-th
+//      largest key T and how many keys equal to T to take (when bin B holds more keys than the
+//      area, the passes filter the registers instead);
 //   4. one pass compacts, in increasing index order, every key > T and the lowest-indexed keys
 //      == T, with ballots, writing the winners from registers: the output is unique and
 //      deterministic, ties to the lower index, each row sorted by index (values are returned
@@ -28,8 +30,16 @@
 namespace dsa {
 namespace {
 
-constexpr int kWaveCand = 2048;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBinBits = 12;
+constexpr int kBins = 1 << kBinBits;          // fine histogram bins per wave
+constexpr int kAreaWords = kBins / 2;         // 8 KiB per wave: histogram, then candidates, then slots
+constexpr int kWaveCand = kAreaWords;         // candidate keys that fit the area
 constexpr int kMaxTopk = 2048;
+constexpr int kSubBits = 7;                   // refinement digit width
+constexpr int kSubBins = 1 << kSubBits;
+static_assert(kMaxTopk * 2 <= kAreaWords * 4, "winner slots must fit the area");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -46,11 +56,40 @@ __device__ __forceinline__ float key_value(uint32_t u) {
 }
 
 // Hide a value from the optimiser (emits nothing): per-key values derived in one pass are then
-// recomputed in the next instead of being kept live, which would triple the registers per key.
+// recomputed in the next instead of being kept live, which would multiply the registers per key.
 template <int N>
 __device__ __forceinline__ void launder(uint32_t (&v)[N]) {
 #pragma unroll
   for (int j = 0; j < N; ++j) asm volatile("" : "+v"(v[j]));
+}
+
+// Make v depend on the scalar s (emits nothing).  Chaining each iteration of a ballot loop to the
+// previous iteration's count keeps the compiler from evaluating every iteration's ballot up front,
+// which would need two SGPRs per key and spill them.
+__device__ __forceinline__ uint32_t after(uint32_t v, uint32_t s) {
+  asm volatile("" : "+v"(v) : "s"(s));
+  return v;
+}
+
+// A copy of a wave-uniform value the compiler cannot identify with the original (emits nothing):
+// the loops below each test their group index against a fresh copy, so the per-group results of
+// one loop are not kept alive for the next.
+__device__ __forceinline__ int32_t fresh(int32_t v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// Raw buffer view of n floats at p (p wave-uniform): loads whose (vector + immediate) offset lies
+// at or past the end return 0 without touching memory, so a wave loads whole 64-slot groups with
+// no clamping.  The scalar offset is not range-checked, so it stays 0.  Word 3 of a gfx9-family
+// descriptor selects 32-bit elements.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const float* p, int32_t n) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, n * 4, 0x00020000);
 }
 
 // Number of lanes below this one whose bit is set in `mask` (wave64).
@@ -59,103 +98,141 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, int lane) {
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x - v;
+// Cross-lane steps with DPP (no LDS traffic).  dpp<ctrl, row_mask>(x, id) returns, per lane, x of
+// the lane the control selects, or id where there is none (outside the 16-lane row, or in a row
+// the mask leaves out).  Controls: row_shr:n = 0x110 + n; row_bcast:15 = 0x142 (lane 15 of each
+// row to the next row); row_bcast:31 = 0x143 (lane 31 to rows 2 and 3).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t x, uint32_t id) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(x),
+                                                           CTRL, ROW_MASK, 0xF, false));
 }
 
-// Among nb bins (nb a multiple of 64), the descending digit holding the rank-`want` largest entry
-// and the number of entries in higher digits.  Lane l owns digits nb-1-l*per .. nb-per-l*per.
-__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, int nb, uint32_t want,
-                                                int lane, uint32_t* digit, uint32_t* above) {
-  const int per = nb / 64;
+// Inclusive wave scan with an associative op and its identity.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp<0x111, 0xF>(x, id));
+  x = op(x, dpp<0x112, 0xF>(x, id));
+  x = op(x, dpp<0x114, 0xF>(x, id));
+  x = op(x, dpp<0x118, 0xF>(x, id));
+  x = op(x, dpp<0x142, 0xA>(x, id));
+  x = op(x, dpp<0x143, 0xC>(x, id));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, int /*lane*/) {
+  return wave_incl_scan(v, 0u, [](uint32_t p, uint32_t q) { return p + q; }) - v;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  v = wave_incl_scan(v, 0xFFFFFFFFu, [](uint32_t p, uint32_t q) { return p < q ? p : q; });
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = wave_incl_scan(v, 0u, [](uint32_t p, uint32_t q) { return p > q ? p : q; });
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Value of x in lane src (src wave-uniform).
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int src) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), src));
+}
+
+// Descending scan of the packed fine histogram (bin 2w in the low half of word w, bin 2w+1 in the
+// high half): the bin holding the want-th largest key, the count in higher bins and the bin's own
+// count.  Lane l first sums words [kAreaWords - 32 (l+1), kAreaWords - 32 l); the lane whose block
+// holds the crossing then has its 32 words spread over lanes 0..31 for the exact bin.
+__device__ __forceinline__ void wave_find_bin(const uint32_t* words, uint32_t want, int lane,
+                                              uint32_t* bin, uint32_t* above, uint32_t* count) {
+  const int lo_word = kAreaWords - 32 * (lane + 1);
+  const u32x4* blk = reinterpret_cast<const u32x4*>(words + lo_word);
   uint32_t local = 0;
-  for (int p = 0; p < per; ++p) local += hist[nb - 1 - (lane * per + p)];
-  uint32_t run = wave_excl_scan(local, lane);
-  uint32_t d_found = 0, a_found = 0;
-  bool hit = false;
-  for (int p = 0; p < per; ++p) {
-    const int d = nb - 1 - (lane * per + p);
-    const uint32_t c = hist[d];
-    if (!hit && run < want && run + c >= want) {
-      hit = true;
-      d_found = static_cast<uint32_t>(d);
-      a_found = run;
-    }
-    run += c;
-  }
-  const uint64_t m = __ballot(hit);
-  const int src = m ? __builtin_ctzll(m) : 0;
-  *digit = __shfl(d_found, src, 64);
-  *above = __shfl(a_found, src, 64);
-}
-
-// Exact select within top digit d0: the k_rem-th largest key T among the keys v[0..N) of every
-// lane for which take(j) holds (all of them have top byte d0), and how many keys equal to T belong
-// to the top k_rem.  Three passes of 8-bit digits.
-template <int N, typename Take>
-__device__ __forceinline__ void wave_radix_select(const uint32_t (&v)[N], Take take, uint32_t d0,
-                                                  uint32_t k_rem, uint32_t* hist, int lane,
-                                                  uint32_t* T_out, uint32_t* eq_take) {
-  uint32_t prefix = d0;
-#pragma unroll 1
-  for (int pass = 1; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int d = lane; d < 256; d += 64) hist[d] = 0;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      if (take(j) && (v[j] >> (shift + 8)) == prefix) atomicAdd(&hist[(v[j] >> shift) & 255u], 1u);
-    }
-    uint32_t d, gt;
-    wave_find_digit(hist, 256, k_rem, lane, &d, &gt);
-    prefix = (prefix << 8) | d;
-    k_rem -= gt;
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 w = blk[i];
+    local += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) +
+             (w.z & 0xFFFFu) + (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
   }
-  *T_out = prefix;
-  *eq_take = k_rem;
+  const uint32_t run = wave_excl_scan(local, lane);
+  const uint64_t hm = __ballot(run < want && run + local >= want);
+  const int L = __builtin_amdgcn_readfirstlane(hm ? __builtin_ctzll(hm) : 0);
+  const uint32_t run_l = lane_value(run, L);
+  // level 2: lane i < 32 takes word (top of block L) - i
+  const int wi = kAreaWords - 32 * L - 1 - (lane & 31);
+  const uint32_t word = lane < 32 ? words[wi] : 0u;
+  const uint32_t hi = word >> 16, lo = word & 0xFFFFu;
+  const uint32_t r2 = run_l + wave_excl_scan(hi + lo, lane);
+  // the high half (the larger bin) comes first in descending order
+  const bool hit_hi = lane < 32 && r2 < want && r2 + hi >= want;
+  const bool hit_lo = lane < 32 && r2 + hi < want && r2 + hi + lo >= want;
+  const uint64_t m = __ballot(hit_hi || hit_lo);
+  const int src = __builtin_amdgcn_readfirstlane(m ? __builtin_ctzll(m) : 0);
+  const uint32_t b = hit_hi ? 2u * static_cast<uint32_t>(wi) + 1u : 2u * static_cast<uint32_t>(wi);
+  const uint32_t a = hit_hi ? r2 : r2 + hi;
+  const uint32_t c = hit_hi ? hi : lo;
+  *bin = lane_value(b, src);
+  *above = lane_value(a, src);
+  *count = lane_value(c, src);
 }
 
-// The same over m candidate keys held in LDS.
-__device__ __forceinline__ void wave_radix_select_lds(const uint32_t* cand, uint32_t m, uint32_t d0,
-                                                      uint32_t k_rem, uint32_t* hist, int lane,
-                                                      uint32_t* T_out, uint32_t* eq_take) {
-  uint32_t prefix = d0;
+// Among kSubBins bins, the descending digit holding the rank-`want` largest entry and the number
+// of entries in higher digits.  Lane l owns digits kSubBins-1-2l and kSubBins-2-2l.
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t want, int lane,
+                                                uint32_t* digit, uint32_t* above) {
+  static_assert(kSubBins == 128, "two digits per lane");
+  const uint32_t c0 = hist[kSubBins - 1 - 2 * lane];
+  const uint32_t c1 = hist[kSubBins - 2 - 2 * lane];
+  const uint32_t run = wave_excl_scan(c0 + c1, lane);
+  const bool h0 = run < want && run + c0 >= want;
+  const bool h1 = run + c0 < want && run + c0 + c1 >= want;
+  const uint64_t m = __ballot(h0 || h1);
+  const int src = __builtin_amdgcn_readfirstlane(m ? __builtin_ctzll(m) : 0);
+  const uint32_t d = h0 ? static_cast<uint32_t>(kSubBins - 1 - 2 * lane)
+                        : static_cast<uint32_t>(kSubBins - 2 - 2 * lane);
+  *digit = lane_value(d, src);
+  *above = lane_value(h0 ? run : run + c0, src);
+}
+
+// Exact select inside fine bin B: the k_rem-th largest offset (key - kmin) among the selected
+// keys, whose offsets all share the bits above `bits`, and how many keys equal to it belong to the
+// top k_rem.  Radix passes of up to 7 bits, high to low.  `offset_of(i, &d)` yields candidate i's
+// offset and whether it is a candidate at all; `count` candidates are visited per lane loop.
+template <typename Visit>
+__device__ __forceinline__ void refine(Visit visit, uint32_t prefix, int bits, uint32_t k_rem,
+                                       uint32_t* sub, int lane, uint32_t* off_out,
+                                       uint32_t* eq_take) {
 #pragma unroll 1
-  for (int pass = 1; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int d = lane; d < 256; d += 64) hist[d] = 0;
-    for (uint32_t i = lane; i < m; i += 64) {
-      const uint32_t v = cand[i];
-      if ((v >> (shift + 8)) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
-    }
+  while (bits > 0) {
+    const int w = bits < kSubBits ? bits : kSubBits;
+    const int shift = bits - w;
+    sub[lane] = 0u;
+    sub[lane + 64] = 0u;
+    visit([&](uint32_t off) {
+      if ((off >> bits) == prefix) atomicAdd(&sub[(off >> shift) & ((1u << w) - 1u)], 1u);
+    });
     uint32_t d, gt;
-    wave_find_digit(hist, 256, k_rem, lane, &d, &gt);
-    prefix = (prefix << 8) | d;
+    wave_find_digit(sub, k_rem, lane, &d, &gt);
+    prefix = (prefix << w) | d;
     k_rem -= gt;
+    bits = shift;
   }
-  *T_out = prefix;
+  *off_out = prefix;
   *eq_take = k_rem;
 }
 
 template <int E, bool HAS_IDX>
 __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
-  __shared__ uint32_t hist_all[4][256];
-  __shared__ uint32_t cand_all[4][kWaveCand];
-  __shared__ uint16_t sel_all[4][kMaxTopk];
+  __shared__ __attribute__((aligned(16))) uint32_t area_all[4][kAreaWords];
+  __shared__ uint32_t sub_all[4][kSubBins];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + wid;
   if (task >= a.n_rows * a.n_seg) return;
   const int64_t r = task / a.n_seg;
   const int32_t seg = static_cast<int32_t>(task % a.n_seg);
-  uint32_t* hist = hist_all[wid];
-  uint32_t* cand = cand_all[wid];
-  uint16_t* sel = sel_all[wid];
+  uint32_t* area = area_all[wid];
+  uint32_t* sub = sub_all[wid];
 
   int64_t len = a.row_len ? static_cast<int64_t>(a.row_len[r]) : a.row_stride;
   len = len < 0 ? 0 : (len > a.row_stride ? a.row_stride : len);
@@ -165,7 +242,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
     n64 = len - base_e;
     n64 = n64 < 0 ? 0 : (n64 > a.seg_len ? a.seg_len : n64);
   }
-  const int32_t n = static_cast<int32_t>(n64);
+  const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(n64));   // wave-uniform
   const int32_t k = a.k;
   const float* row = a.scores + r * a.row_stride + base_e;
   const int32_t* ridx = HAS_IDX ? a.src_idx + r * a.row_stride + base_e : nullptr;
@@ -198,74 +275,120 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
     return;
   }
 
-  // 1. keys in registers (key 0: past the end or padding, below every real key incl. -inf's).
-  //    All loads first, unconditionally (clamped index), so that they are in flight together.
+  // 1. keys in registers, all loads first (buffer loads, in range or returning 0) so that they are
+  //    in flight together.  Slots past the end hold key 0 like padding entries.  Key 0 is the lowest
+  //    key, and equal keys are taken in index order, so a slot past the end is never selected
+  //    (n > k real entries precede it); whole 64-slot groups past the end are skipped below with
+  //    a wave-uniform test, and the group holding the end is processed like any other.
   uint32_t u[E];
+  {
+    const __amdgpu_buffer_rsrc_t view = buffer_view(row, n);
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int32_t e = j * 64 + lane;
-    u[j] = __float_as_uint(row[e < n ? e : n - 1]);   // n > k >= 1 here
+    for (int j = 0; j < E; ++j)
+      u[j] = __builtin_amdgcn_raw_buffer_load_b32(view, lane * 4 + j * 256, 0, 0);
   }
   launder(u);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < E; ++j)
+  for (int j = 0; j < E; ++j) {
     u[j] = j * 64 + lane < n ? order_key(__uint_as_float(u[j])) : 0u;
+    kmin = min(kmin, u[j] ? u[j] : 0xFFFFFFFFu);
+    kmax = max(kmax, u[j]);
+  }
+  // offsets: key 0 -> 0, other keys -> key - kmin + 1 >= 1 (order preserved)
+  const uint32_t kbase = wave_min(kmin) - 1u;
+  kmax = wave_max(kmax);
+  const uint32_t top_off = kmax ? kmax - kbase : 0u;
+  const int span = top_off ? 32 - __builtin_clz(top_off) : 0;
+  const int shift = span > kBinBits ? span - kBinBits : 0;   // (top_off >> shift) < kBins
+  auto off_of = [&](uint32_t key) { return key ? key - kbase : 0u; };
+  const int32_t groups = (n + 63) >> 6;       // 64-slot groups holding entries
 
-  // 2. histogram of the top 8 key bits (sign + 7 exponent bits): the digit D holding the k-th
-  //    largest key; everything in higher digits is selected.  Out-of-range slots carry key 0 and
-  //    land in digit 0, which the scan only reaches if the row holds fewer than k real keys (it
-  //    cannot: n > k).
-  for (int d = lane; d < 256; d += 64) hist[d] = 0;
+  // 2. fine histogram of the offsets
 #pragma unroll
-  for (int j = 0; j < E; ++j) atomicAdd(&hist[u[j] >> 24], 1u);
-  uint32_t dD, above;
-  wave_find_digit(hist, 256, static_cast<uint32_t>(k), lane, &dD, &above);
-  const uint32_t c_d = hist[dD] - (dD == 0u ? static_cast<uint32_t>(E * 64 - n) : 0u);
-  const uint32_t k_rem = static_cast<uint32_t>(k) - above;    // 1 <= k_rem <= c_d
+  for (int i = 0; i < kAreaWords / 256; ++i)
+    reinterpret_cast<u32x4*>(area)[i * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+  launder(u);
+  {
+    const int32_t ng = fresh(groups);
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (j < ng) {
+      const uint32_t b = off_of(after(u[j], 0u)) >> shift;   // computed here, not hoisted
+      atomicAdd(&area[b >> 1], 1u << ((b & 1u) << 4));
+    }
+  }
+  }
+  uint32_t bB, above, c_b;
+  wave_find_bin(area, static_cast<uint32_t>(k), lane, &bB, &above, &c_b);
+  const uint32_t k_rem = static_cast<uint32_t>(k) - above;    // 1 <= k_rem <= c_b
 
-  // 3. exact threshold among the keys of digit D: gathered into LDS (ballot compaction) when they
-  //    fit, otherwise filtered in registers; three more 8-bit passes.
-  uint32_t T, eq_take;
-  if (c_d <= static_cast<uint32_t>(kWaveCand)) {
+  // 3. exact threshold among the offsets in bin B: gathered into the area (ballot compaction)
+  //    when they fit, otherwise filtered in registers.
+  uint32_t t_off, eq_take;
+  launder(u);
+  if (c_b <= static_cast<uint32_t>(kWaveCand)) {
     uint32_t cnt = 0;
+    const int32_t ng = fresh(groups);
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const bool ind = (u[j] >> 24) == dD && j * 64 + lane < n;
-      const uint64_t m = __ballot(ind);
-      if (ind) cand[cnt + lanes_below(m)] = u[j];
-      cnt += static_cast<uint32_t>(__popcll(m));
+      if (j < ng) {
+        const uint32_t o = off_of(after(u[j], cnt));
+        const bool ind = (o >> shift) == bB;
+        const uint64_t m = __ballot(ind);
+        if (ind) area[cnt + lanes_below(m)] = o;
+        cnt += static_cast<uint32_t>(__popcll(m));
+      }
     }
-    wave_radix_select_lds(cand, c_d, dD, k_rem, hist, lane, &T, &eq_take);
+    refine([&](auto add) {
+             for (uint32_t i = lane; i < c_b; i += 64) add(area[i]);
+           },
+           bB, shift, k_rem, sub, lane, &t_off, &eq_take);
   } else {
-    wave_radix_select(u, [&](int j) { return (u[j] >> 24) == dD && j * 64 + lane < n; }, dD,
-                      k_rem, hist, lane, &T, &eq_take);
+    refine([&](auto add) {
+             const int32_t ng = fresh(groups);
+#pragma unroll
+             for (int j = 0; j < E; ++j) {
+               if (j < ng) {
+                 const uint32_t o = off_of(after(u[j], 0u));   // recomputed every pass
+                 if ((o >> shift) == bB) add(o);
+               }
+             }
+           },
+           bB, shift, k_rem, sub, lane, &t_off, &eq_take);
   }
-  const uint32_t n_gt = static_cast<uint32_t>(k) - eq_take;
+  const uint32_t T = t_off ? t_off + kbase : 0u;
 
   // 4. compaction in index order: a key > T goes to (#keys > T before it) + (#selected keys == T
   //    before it); a key == T is selected while fewer than eq_take equal keys precede it.  Values
   //    come from the keys (-0 is returned as +0); candidate lists record positions for step 5.
+  uint16_t* sel = reinterpret_cast<uint16_t*>(area);
   launder(u);
   uint32_t gt_seen = 0, eq_seen = 0;
+  const int32_t ng = fresh(groups);
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const int32_t e = j * 64 + lane;
-    const bool gtv = e < n && u[j] > T;
-    const bool eqv = e < n && u[j] == T;
-    const uint64_t mg = __ballot(gtv);
-    const uint64_t me = __ballot(eqv);
-    const uint32_t gpre = gt_seen + lanes_below(mg);
-    const uint32_t epre = eq_seen + lanes_below(me);
-    uint32_t pos = 0xFFFFFFFFu;
-    if (gtv) pos = gpre + (epre < eq_take ? epre : eq_take);
-    else if (eqv && epre < eq_take) pos = gpre + epre;
-    if (pos < static_cast<uint32_t>(k)) {
-      if constexpr (HAS_IDX) sel[pos] = static_cast<uint16_t>(e);
-      else oi[pos] = static_cast<int32_t>(base_e + e);
-      if (ov) ov[pos] = u[j] ? key_value(u[j]) : pad_val;   // key 0: a padding entry
+    if (j < ng) {
+      const int32_t e = j * 64 + lane;
+      const uint32_t uj = after(u[j], gt_seen + eq_seen);
+      const bool gtv = uj > T;
+      const bool eqv = uj == T;
+      const uint64_t mg = __ballot(gtv);
+      const uint64_t me = __ballot(eqv);
+      const uint32_t gpre = gt_seen + lanes_below(mg);
+      const uint32_t epre = eq_seen + lanes_below(me);
+      uint32_t pos = 0xFFFFFFFFu;
+      if (gtv) pos = gpre + (epre < eq_take ? epre : eq_take);
+      else if (eqv && epre < eq_take) pos = gpre + epre;
+      if (pos < static_cast<uint32_t>(k)) {
+        if constexpr (HAS_IDX)   // the slot number is formed here rather than kept per key
+          sel[pos] = static_cast<uint16_t>(after(static_cast<uint32_t>(lane), 0u) + j * 64);
+        else oi[pos] = static_cast<int32_t>(base_e + e);
+        if (ov) ov[pos] = uj ? key_value(uj) : pad_val;   // key 0: a padding entry
+      }
+      gt_seen += static_cast<uint32_t>(__popcll(mg));
+      eq_seen += static_cast<uint32_t>(__popcll(me));
     }
-    gt_seen += static_cast<uint32_t>(__popcll(mg));
-    eq_seen += static_cast<uint32_t>(__popcll(me));
   }
   // 5. candidate lists: the winners' original indices, gathered 8 per lane at a time
   if constexpr (HAS_IDX) {
