@@ -31,8 +31,10 @@ bool prefill_shaped(int64_t n_rows, int32_t n_seq) {
 }
 
 hipError_t score_launch(const ScoreArgs& a, int dtype, hipStream_t s) {
-  return prefill_shaped(a.n_rows, a.n_seq) ? launch_score_rows(a, dtype, s)
-                                           : launch_score(a, dtype, s);
+  // the rows kernel stages pages unconditionally, so it needs at least one page in the pool
+  return prefill_shaped(a.n_rows, a.n_seq) && a.n_pages_pool > 0
+             ? launch_score_rows(a, dtype, s)
+             : launch_score(a, dtype, s);
 }
 
 RopeFreq rope_table() {

@@ -47,6 +47,18 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
       reinterpret_cast<uintptr_t>(p));
 }
 
+// Raw buffer view of n floats at p (p wave-uniform).  Stores whose (vector + immediate) offset
+// lies at or past the end are dropped by the hardware, so a wave can store whole tiles without
+// clamping; the scalar offset is not range-checked and stays 0.  Word 3 of a gfx9-family
+// descriptor selects 32-bit elements.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(float* p, int64_t n) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
+  void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(n * 4), 0x00020000);
+}
+
 // Sequence of flattened query row i: the last b with cu_q[b] <= i (binary search), or -1 when i
 // lies outside every [cu_q[b], cu_q[b+1]).
 __device__ __forceinline__ int32_t seq_of_row(const int32_t* cu_q, int32_t n_seq, int64_t i) {
@@ -80,7 +92,12 @@ __device__ __forceinline__ float head_sum(const floatx16& acc0, const floatx16& 
   for (int rr = 0; rr < 16; ++rr)
     p[rr & 3] = fmaf(relu(acc1[rr]), wv[1][rr], p[rr & 3]);
   const float part = (p[0] + p[1]) + (p[2] + p[3]);
-  return part + __shfl_xor(part, 32, 64);
+  // v_permlane32_swap with both operands = part: the first result holds the low half's partial
+  // sums in both halves, the second the high half's, so their sum is the key's total in every
+  // lane (one VALU op; fp32 addition is commutative, so both halves get identical bits).
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                   false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // Load a 32-key column block of B fragments for the split kernel: lane (m, g) reads key s (its
@@ -305,7 +322,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int g = lane >> 5;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wid;
@@ -380,80 +397,94 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 
     // Page t (id `page`) into this thread's staging registers.  The load is unconditional so that
     // the staging registers stay registers: an invalid page id reads page 0 instead (its scores
-    // are then replaced by -inf) and key slots past the visible range are inside the page anyway
-    // (their columns are never stored).  An empty pool has no page to read at all.
+    // are then replaced by -inf; the host never sends an empty pool here) and key slots past the
+    // visible range are inside the page anyway (their columns are never stored).
     Stage<DT> st;
     bool st_ok = false;
-    const bool have_pool = a.n_pages_pool > 0;
     uint8_t* const lds_dst0 = &tile[0][kk * kLdsRow + qq * 64];
     uint8_t* const lds_dst1 = &tile[1][kk * kLdsRow + qq * 64];
+    // This row's scores go out through a buffer view of its visible columns: lane (m, g) stores
+    // the column 32 g + m of each page, one coalesced 256-byte store per wave and page, and the
+    // hardware drops the columns past the visible range.
+    const __amdgpu_buffer_rsrc_t out_view = buffer_view(out_row, mine ? nv_own : 0);
 
-    int32_t pend_s = -1;        // column of this lane's deferred scores (-1: none)
-    float pend_v[2] = {0.0f, 0.0f};
-    // Page ids run two pages ahead of the data so that no page-table read is waited on.
+    // First column of this wave's deferred scores; -64 (no scores yet) puts every lane's store
+    // out of the view's range, so the store below needs no condition.
+    int32_t pend_s = -kTileKeys;
+    float pend_v = 0.0f;
+    // Page ids run two pages ahead of the data so that no page-table read is waited on.  Every
+    // load below is unconditional (indices clamped to the last page): a conditional load into a
+    // loop-carried register would be waited on at once, and with it the page loads before it.
     // (Vector loads: a scalar load would share the LDS completion counter and turn every wait
     // for a B-fragment read into a wait for the page-table read.)
-    int32_t pid_next = n_tiles > 1 ? pt_row[1] : -1;
+    const int last = n_tiles - 1;
+    // The page ids are read through a per-lane index (the same in every lane): a read the
+    // compiler knows to be uniform would be moved to a scalar register, and that move waits for
+    // the read (and for every load before it) on the spot.
+    auto page_id = [&](int tt) {
+      int idx = min(tt, last);
+      asm volatile("" : "+v"(idx));
+      return pt_row[idx];
+    };
+    int32_t pid_next = page_id(1);
     bool ok_cur = false;
     {
       const int32_t page = pt_row[0];
       st_ok = page >= 0 && page < a.n_pages_pool;
-      if (have_pool) st.load(a.kcache, st_ok ? page : 0, kk, qq);
+      st.load(a.kcache, st_ok ? page : 0, kk, qq);
       st.commit(lds_dst0, &tscale[0][kk], qq);
     }
     ok_cur = st_ok;
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
       const int buf = t & 1;
-      const bool more = t + 1 < n_tiles;
-      if (more) {
-        st_ok = pid_next >= 0 && pid_next < a.n_pages_pool;
-        if (have_pool) st.load(a.kcache, st_ok ? pid_next : 0, kk, qq);
-      }
-      if (t + 2 < n_tiles) pid_next = pt_row[t + 2];
+      // the next page (the last page again at the end: staged into the idle buffer, never read)
+      st_ok = pid_next >= 0 && pid_next < a.n_pages_pool;
+      st.load(a.kcache, st_ok ? pid_next : 0, kk, qq);
+      pid_next = page_id(t + 2);
       const int32_t s_tile = t * kTileKeys;
       // Scores of the previous page go out first, so that they retire behind this page's work
       // instead of stalling the wait for the next page's loads.
-      if (pend_s >= 0) {
-        if (pend_s < nv_own) out_row[pend_s] = pend_v[0];
-        if (pend_s + 32 < nv_own) out_row[pend_s + 32] = pend_v[1];
-        pend_s = -1;
-      }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), out_view,
+                                            (pend_s + lane) * 4, 0, 0);
+      pend_s = -kTileKeys;
       if (mine && s_tile < nv_own) {
-        // Both 32-key halves of the page: the second half's MFMAs overlap the first half's
-        // epilogue.  Keys past this row's visible count are computed but not stored.
-        floatx16 acc[2][2];
+        // Both 32-key halves of the page.  Keys past this row's visible count are computed but
+        // not stored.
+        // Four independent accumulator chains (2 key halves x 2 head tiles), interleaved per
+        // k-step so that each chain's next MFMA issues three MFMAs after its previous one.
+        floatx16 acc[2][2] = {};
+        const u32x4* src0 = reinterpret_cast<const u32x4*>(&tile[buf][m * kLdsRow + 128 * g]);
+        const u32x4* src1 =
+            reinterpret_cast<const u32x4*>(&tile[buf][(32 + m) * kLdsRow + 128 * g]);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          Frag b0, b1;
+          b0.u = src0[jj];
+          b1.u = src1[jj];
+          acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, b0.v, acc[0][0], 0, 0, 0);
+          acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, b0.v, acc[0][1], 0, 0, 0);
+          acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, b1.v, acc[1][0], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, b1.v, acc[1][1], 0, 0, 0);
+        }
+        float tot[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          Frag kb[8];
-          const uint8_t* srcb = &tile[buf][(32 * h + m) * kLdsRow + 128 * g];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) kb[jj].u = reinterpret_cast<const u32x4*>(srcb)[jj];
-          acc[h][0] = floatx16{};
-          acc[h][1] = floatx16{};
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            acc[h][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, kb[jj].v, acc[h][0], 0, 0, 0);
-            acc[h][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc[h][1], 0, 0, 0);
-          }
+          tot[h] = head_sum(acc[h][0], acc[h][1], wv);
+          if constexpr (DT == kFp8) tot[h] *= tscale[buf][32 * h + m];
+          tot[h] = ok_cur ? tot[h] : -INFINITY;
         }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float tot = head_sum(acc[h][0], acc[h][1], wv);
-          if constexpr (DT == kFp8) tot *= tscale[buf][32 * h + m];
-          pend_v[h] = ok_cur ? tot : -INFINITY;
-        }
-        if (g == 0) pend_s = s_tile + m;
+        // both lane halves hold both halves' sums: lane (m, g) keeps key 32 g + m
+        pend_v = g ? tot[1] : tot[0];
+        pend_s = s_tile;
       }
-      if (more) st.commit(buf ? lds_dst0 : lds_dst1, &tscale[buf ^ 1][kk], qq);
+      st.commit(buf ? lds_dst0 : lds_dst1, &tscale[buf ^ 1][kk], qq);
       const bool ok_next = st_ok;
       __syncthreads();
       ok_cur = ok_next;
     }
-    if (pend_s >= 0) {
-      if (pend_s < nv_own) out_row[pend_s] = pend_v[0];
-      if (pend_s + 32 < nv_own) out_row[pend_s + 32] = pend_v[1];
-    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), out_view, (pend_s + lane) * 4,
+                                          0, 0);
   }
 }
 
