@@ -488,13 +488,249 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   }
 }
 
+// bf16 keys, prefill-shaped batches: the same work split as score_rows_kernel, but the pages go
+// from global memory straight into LDS (gfx950 global_load_lds_dwordx4: each lane's 16 bytes land
+// at M0 + 16 * lane), so no registers hold staged data and no VALU or LDS-write work copies it.
+// Three page buffers let each page be requested two pages ahead of its use.  Key rows are 256 B
+// without padding; the 16-byte chunks of key row kk sit at chunk ^ (kk & 15), which keeps the
+// fragment reads of every 16 consecutive lanes (16 consecutive keys) on distinct LDS banks.
+// Barriers are bare s_barrier with explicit counter waits: a full __syncthreads() fence would also
+// wait for the page requested two pages ahead.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kPageBytesBf16 = kTileKeys * kHeadDim * 2;   // 16384
+
+// s_waitcnt with vmcnt <= V and lgkmcnt <= L (expcnt unconstrained); gfx9 field layout: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int V, int L>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(V >= 0 && V < 64 && L >= 0 && L < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (L << 8) | ((V >> 4) << 14));
+}
+
+// readfirstlane kept after the preceding barrier (a plain builtin may be hoisted above it, to a
+// point where its operand's load has not been waited for yet).
+__device__ __forceinline__ int32_t uniform_after_wait(int32_t v) {
+  int32_t u;
+  asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(u) : "v"(v));
+  return u;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void score_rows_bf16_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t pg0[kPageBytesBf16];
+  __shared__ __attribute__((aligned(16))) uint8_t pg1[kPageBytesBf16];
+  __shared__ __attribute__((aligned(16))) uint8_t pg2[kPageBytesBf16];
+  __shared__ __attribute__((aligned(16))) float wsh[4][kHeads];
+  __shared__ int32_t seg_b[4];
+  __shared__ int32_t seg_nvis[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31;
+  const int g = lane >> 5;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+  const bool row_ok = r < a.n_rows;
+  const int64_t i = a.q_begin + (row_ok ? r : a.n_rows - 1);
+
+  int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
+  int64_t n_vis = 0;
+  if (b >= 0) {
+    const int64_t q_len = a.cu_q[b + 1] - a.cu_q[b];
+    const int64_t t = static_cast<int64_t>(a.seq_lens[b]) - q_len + (i - a.cu_q[b]);
+    if (t >= 0) {
+      n_vis = (t + 1) / kRatio;
+      const int64_t cap = static_cast<int64_t>(a.max_pages) * kPageKeys;
+      n_vis = n_vis < cap ? n_vis : cap;
+    }
+  }
+  if (!row_ok) {
+    b = -1;
+    n_vis = 0;
+  }
+  const int32_t nv_own = static_cast<int32_t>(min<int64_t>(n_vis, a.n_cols));
+  float* out_row = a.out + (row_ok ? r : 0) * a.out_stride;
+  if (row_ok) {
+    if (a.row_nvis && lane == 0) a.row_nvis[r] = static_cast<int32_t>(n_vis);
+    if (a.fill_invisible)
+      for (int32_t s = nv_own + lane; s < a.n_cols; s += 64) out_row[s] = -INFINITY;
+  }
+  if (lane == 0) {
+    seg_b[wid] = nv_own > 0 ? b : -1;
+    seg_nvis[wid] = nv_own;
+  }
+
+  // A operand (this wave's query, both 32-head tiles); the head weights wait in LDS.
+  Frag qa[2][8];
+  if (nv_own > 0) {
+    const uint16_t* qrow = a.q + i * (kHeads * kHeadDim);
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(qrow + (32 * ht + m) * kHeadDim + 64 * g);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) qa[ht][jj].u = src[jj];
+    }
+    wsh[wid][lane] = a.w[i * kHeads + lane];
+  }
+  __syncthreads();
+
+  // Page staging: wave wid, request c (0..3) fills LDS rows 16 wid + 4 c .. + 3 (1 KiB); lane L
+  // of it writes physical chunk L % 16 of row 16 wid + 4 c + L / 16, i.e. logical chunk
+  // (L % 16) ^ (row & 15) of that key.
+  // (row & 15 = 4 c + L / 16, whose bits are disjoint, so the chunk is (L % 16) ^ (L / 16) ^ 4 c.)
+  const int dma_row = 16 * wid + (lane >> 4);
+  const int dma_chunk = (lane & 15) ^ (lane >> 4);
+  // Fragment reads: key row m (+32 for the second half), logical chunk 8 g + jj.
+  const int frag_x = (8 * g) ^ (m & 15);
+  const int frag_row = m * (kHeadDim * 2);
+
+  for (int j = 0; j < 4; ++j) {
+    const int32_t bj = seg_b[j];
+    if (bj < 0) continue;
+    bool seen = false;
+    int32_t nmax = 0;
+    for (int jj = 0; jj < 4; ++jj) {
+      if (jj < j && seg_b[jj] == bj) seen = true;
+      if (seg_b[jj] == bj) nmax = max(nmax, seg_nvis[jj]);
+    }
+    if (seen) continue;
+    const bool mine = (b == bj) && nv_own > 0;
+    const int32_t bu = __builtin_amdgcn_readfirstlane(bj);
+    const int32_t* pt_row = a.page_table + static_cast<int64_t>(bu) * a.max_pages;
+    const int n_tiles = (nmax + kTileKeys - 1) / kTileKeys;
+    const int last = n_tiles - 1;
+    const __amdgpu_buffer_rsrc_t out_view = buffer_view(out_row, mine ? nv_own : 0);
+
+    // Page ids are read through a per-lane index (the same in every lane) so that the compiler
+    // does not move them to scalar registers, which would wait for the read on the spot; each is
+    // made uniform one page later, after a barrier wait has covered it.
+    auto page_id = [&](int tt) {
+      int idx = min(tt, last);
+      asm volatile("" : "+v"(idx));
+      return pt_row[idx];
+    };
+    auto valid = [&](int32_t pid) { return pid >= 0 && pid < a.n_pages_pool; };
+    // Request one page (id pu, wave-uniform, already validated) into buffer dst: 4 requests per
+    // wave, the last vector-memory operations of a tile.
+    auto stage = [&](uint8_t* dst, int32_t pu) {
+      const uint8_t* src = a.kcache + static_cast<int64_t>(pu) * kPageBytesBf16;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        __builtin_amdgcn_global_load_lds(src + (dma_row + 4 * c) * (kHeadDim * 2) +
+                                             16 * (dma_chunk ^ (4 * c)),
+                                         (lds_void*)(dst + (16 * wid + 4 * c) * (kHeadDim * 2)),
+                                         16, 0, 0);
+    };
+
+    int32_t pend_s = -kTileKeys;   // first column of the deferred scores (-64: none)
+    float pend_v = 0.0f;
+    bool ok0, ok1;                 // validity of the pages of tiles t and t + 1
+    int32_t pu2;                   // page id of tile t + 2, wave-uniform
+    {
+      const int32_t p0 = __builtin_amdgcn_readfirstlane(page_id(0));
+      const int32_t p1 = __builtin_amdgcn_readfirstlane(page_id(1));
+      ok0 = valid(p0);
+      ok1 = valid(p1);
+      stage(pg0, ok0 ? p0 : 0);
+      const int32_t pid2 = page_id(2);
+      stage(pg1, ok1 ? p1 : 0);
+      wait_counts<4, 0>();         // page 0 and pid2 are in; page 1 may still be in flight
+      __builtin_amdgcn_s_barrier();
+      pu2 = uniform_after_wait(pid2);
+    }
+
+    // One tile: scores of page t from buffer cur while page t + 2 streams into buffer nxt2.  The
+    // vector-memory operations of a tile are, in order: the page-id read for tile t + 3, the
+    // previous scores' store and the 4 requests of page t + 2, so waiting for all but the last 4
+    // covers the page of tile t + 1 and that page id, which is then made uniform (an SGPR value
+    // crossing the loop's back edge needs no wait there).
+    auto tile = [&](int t, const uint8_t* cur, uint8_t* nxt2) {
+      const int32_t p2 = pu2;
+      const bool ok2 = valid(p2);
+      const int32_t pid3 = page_id(t + 3);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), out_view,
+                                            (pend_s + lane) * 4, 0, 0);
+      pend_s = -kTileKeys;
+      const int32_t s_tile = t * kTileKeys;
+      if (mine && s_tile < nv_own) {
+        // an opaque copy: the eight fragment offsets are formed here, per page, instead of being
+        // hoisted out of the loop as invariants (which spills them)
+        int fx = frag_x;
+        asm volatile("" : "+v"(fx));
+        floatx16 acc[2][2] = {};
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const uint8_t* src = cur + frag_row + 16 * (fx ^ jj);
+          Frag b0, b1;
+          b0.u = *reinterpret_cast<const u32x4*>(src);
+          b1.u = *reinterpret_cast<const u32x4*>(src + 32 * (kHeadDim * 2));
+          acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, b0.v, acc[0][0], 0, 0, 0);
+          acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, b0.v, acc[0][1], 0, 0, 0);
+          acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][jj].v, b1.v, acc[1][0], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, b1.v, acc[1][1], 0, 0, 0);
+        }
+        // Weighted ReLU head sum, in the same order as head_sum (bit-identical logits): per key
+        // half, four fma chains over head tile 0's rows, then head tile 1's.
+        float p[2][4] = {};
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          float wv[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 w4 = *reinterpret_cast<const float4*>(&wsh[wid][32 * ht + 8 * q4 + 4 * g]);
+            wv[4 * q4 + 0] = w4.x;
+            wv[4 * q4 + 1] = w4.y;
+            wv[4 * q4 + 2] = w4.z;
+            wv[4 * q4 + 3] = w4.w;
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+              p[h][rr & 3] = fmaf(relu(acc[h][ht][rr]), wv[rr], p[h][rr & 3]);
+        }
+        float tot[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float part = (p[h][0] + p[h][1]) + (p[h][2] + p[h][3]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                           __float_as_uint(part), false, false);
+          tot[h] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+          tot[h] = ok0 ? tot[h] : -INFINITY;
+        }
+        pend_v = g ? tot[1] : tot[0];   // lane (m, g) keeps key 32 g + m
+        pend_s = s_tile;
+      }
+      stage(nxt2, ok2 ? p2 : 0);
+      ok0 = ok1;
+      ok1 = ok2;
+      wait_counts<4, 0>();           // page t + 1 is in; page t + 2 stays in flight
+      __builtin_amdgcn_s_barrier();
+      pu2 = uniform_after_wait(pid3);
+    };
+
+    for (int t = 0; t < n_tiles; t += 3) {
+      tile(t, pg0, pg2);
+      if (t + 1 >= n_tiles) break;
+      tile(t + 1, pg1, pg0);
+      if (t + 2 >= n_tiles) break;
+      tile(t + 2, pg2, pg1);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), out_view, (pend_s + lane) * 4,
+                                          0, 0);
+    // the pages requested past the end must land before the buffers are reused or released
+    wait_counts<0, 0>();
+    __builtin_amdgcn_s_barrier();
+  }
+  wait_counts<0, 0>();
+}
+
 }  // namespace
 
 hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream) {
   if (a.n_rows <= 0) return hipSuccess;
   const int64_t blocks = (a.n_rows + 3) / 4;
   if (dtype == kBf16)
-    hipLaunchKernelGGL(score_rows_kernel<kBf16>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+    hipLaunchKernelGGL(score_rows_bf16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                        stream, a);
   else
     hipLaunchKernelGGL(score_rows_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
