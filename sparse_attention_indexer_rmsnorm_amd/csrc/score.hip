@@ -498,6 +498,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 // wait for the page requested two pages ahead.
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kPageBytesBf16 = kTileKeys * kHeadDim * 2;   // 16384
+constexpr int kBf16RowsPerGroup = 4;    // 4 waves share a page; 3 workgroups per CU
 
 // s_waitcnt with vmcnt <= V and lgkmcnt <= L (expcnt unconstrained); gfx9 field layout: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
@@ -515,20 +516,37 @@ __device__ __forceinline__ int32_t uniform_after_wait(int32_t v) {
   return u;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void score_rows_bf16_kernel(ScoreArgs a) {
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0..5.
+__device__ __forceinline__ void wait_vmcnt_lgkm0(int n) {
+  switch (n) {
+    case 0: wait_counts<0, 0>(); break;
+    case 1: wait_counts<1, 0>(); break;
+    case 2: wait_counts<2, 0>(); break;
+    case 3: wait_counts<3, 0>(); break;
+    case 4: wait_counts<4, 0>(); break;
+    default: wait_counts<5, 0>(); break;
+  }
+}
+
+// W waves (W query rows) per workgroup share every staged page.  A page is 16 requests of 1 KiB
+// (4 key rows each); wave w issues requests w, w + W, ... (1 to 4 of them).
+template <int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void score_rows_bf16_kernel(ScoreArgs a) {
+  static_assert(W >= 4 && W <= 16, "4 to 16 waves");
   __shared__ __attribute__((aligned(16))) uint8_t pg0[kPageBytesBf16];
   __shared__ __attribute__((aligned(16))) uint8_t pg1[kPageBytesBf16];
   __shared__ __attribute__((aligned(16))) uint8_t pg2[kPageBytesBf16];
-  __shared__ __attribute__((aligned(16))) float wsh[4][kHeads];
-  __shared__ int32_t seg_b[4];
-  __shared__ int32_t seg_nvis[4];
+  __shared__ __attribute__((aligned(16))) float wsh[W][kHeads];
+  __shared__ int32_t seg_b[W];
+  __shared__ int32_t seg_nvis[W];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int g = lane >> 5;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * W + wid;
   const bool row_ok = r < a.n_rows;
   const int64_t i = a.q_begin + (row_ok ? r : a.n_rows - 1);
 
@@ -573,22 +591,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
   __syncthreads();
 
-  // Page staging: wave wid, request c (0..3) fills LDS rows 16 wid + 4 c .. + 3 (1 KiB); lane L
-  // of it writes physical chunk L % 16 of row 16 wid + 4 c + L / 16, i.e. logical chunk
-  // (L % 16) ^ (row & 15) of that key.
-  // (row & 15 = 4 c + L / 16, whose bits are disjoint, so the chunk is (L % 16) ^ (L / 16) ^ 4 c.)
-  const int dma_row = 16 * wid + (lane >> 4);
+  // Page staging: request q (0..15) fills LDS rows 4 q .. 4 q + 3 (1 KiB); lane L of it writes
+  // physical chunk L % 16 of row 4 q + L / 16, i.e. logical chunk (L % 16) ^ (row & 15) of that
+  // key.  (row & 15 = 4 (q & 3) + L / 16, whose parts have disjoint bits, so the chunk is
+  // (L % 16) ^ (L / 16) ^ 4 (q & 3).)
+  const int n_req = 16 % W == 0 ? 16 / W : (16 - wid + W - 1) / W;   // this wave's requests
   const int dma_chunk = (lane & 15) ^ (lane >> 4);
   // Fragment reads: key row m (+32 for the second half), logical chunk 8 g + jj.
   const int frag_x = (8 * g) ^ (m & 15);
   const int frag_row = m * (kHeadDim * 2);
 
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < W; ++j) {
     const int32_t bj = seg_b[j];
     if (bj < 0) continue;
     bool seen = false;
     int32_t nmax = 0;
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < W; ++jj) {
       if (jj < j && seg_b[jj] == bj) seen = true;
       if (seg_b[jj] == bj) nmax = max(nmax, seg_nvis[jj]);
     }
@@ -609,16 +627,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       return pt_row[idx];
     };
     auto valid = [&](int32_t pid) { return pid >= 0 && pid < a.n_pages_pool; };
-    // Request one page (id pu, wave-uniform, already validated) into buffer dst: 4 requests per
-    // wave, the last vector-memory operations of a tile.
+    // Request one page (id pu, wave-uniform, already validated) into buffer dst: this wave's
+    // n_req requests.
     auto stage = [&](uint8_t* dst, int32_t pu) {
       const uint8_t* src = a.kcache + static_cast<int64_t>(pu) * kPageBytesBf16;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        __builtin_amdgcn_global_load_lds(src + (dma_row + 4 * c) * (kHeadDim * 2) +
-                                             16 * (dma_chunk ^ (4 * c)),
-                                         (lds_void*)(dst + (16 * wid + 4 * c) * (kHeadDim * 2)),
-                                         16, 0, 0);
+      for (int c = 0; c < (16 + W - 1) / W; ++c) {
+        if (c < n_req) {
+          const int q = wid + W * c;
+          __builtin_amdgcn_global_load_lds(
+              src + (4 * q + (lane >> 4)) * (kHeadDim * 2) + 16 * (dma_chunk ^ (4 * (q & 3))),
+              (lds_void*)(dst + q * (4 * kHeadDim * 2)), 16, 0, 0);
+        }
+      }
     };
 
     int32_t pend_s = -kTileKeys;   // first column of the deferred scores (-64: none)
@@ -633,20 +654,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       stage(pg0, ok0 ? p0 : 0);
       const int32_t pid2 = page_id(2);
       stage(pg1, ok1 ? p1 : 0);
-      wait_counts<4, 0>();         // page 0 and pid2 are in; page 1 may still be in flight
+      wait_vmcnt_lgkm0(n_req);     // page 0 and pid2 are in; page 1 may still be in flight
       __builtin_amdgcn_s_barrier();
       pu2 = uniform_after_wait(pid2);
     }
 
-    // One tile: scores of page t from buffer cur while page t + 2 streams into buffer nxt2.  The
-    // vector-memory operations of a tile are, in order: the page-id read for tile t + 3, the
-    // previous scores' store and the 4 requests of page t + 2, so waiting for all but the last 4
-    // covers the page of tile t + 1 and that page id, which is then made uniform (an SGPR value
-    // crossing the loop's back edge needs no wait there).
+    // One tile: scores of page t from buffer cur while page t + 2 streams into buffer nxt2 (last
+    // read in tile t - 1, before the barrier that ended it).  The vector-memory operations of a
+    // tile are, in order: the page-id read for tile t + 3, the n_req requests of page t + 2 and
+    // the previous scores' store, so waiting for all but the last n_req + 1 covers that page id
+    // and, issued before it, the page of tile t + 1; the page id is then made uniform (an SGPR value crossing
+    // the loop's back edge needs no wait there).  Each page has two tiles to arrive.
     auto tile = [&](int t, const uint8_t* cur, uint8_t* nxt2) {
       const int32_t p2 = pu2;
       const bool ok2 = valid(p2);
       const int32_t pid3 = page_id(t + 3);
+      stage(nxt2, ok2 ? p2 : 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), out_view,
                                             (pend_s + lane) * 4, 0, 0);
       pend_s = -kTileKeys;
@@ -700,10 +723,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         pend_v = g ? tot[1] : tot[0];   // lane (m, g) keeps key 32 g + m
         pend_s = s_tile;
       }
-      stage(nxt2, ok2 ? p2 : 0);
       ok0 = ok1;
       ok1 = ok2;
-      wait_counts<4, 0>();           // page t + 1 is in; page t + 2 stays in flight
+      wait_vmcnt_lgkm0(n_req + 1);   // page t + 1 and pid3 are in; page t + 2 stays in flight
       __builtin_amdgcn_s_barrier();
       pu2 = uniform_after_wait(pid3);
     };
@@ -728,13 +750,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
 hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream) {
   if (a.n_rows <= 0) return hipSuccess;
+  if (dtype == kBf16) {
+    const int64_t groups = (a.n_rows + kBf16RowsPerGroup - 1) / kBf16RowsPerGroup;
+    hipLaunchKernelGGL(score_rows_bf16_kernel<kBf16RowsPerGroup>, dim3(static_cast<uint32_t>(groups)),
+                       dim3(64 * kBf16RowsPerGroup), 0, stream, a);
+    return hipGetLastError();
+  }
   const int64_t blocks = (a.n_rows + 3) / 4;
-  if (dtype == kBf16)
-    hipLaunchKernelGGL(score_rows_bf16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(score_rows_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
+  hipLaunchKernelGGL(score_rows_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
