@@ -107,6 +107,47 @@ def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int) -> dict:
                       f"{secs:.2f} s of wall time"}
 
 
+def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
+    """S1 alone: store every key of the workload, --steps times; keys stored per second and the
+    store kernel's HBM roofline (per key: 512 B of activations and 8 B of indices read, 132 or
+    256 B written)."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+
+    def step():
+        ix.store_keys(d["x"], d["gamma"], d["key_idx"], d["page_table"], pool, dtype, eps=wl.eps,
+                      key_seq=d["key_seq"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    key_bytes = 132 if dtype == 0 else 256
+    algo = wl.n_keys * (512 + 8 + key_bytes)
+    achieved = algo / (kms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "keys stored/s (S1: RMSNorm + RoPE + quantise + paged store)",
+        "value": wl.n_keys / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "-store-population", "keys": wl.n_keys,
+                   "kv_dtype": "fp8" if dtype == 0 else "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "store_keys_kernel", "kernel_ms": round(kms, 4)},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +156,13 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB buffer before every step so that the step's keys come "
+                         "from HBM, not the 256 MB MALL; steps are then timed with HIP events "
+                         "around each step (the flush excluded)")
+    ap.add_argument("--store-population", action="store_true",
+                    help="time only the store of the workload's whole key population (S1 alone): "
+                         "keys stored per second and the store kernel's HBM roofline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the "
                          "reference for scaling HBM byte counters); prints its bytes per copy")
@@ -154,6 +202,8 @@ def main() -> int:
         "w": torch.from_numpy(wl.w).to(dev),
     }
     pool = ix.new_cache(wl.n_pages_pool, dtype, device=dev)
+    if args.store_population:
+        return store_population(args, wl, dtype, d, pool, ix, torch)
     step_mask = wl.step_keys if wl.step_keys is not None else np.ones(wl.n_keys, bool)
     pre = np.nonzero(~step_mask)[0]
     stp = np.nonzero(step_mask)[0]
@@ -170,9 +220,12 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    for a, b in evs:            # materialise the underlying hipEvent_t handles
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+    for a, b in evs + step_evs:     # materialise the underlying hipEvent_t handles
         a.record(stream)
         b.record(stream)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
     def step(events=None):
         ix.store_keys(sx, d["gamma"], sidx, d["page_table"], pool, dtype, eps=wl.eps,
@@ -185,11 +238,18 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        step_evs[i][0].record(stream)
         step(evs[i])
+        step_evs[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    ms = (t1 - t0) * 1e3 / args.steps
+    if flush is None:
+        ms = (t1 - t0) * 1e3 / args.steps
+    else:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in step_evs]))
     pairs, nv = _pairs(wl)
     score_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     key_bytes = 132 if dtype == 0 else 256
@@ -221,7 +281,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic" + (", MALL flushed before every step" if args.cold else ""),
         "config": {"workload": wl.name, "queries": wl.n_q, "keys": int(wl.max_keys),
                    "visible_pairs": pairs, "k": wl.k, "kv_dtype": "fp8" if dtype == 0 else "bf16",
                    "keys_stored_in_step": int(stp.size), "heads": 64, "head_dim": 128,

@@ -148,9 +148,11 @@ __device__ __forceinline__ void wave_find_bin(const uint32_t* words, uint32_t wa
   const int lo_word = kAreaWords - 32 * (lane + 1);
   const u32x4* blk = reinterpret_cast<const u32x4*>(words + lo_word);
   uint32_t local = 0;
+  // chunk i of the block is read at step (i - lane) mod 8, so the lanes of a 16-lane group hit
+  // different banks (blocks are 128 B apart, which alone would map them onto the same banks)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const u32x4 w = blk[i];
+    const u32x4 w = blk[(i + lane) & 7];
     local += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) +
              (w.z & 0xFFFFu) + (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
   }
@@ -408,6 +410,255 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Batches of few long rows (decode): one workgroup of 16 waves selects one whole row, so that a
+// row of up to 16 x 64 x E scores (E <= 32: 32768) is spread over 1024 lanes in a single pass
+// instead of a few long-running waves per row.  Wave w holds elements w*64*E + 64 j + lane (contiguous slices, so
+// wave order is index order).  The steps are those of the wave kernel, shared through LDS: the
+// row's key range (min / max reduced over the waves), one 4096-bin histogram with 32-bit counts,
+// the radix refinement of the threshold bin done over the registers of all waves into
+// pre-cleared 128-bin histograms (no candidate list, so no capacity limit), and the final
+// compaction in index order with per-wave prefix counts of the keys > T and == T.
+constexpr int kBlockWaves = 16;
+constexpr int kBlockRowsMax = 128;     // batches with at most this many rows use the block kernel
+constexpr int kBlockMaxE = 32;        // 1024-lane groups leave 128 VGPRs: up to 32 keys per lane
+
+// Descending scan of nb 32-bit bins (nb a multiple of 64): the bin holding the want-th largest
+// entry, the count above it and its own count.  Lane l sums bins [nb - per (l+1), nb - per l);
+// then the crossing lane's bins are spread over the wave.
+template <int NB>
+__device__ __forceinline__ void wave_find_bin32(const uint32_t* bins, uint32_t want, int lane,
+                                                uint32_t* bin, uint32_t* above, uint32_t* count) {
+  constexpr int per = NB / 64;
+  static_assert(per % 4 == 0 && per <= 64 && ((per / 4) & (per / 4 - 1)) == 0, "bins per lane");
+  const u32x4* blk = reinterpret_cast<const u32x4*>(bins + NB - per * (lane + 1));
+  uint32_t local = 0;
+  // rotated chunk order: blocks are per * 4 B apart, so reading chunk i in every lane at once
+  // would put a whole 16-lane group on the same banks
+#pragma unroll
+  for (int i = 0; i < per / 4; ++i) {
+    const u32x4 v = blk[(i + lane) & (per / 4 - 1)];
+    local += (v.x + v.y) + (v.z + v.w);
+  }
+  const uint32_t run = wave_excl_scan(local, lane);
+  const uint64_t hm = __ballot(run < want && run + local >= want);
+  const int L = __builtin_amdgcn_readfirstlane(hm ? __builtin_ctzll(hm) : 0);
+  const uint32_t run_l = lane_value(run, L);
+  const int bi = NB - per * L - 1 - lane;               // lane i < per: the i-th bin from the top
+  const uint32_t c = lane < per ? bins[bi] : 0u;
+  const uint32_t r2 = run_l + wave_excl_scan(c, lane);
+  const uint64_t m = __ballot(lane < per && r2 < want && r2 + c >= want);
+  const int src = __builtin_amdgcn_readfirstlane(m ? __builtin_ctzll(m) : 0);
+  *bin = static_cast<uint32_t>(NB - per * L - 1 - src);
+  *above = lane_value(r2, src);
+  *count = lane_value(c, src);
+}
+
+constexpr int kBlockCand = 4096;       // threshold-bin keys refined from an LDS list
+
+template <int E>
+__global__ __launch_bounds__(64 * kBlockWaves) void topk_block_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t cand[kBlockCand];
+  __shared__ __attribute__((aligned(16))) uint32_t sub[3][kSubBins];
+  __shared__ uint32_t red[2][kBlockWaves];
+  __shared__ uint32_t cnt[2][kBlockWaves];
+  __shared__ uint32_t n_cand;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t r = blockIdx.x;
+  int64_t len = a.row_len ? static_cast<int64_t>(a.row_len[r]) : a.row_stride;
+  len = len < 0 ? 0 : (len > a.row_stride ? a.row_stride : len);
+  const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(len));
+  const int32_t k = a.k;
+  const float* row = a.scores + r * a.row_stride;
+  int32_t* oi = a.out_idx + r * k;
+  float* ov = a.out_val ? a.out_val + r * k : nullptr;
+
+  if (n <= k) {   // everything is selected, then padding
+    for (int32_t e = tid; e < k; e += 64 * kBlockWaves) {
+      oi[e] = e < n ? e : -1;
+      if (ov) ov[e] = e < n ? key_value(order_key(row[e])) : -INFINITY;
+    }
+    return;
+  }
+
+  // 1. this wave's slice in registers (buffer loads past the row end return 0 -> key 0)
+  const int32_t base_w = wid * 64 * E;
+  const int32_t groups = min(max((n - base_w + 63) >> 6, 0), E);   // 64-slot groups holding entries
+  uint32_t u[E];
+  {
+    const __amdgpu_buffer_rsrc_t view = buffer_view(row, n);
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      u[j] = __builtin_amdgcn_raw_buffer_load_b32(view, (base_w + lane) * 4 + j * 256, 0, 0);
+  }
+  launder(u);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    u[j] = base_w + j * 64 + lane < n ? order_key(__uint_as_float(u[j])) : 0u;
+    kmin = min(kmin, u[j] ? u[j] : 0xFFFFFFFFu);
+    kmax = max(kmax, u[j]);
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    red[0][wid] = kmin;
+    red[1][wid] = kmax;
+  }
+  reinterpret_cast<u32x4*>(hist)[tid] = u32x4{0u, 0u, 0u, 0u};      // 1024 x 16 B = all bins
+  if (tid < 3 * kSubBins) (&sub[0][0])[tid] = 0u;
+  if (tid == 0) n_cand = 0u;
+  __syncthreads();
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kBlockWaves; ++w) {
+    kmin = min(kmin, red[0][w]);
+    kmax = max(kmax, red[1][w]);
+  }
+  const uint32_t kbase = kmin - 1u;
+  const uint32_t top_off = kmax ? kmax - kbase : 0u;
+  const int span = top_off ? 32 - __builtin_clz(top_off) : 0;
+  const int shift = span > kBinBits ? span - kBinBits : 0;
+  auto off_of = [&](uint32_t key) { return key ? key - kbase : 0u; };
+
+  // 2. shared fine histogram
+  launder(u);
+  {
+    const int32_t ng = fresh(groups);
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (j < ng) atomicAdd(&hist[off_of(after(u[j], 0u)) >> shift], 1u);
+  }
+  __syncthreads();
+  uint32_t bB, above, c_b;
+  wave_find_bin32<kBins>(hist, static_cast<uint32_t>(k), lane, &bB, &above, &c_b);
+  uint32_t k_rem = static_cast<uint32_t>(k) - above;      // 1 <= k_rem <= c_b
+
+  // 3. exact threshold inside bin B: radix passes over its keys, gathered into an LDS list
+  //    (one reservation per wave ballot; the list order does not matter) when they fit, else
+  //    over every wave's registers
+  const bool listed = shift > 0 && c_b <= static_cast<uint32_t>(kBlockCand);
+  if (listed) {
+    const int32_t ng = fresh(groups);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      if (j < ng) {
+        const uint32_t o = off_of(after(u[j], 0u));
+        const bool in = (o >> shift) == bB;
+        const uint64_t m = __ballot(in);
+        if (m) {
+          uint32_t at = 0;
+          if (lane == 0) at = atomicAdd(&n_cand, static_cast<uint32_t>(__popcll(m)));
+          at = lane_value(at, 0);
+          if (in) cand[at + lanes_below(m)] = o;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  uint32_t prefix = bB;
+  int bits = shift;
+#pragma unroll 1
+  for (int pass = 0; bits > 0; ++pass) {
+    const int w = bits < kSubBits ? bits : kSubBits;
+    const int sh = bits - w;
+    if (listed) {
+      for (uint32_t c = tid; c < c_b; c += 64 * kBlockWaves) {
+        const uint32_t o = cand[c];
+        if ((o >> bits) == prefix) atomicAdd(&sub[pass][(o >> sh) & ((1u << w) - 1u)], 1u);
+      }
+    } else {
+      const int32_t ng = fresh(groups);
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        if (j < ng) {
+          const uint32_t o = off_of(after(u[j], 0u));
+          if ((o >> bits) == prefix) atomicAdd(&sub[pass][(o >> sh) & ((1u << w) - 1u)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    uint32_t d, gt;
+    wave_find_digit(sub[pass], k_rem, lane, &d, &gt);
+    prefix = (prefix << w) | d;
+    k_rem -= gt;
+    bits = sh;
+  }
+  const uint32_t T = prefix ? prefix + kbase : 0u;
+  const uint32_t eq_take = k_rem;
+
+  // 4. per-wave counts of keys > T and == T, prefix-summed over the waves
+  uint32_t n_gt = 0, n_eq = 0;
+  launder(u);
+  {
+    const int32_t ng = fresh(groups);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      if (j < ng) {
+        const uint32_t uj = after(u[j], n_gt + n_eq);
+        n_gt += static_cast<uint32_t>(__popcll(__ballot(uj > T)));
+        n_eq += static_cast<uint32_t>(__popcll(__ballot(uj == T)));
+      }
+    }
+  }
+  if (lane == 0) {
+    cnt[0][wid] = n_gt;
+    cnt[1][wid] = n_eq;
+  }
+  __syncthreads();
+  uint32_t gt_seen = 0, eq_seen = 0;
+  for (int w = 0; w < wid; ++w) {
+    gt_seen += cnt[0][w];
+    eq_seen += cnt[1][w];
+  }
+
+  // 5. compaction in index order (ties: the lowest-indexed keys equal to T)
+  launder(u);
+  {
+    const int32_t ng = fresh(groups);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      if (j < ng) {
+        const uint32_t uj = after(u[j], gt_seen + eq_seen);
+        const bool gtv = uj > T;
+        const bool eqv = uj == T;
+        const uint64_t mg = __ballot(gtv);
+        const uint64_t me = __ballot(eqv);
+        const uint32_t gpre = gt_seen + lanes_below(mg);
+        const uint32_t epre = eq_seen + lanes_below(me);
+        uint32_t pos = 0xFFFFFFFFu;
+        if (gtv) pos = gpre + (epre < eq_take ? epre : eq_take);
+        else if (eqv && epre < eq_take) pos = gpre + epre;
+        if (pos < static_cast<uint32_t>(k)) {
+          oi[pos] = base_w + j * 64 + lane;
+          if (ov) ov[pos] = uj ? key_value(uj) : -INFINITY;
+        }
+        gt_seen += static_cast<uint32_t>(__popcll(mg));
+        eq_seen += static_cast<uint32_t>(__popcll(me));
+      }
+    }
+  }
+}
+
+bool use_block(int64_t n_rows, int64_t cols) {
+  return n_rows <= kBlockRowsMax && cols <= static_cast<int64_t>(kBlockWaves) * 64 * kBlockMaxE;
+}
+
+hipError_t launch_block(const TopkArgs& a, int64_t cols, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(a.n_rows)), block(64 * kBlockWaves);
+  if (cols <= kBlockWaves * 64 * 8)
+    hipLaunchKernelGGL(topk_block_kernel<8>, grid, block, 0, stream, a);
+  else if (cols <= kBlockWaves * 64 * 16)
+    hipLaunchKernelGGL(topk_block_kernel<16>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(topk_block_kernel<kBlockMaxE>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int E>
 hipError_t launch_wave(const TopkArgs& a, hipStream_t stream) {
   const int64_t tasks = a.n_rows * a.n_seg;
@@ -458,6 +709,7 @@ TopkPlan topk_plan(int64_t n_rows, int64_t cols, int32_t k) {
   TopkPlan p{};
   p.passes = 1;
   p.cand_elems = 0;
+  if (use_block(n_rows, cols)) return p;
   int64_t c = cols;
   int32_t ns = first_pass_segments(n_rows, c, k);
   while (ns > 1) {
@@ -492,6 +744,13 @@ hipError_t run_topk(const float* scores, int64_t row_stride, const int32_t* row_
   a.k = k;
   a.src_idx = nullptr;
   a.pad_bits = 0;
+  if (use_block(n_rows, cols)) {
+    a.n_seg = 1;
+    a.seg_len = 0;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    return launch_block(a, cols, stream);
+  }
   int32_t ns = first_pass_segments(n_rows, cols, k);
   if (ns <= 1) {
     a.n_seg = 1;

@@ -65,8 +65,9 @@ class Workload:
     k: int
     eps: float = EPS
     dtypes: tuple = (FP8, BF16)
-    # keys that belong to the measured store step (cfg3 stores its chunk inside the step;
-    # everything else is pre-stored).  Boolean mask over the key rows.
+    # keys that belong to the measured store step (the prefill chunk stores its own keys inside
+    # the step, a decode step the newest compressed key of each sequence; everything else is
+    # stored beforehand).  Boolean mask over the key rows.
     step_keys: Optional[np.ndarray] = None
     # needles: per needle (seq b, query row i, key row n, logical s)
     needles: dict = field(default_factory=dict)
@@ -203,12 +204,20 @@ def cfg1(seed: int = 101) -> Workload:
     return wl
 
 
+def newest_keys(wl: Workload) -> np.ndarray:
+    """Mask of each sequence's last compressed key (the key a decode step adds)."""
+    last = wl.seq_lens[wl.key_seq] // 4 - 1
+    return wl.key_idx == last
+
+
 def cfg2(seed: int = 102) -> Workload:
     """Decode batch: 64 sequences, L_b ~ U{4096..22528}, one query each at t = L_b - 1, top-512,
     random page permutation over a shared pool, max 88 pages per sequence."""
     lens = rng(seed, T_LENS).integers(4096, 22528, size=64, endpoint=True).astype(np.int32)
-    return make_workload("decode-64x4k-22k", seed, lens, np.ones(64, np.int32), 512,
-                         permute_pages=True, max_pages=88)
+    wl = make_workload("decode-64x4k-22k", seed, lens, np.ones(64, np.int32), 512,
+                       permute_pages=True, max_pages=88)
+    wl.step_keys = newest_keys(wl)
+    return wl
 
 
 def cfg3(seed: int = 103) -> Workload:
@@ -227,6 +236,7 @@ def cfg4(seed: int = 104, needles: bool = True) -> Workload:
                        1024, permute_pages=True, max_pages=512)
     if needles:
         wl.needles = draw_needles(wl, 32)
+    wl.step_keys = newest_keys(wl)
     return wl
 
 

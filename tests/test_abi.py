@@ -41,11 +41,13 @@ def test_page_bytes(L):
 
 def test_workspace_sizes(L):
     # decode batch of 32 queries over 512 pages: a row of 32768 fp32 scores each plus visible
-    # counts, plus two candidate buffers for a two-pass selection (6 segments of <= 6144 scores,
-    # k (index, value) candidates each)
+    # counts; few rows are selected one workgroup per row in a single pass (no candidates)
     scores = 256 + 32 * 32768 * 4
-    cand = 2 * (32 * 6 * 1024 * 8 + 256)
-    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == scores + cand
+    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == scores
+    # 256 such rows go through the segmented two-pass selection: two candidate buffers of
+    # 6 segments x k (index, value) pairs per row
+    cand = 2 * (256 * 6 * 1024 * 8 + 256)
+    assert L.idx_topk_rows_workspace_size(256, 32768, 1024) == cand
     # long prefill chunk: 8192 queries x 5632 keys fits the 256 MiB cap in one pass, one-pass top-k
     ws = L.idx_logits_topk_workspace_size(8192, 1, 88, 512)
     assert ws == 8192 * 4 + 8192 * 5632 * 4 and ws <= 256 << 20
@@ -57,7 +59,8 @@ def test_workspace_sizes(L):
     assert L.idx_logits_topk_workspace_size(8192, 1, 88, 512) < 8192 * 5632 * 64 * 4 / 50
     # stand-alone selection: one pass needs none; long rows of a small batch need candidates
     assert L.idx_topk_rows_workspace_size(8192, 5632, 512) == 0
-    assert L.idx_topk_rows_workspace_size(32, 32768, 1024) > 0
+    assert L.idx_topk_rows_workspace_size(32, 32768, 1024) == 0     # one workgroup per row
+    assert L.idx_topk_rows_workspace_size(32, 40000, 1024) > 0      # longer than a workgroup
 
 
 def _store(L, **kw):

@@ -38,6 +38,9 @@ def _rows(seed, n_rows, stride, kind):
     (4, 32768, 1024, "normal"), (3, 32768, 2048, "ties"), (2, 40000, 1024, "normal"),
     (2, 40000, 700, "ties"), (16, 100, 1, "ties"), (16, 100, 2048, "normal"),
     (5, 513, 512, "ties"), (5, 512, 512, "normal"),
+    # more rows than the one-workgroup-per-row path takes: one wave per row or segment
+    (160, 6000, 512, "normal"), (150, 40000, 1024, "normal"), (140, 20000, 2048, "ties"),
+    (129, 9000, 64, "mixed"),
 ])
 def test_topk_rows_bit_exact(oracle_mod, n_rows, stride, k, kind):
     v = _rows(n_rows * 1000003 + stride * 31 + k + 7 * len(kind), n_rows, stride, kind)
@@ -147,10 +150,11 @@ def test_logits_topk_repeatable():
 
 
 @pytest.mark.parametrize("dtype,k", [(FP8, 512), (BF16, 1024), (FP8, 64)])
-def test_two_pass_selection_matches_one_pass(dtype, k):
-    """Decode-shaped batches select each row in segments, then among the segments' candidates.
-    Rows shorter than k, a row spanning few segments, and keys on an invalid page (-inf) included;
-    the result must equal a one-pass selection over the dense logits, bit for bit."""
+def test_decode_selection_matches_dense_then_select(dtype, k):
+    """Decode-shaped batches (few long rows; one workgroup per row, or segments and a second pass
+    for rows longer than a workgroup holds).  Rows shorter than k, rows just below and above k,
+    and keys on an invalid page (-inf) included; the result must equal the selection over the
+    dense logits, bit for bit."""
     r = np.random.default_rng(40 + k)
     lens = r.integers(8, 60000, 24).astype(np.int32)
     lens[:3] = [12, 4 * k - 4, 4 * k + 8]             # n_vis < k, just below and above k
