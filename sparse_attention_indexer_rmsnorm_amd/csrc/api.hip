@@ -15,9 +15,10 @@ constexpr size_t kAlign = 256;
 // Recommended workspace cap: query chunks are sized so that one chunk's head-reduced scores
 // stay within this bound, whatever the batch (the 8192 x 5632 long-prefill chunk needs 185 MB).
 constexpr size_t kWorkspaceCap = size_t(256) << 20;
-// Target number of waves per scoring launch; key chunks shrink until the launch has about this
-// many (row, chunk) work items, but never below kMinChunkKeys keys per wave.
-constexpr int64_t kTargetWaves = 8192;
+// Key chunk per wave of the split (decode) kernel: 512 keys while the launch still has at least
+// kMinWaves (row, chunk) work items (two per SIMD), else down to 256.
+constexpr int64_t kMinWaves = 2048;
+constexpr int32_t kMaxChunkKeys = 512;
 constexpr int32_t kMinChunkKeys = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -87,8 +88,8 @@ int64_t rows_fitting(size_t bytes, int32_t max_pages, int32_t k, int64_t n_q) {
 
 void plan_chunks(int64_t n_rows, int32_t n_cols, int32_t* chunk_keys, int32_t* n_chunks) {
   const int64_t cols32 = (static_cast<int64_t>(n_cols) + 31) / 32 * 32;
-  int64_t ck = (static_cast<int64_t>(n_cols) * n_rows + kTargetWaves - 1) / kTargetWaves;
-  ck = (ck + 31) / 32 * 32;
+  int64_t ck = static_cast<int64_t>(n_cols) * n_rows / kMinWaves / 32 * 32;
+  if (ck > kMaxChunkKeys) ck = kMaxChunkKeys;
   if (ck < kMinChunkKeys) ck = kMinChunkKeys;
   if (ck > cols32) ck = cols32;
   if (ck < 32) ck = 32;

@@ -214,24 +214,22 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     for (int rr = 0; rr < 16; ++rr) wv[ht][rr] = wrow[32 * ht + 8 * (rr >> 2) + 4 * g + (rr & 3)];
 
   const int32_t* pt_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-
-  // Key block s0 .. s0+31 (32-aligned, so inside one page): lane (m, g) holds key s0 + m.  The
-  // next block's keys are fetched while the current one is multiplied; page ids (wave-uniform,
-  // scalar loads) run one more block ahead.
   auto page_ok = [&](int32_t page) { return page >= 0 && page < a.n_pages_pool; };
-  KeyBlock<DT> cur, nxt;
-  int32_t page = load_uniform(pt_row + c_begin / kPageKeys);
-  int32_t page_n = c_begin + 32 < s_end ? load_uniform(pt_row + (c_begin + 32) / kPageKeys) : -1;
-  bool ok = page_ok(page);
-  cur.load(a.kcache, page, (c_begin + m) % kPageKeys, g, ok && c_begin + m < s_end);
+  // Key block s0 .. s0+31 (32-aligned, so inside one page): lane (m, g) holds key s0 + m.  Two
+  // blocks are in flight while one is multiplied (decode batches are bound by the key bytes in
+  // flight); page ids (wave-uniform scalar loads) run one block further ahead.
+  KeyBlock<DT> b0, b1, b2;
+  auto pg_of = [&](int32_t s0) { return s0 < s_end ? load_uniform(pt_row + s0 / kPageKeys) : -1; };
+  int32_t p0 = pg_of(c_begin), p1 = pg_of(c_begin + 32), p2 = pg_of(c_begin + 64);
+  bool ok0 = page_ok(p0), ok1 = page_ok(p1), ok2;
+  b0.load(a.kcache, p0, (c_begin + m) % kPageKeys, g, ok0 && c_begin + m < s_end);
+  b1.load(a.kcache, p1, (c_begin + 32 + m) % kPageKeys, g, ok1 && c_begin + 32 + m < s_end);
   for (int32_t s0 = c_begin; s0 < s_end; s0 += 32) {
-    const bool more = s0 + 32 < s_end;
-    const bool ok_n = page_ok(page_n);
-    if (more) nxt.load(a.kcache, page_n, (s0 + 32 + m) % kPageKeys, g, ok_n && s0 + 32 + m < s_end);
-    const int32_t page_nn =
-        s0 + 64 < s_end ? load_uniform(pt_row + (s0 + 64) / kPageKeys) : -1;
+    ok2 = page_ok(p2);
+    if (s0 + 64 < s_end) b2.load(a.kcache, p2, (s0 + 64 + m) % kPageKeys, g, ok2 && s0 + 64 + m < s_end);
+    const int32_t p3 = pg_of(s0 + 96);
     Frag kb[8];
-    cur.frags(kb);
+    b0.frags(kb);
     floatx16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -239,14 +237,12 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc1, 0, 0, 0);
     }
     float tot = head_sum(acc0, acc1, wv);
-    if constexpr (DT == kFp8) tot *= cur.scale;
+    if constexpr (DT == kFp8) tot *= b0.scale;
     const int32_t s = s0 + m;
-    if (g == 0 && s < s_end) out_row[s] = ok ? tot : -INFINITY;
-    if (more) {
-      cur = nxt;
-      ok = ok_n;
-    }
-    page_n = page_nn;
+    if (g == 0 && s < s_end) out_row[s] = ok0 ? tot : -INFINITY;
+    b0 = b1; ok0 = ok1;
+    b1 = b2; ok1 = ok2;
+    p2 = p3;
   }
 }
 
