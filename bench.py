@@ -46,6 +46,7 @@ DEFAULT = "prefill-22k-chunk8192-bf16"
 # Sources that determine each kernel's machine code: a committed counter summary for a kernel is
 # used only while its digest over these files still matches.
 KERNEL_SOURCES = {
+    "score_rows_bf16_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "score_rows_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "score_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
 }
@@ -107,6 +108,43 @@ def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int) -> dict:
                       f"{secs:.2f} s of wall time"}
 
 
+def ceilings(args, torch) -> int:
+    """Context for the rooflines: the MFMA rate torch's GEMM reaches on this GPU, and the HBM read
+    rate of a plain reduction, each the best of --steps runs."""
+    dev = torch.device("cuda:0")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        a @ b
+    best = 1e9
+    for _ in range(args.steps):
+        e0.record()
+        a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    gemm = 2 * 8192 ** 3 / (best * 1e-3) / 1e12
+    del a, b
+    x = torch.ones(128 << 20, dtype=torch.float32, device=dev)       # 512 MiB
+    other = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    best_r = 1e9
+    for _ in range(args.steps):
+        other.sum()                        # evicts x from the MALL without dirtying it
+        e0.record()
+        x.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best_r = min(best_r, e0.elapsed_time(e1))
+    read = (512 << 20) / (best_r * 1e-3) / 1e9
+    print(json.dumps({"metric": "device ceilings for library code",
+                      "bf16_gemm_8192_tflops": round(gemm, 1),
+                      "bf16_gemm_frac_of_peak": round(gemm / PEAK_BF16_TFLOPS, 4),
+                      "hbm_read_512mib_gbs": round(read, 1),
+                      "hbm_read_frac_of_peak": round(read / PEAK_HBM_GBS, 4)}), flush=True)
+    return 0
+
+
 def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
     """S1 alone: store every key of the workload, --steps times; keys stored per second and the
     store kernel's HBM roofline (per key: 512 B of activations and 8 B of indices read, 132 or
@@ -163,6 +201,10 @@ def main() -> int:
     ap.add_argument("--store-population", action="store_true",
                     help="time only the store of the workload's whole key population (S1 alone): "
                          "keys stored per second and the store kernel's HBM roofline")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure what this GPU delivers to plain library code: torch's bf16 "
+                         "GEMM at 8192^3 (TFLOP/s) and torch's read of a 512 MiB tensor (GB/s), "
+                         "the latter from HBM after a read of another 512 MiB")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the "
                          "reference for scaling HBM byte counters); prints its bytes per copy")
@@ -176,6 +218,9 @@ def main() -> int:
     import torch  # noqa: PLC0415
     import sparse_attention_indexer_rmsnorm_amd as ix  # noqa: PLC0415
     from sparse_attention_indexer_rmsnorm_amd import workloads as W  # noqa: PLC0415
+
+    if args.ceilings:
+        return ceilings(args, torch)
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -266,8 +311,11 @@ def main() -> int:
         achieved = flops / (score_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    # the prefill-shaped batch runs the LDS-tiled rows kernel, a decode batch the split kernel
-    kernel = "score_kernel" if cfg in (2, 4) else "score_rows_kernel"
+    # prefill-shaped batches (>= 1024 queries, >= 4 per sequence) run a rows kernel (the bf16 one
+    # stages pages straight into LDS), the others the split kernel
+    prefill_shaped = wl.n_q >= 1024 and wl.n_q >= 4 * wl.n_seq
+    kernel = ("score_kernel" if not prefill_shaped else
+              "score_rows_bf16_kernel" if dtype == 1 else "score_rows_kernel")
     roof["traffic"] = committed_traffic(kernel, wl.name)
     roof["kernel"] = kernel
     roof["kernel_ms"] = round(score_ms, 4)
