@@ -33,9 +33,13 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBinBits = 12;
-constexpr int kBins = 1 << kBinBits;          // fine histogram bins per wave
-constexpr int kAreaWords = kBins / 2;         // 8 KiB per wave: histogram, then candidates, then slots
+constexpr int kBins = 1 << kBinBits;          // histogram bins of a workgroup
+constexpr int kWaveBinBits = 11;
+constexpr int kWaveBins = 1 << kWaveBinBits;  // histogram bins of a wave (32-bit counts)
+constexpr int kAreaWords = kWaveBins;         // 8 KiB per wave: histogram, then candidates, then slots
 constexpr int kWaveCand = kAreaWords;         // candidate keys that fit the area
+// candidates of the one-pass path: offset (4 B) and slot (2 B) each
+constexpr int kFastCand = (kAreaWords * 4 / 6) / 16 * 16;
 constexpr int kMaxTopk = 2048;
 constexpr int kSubBits = 7;                   // refinement digit width
 constexpr int kSubBins = 1 << kSubBits;
@@ -45,6 +49,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   u = (u << 1) == 0u ? 0u : u;                         // -0 == +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// order_key of a score that is not a NaN, in four instructions: adding +0 turns -0 into +0 and
+// leaves every other value as it is (fp32 denormals are kept), then the sign selects the mask.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
 
 // Value bits of a padding entry in an intermediate candidate list: a NaN pattern whose order key
@@ -139,42 +150,34 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t x, int src) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), src));
 }
 
-// Descending scan of the packed fine histogram (bin 2w in the low half of word w, bin 2w+1 in the
-// high half): the bin holding the want-th largest key, the count in higher bins and the bin's own
-// count.  Lane l first sums words [kAreaWords - 32 (l+1), kAreaWords - 32 l); the lane whose block
-// holds the crossing then has its 32 words spread over lanes 0..31 for the exact bin.
-__device__ __forceinline__ void wave_find_bin(const uint32_t* words, uint32_t want, int lane,
-                                              uint32_t* bin, uint32_t* above, uint32_t* count) {
-  const int lo_word = kAreaWords - 32 * (lane + 1);
-  const u32x4* blk = reinterpret_cast<const u32x4*>(words + lo_word);
+// Descending scan of nb 32-bit bins (nb a multiple of 64): the bin holding the want-th largest
+// entry, the count above it and its own count.  Lane l sums bins [nb - per (l+1), nb - per l);
+// then the crossing lane's bins are spread over the wave.
+template <int NB>
+__device__ __forceinline__ void wave_find_bin32(const uint32_t* bins, uint32_t want, int lane,
+                                                uint32_t* bin, uint32_t* above, uint32_t* count) {
+  constexpr int per = NB / 64;
+  static_assert(per % 4 == 0 && per <= 64 && ((per / 4) & (per / 4 - 1)) == 0, "bins per lane");
+  const u32x4* blk = reinterpret_cast<const u32x4*>(bins + NB - per * (lane + 1));
   uint32_t local = 0;
-  // chunk i of the block is read at step (i - lane) mod 8, so the lanes of a 16-lane group hit
-  // different banks (blocks are 128 B apart, which alone would map them onto the same banks)
+  // rotated chunk order: blocks are per * 4 B apart, so reading chunk i in every lane at once
+  // would put a whole 16-lane group on the same banks
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const u32x4 w = blk[(i + lane) & 7];
-    local += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) +
-             (w.z & 0xFFFFu) + (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
+  for (int i = 0; i < per / 4; ++i) {
+    const u32x4 v = blk[(i + lane) & (per / 4 - 1)];
+    local += (v.x + v.y) + (v.z + v.w);
   }
   const uint32_t run = wave_excl_scan(local, lane);
   const uint64_t hm = __ballot(run < want && run + local >= want);
   const int L = __builtin_amdgcn_readfirstlane(hm ? __builtin_ctzll(hm) : 0);
   const uint32_t run_l = lane_value(run, L);
-  // level 2: lane i < 32 takes word (top of block L) - i
-  const int wi = kAreaWords - 32 * L - 1 - (lane & 31);
-  const uint32_t word = lane < 32 ? words[wi] : 0u;
-  const uint32_t hi = word >> 16, lo = word & 0xFFFFu;
-  const uint32_t r2 = run_l + wave_excl_scan(hi + lo, lane);
-  // the high half (the larger bin) comes first in descending order
-  const bool hit_hi = lane < 32 && r2 < want && r2 + hi >= want;
-  const bool hit_lo = lane < 32 && r2 + hi < want && r2 + hi + lo >= want;
-  const uint64_t m = __ballot(hit_hi || hit_lo);
+  const int bi = NB - per * L - 1 - lane;               // lane i < per: the i-th bin from the top
+  const uint32_t c = lane < per ? bins[bi] : 0u;
+  const uint32_t r2 = run_l + wave_excl_scan(c, lane);
+  const uint64_t m = __ballot(lane < per && r2 < want && r2 + c >= want);
   const int src = __builtin_amdgcn_readfirstlane(m ? __builtin_ctzll(m) : 0);
-  const uint32_t b = hit_hi ? 2u * static_cast<uint32_t>(wi) + 1u : 2u * static_cast<uint32_t>(wi);
-  const uint32_t a = hit_hi ? r2 : r2 + hi;
-  const uint32_t c = hit_hi ? hi : lo;
-  *bin = lane_value(b, src);
-  *above = lane_value(a, src);
+  *bin = static_cast<uint32_t>(NB - per * L - 1 - src);
+  *above = lane_value(r2, src);
   *count = lane_value(c, src);
 }
 
@@ -223,119 +226,166 @@ __device__ __forceinline__ void refine(Visit visit, uint32_t prefix, int bits, u
   *eq_take = k_rem;
 }
 
-template <int E, bool HAS_IDX>
-__global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t area_all[4][kAreaWords];
-  __shared__ uint32_t sub_all[4][kSubBins];
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + wid;
-  if (task >= a.n_rows * a.n_seg) return;
+// One wave's selection task: a row, or one segment of a row.
+struct WaveTask {
+  const float* row;        // the task's scores
+  const int32_t* ridx;     // reported indices of the scores (candidate lists) or null
+  int32_t* oi;             // k output indices
+  float* ov;               // k output values or null
+  int64_t base_e;          // index of the task's first score within its row
+  int32_t n;               // scores in the task (wave-uniform)
+  int32_t k;
+  float pad_val;           // value reported for padding
+};
+
+__device__ __forceinline__ WaveTask wave_task(const TopkArgs& a, int64_t task) {
+  WaveTask t;
   const int64_t r = task / a.n_seg;
   const int32_t seg = static_cast<int32_t>(task % a.n_seg);
-  uint32_t* area = area_all[wid];
-  uint32_t* sub = sub_all[wid];
-
   int64_t len = a.row_len ? static_cast<int64_t>(a.row_len[r]) : a.row_stride;
   len = len < 0 ? 0 : (len > a.row_stride ? a.row_stride : len);
-  const int64_t base_e = static_cast<int64_t>(seg) * a.seg_len;
+  t.base_e = static_cast<int64_t>(seg) * a.seg_len;
   int64_t n64 = len;
   if (a.n_seg > 1) {
-    n64 = len - base_e;
+    n64 = len - t.base_e;
     n64 = n64 < 0 ? 0 : (n64 > a.seg_len ? a.seg_len : n64);
   }
-  const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(n64));   // wave-uniform
-  const int32_t k = a.k;
-  const float* row = a.scores + r * a.row_stride + base_e;
-  const int32_t* ridx = HAS_IDX ? a.src_idx + r * a.row_stride + base_e : nullptr;
-  int32_t* oi = a.out_idx + task * k;
-  float* ov = a.out_val ? a.out_val + task * k : nullptr;
-  const float pad_val = a.pad_bits ? __uint_as_float(kPadBits) : -INFINITY;
+  t.n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(n64));
+  t.k = a.k;
+  t.row = a.scores + r * a.row_stride + t.base_e;
+  t.ridx = a.src_idx ? a.src_idx + r * a.row_stride + t.base_e : nullptr;
+  t.oi = a.out_idx + task * a.k;
+  t.ov = a.out_val ? a.out_val + task * a.k : nullptr;
+  t.pad_val = a.pad_bits ? __uint_as_float(kPadBits) : -INFINITY;
+  return t;
+}
 
-  if (n <= k) {
-    // Everything is selected.  Loads use an in-range index in every lane and are issued in
-    // batches of 8 before the stores, so that they overlap.
-    for (int32_t p0 = 0; p0 < k; p0 += 8 * 64) {
-      int32_t id[8];
-      float v[8];
+// n <= k: everything is selected, then padding.  Loads use an in-range index in every lane and
+// are issued in batches of 8 before the stores, so that they overlap.
+template <bool HAS_IDX>
+__device__ __forceinline__ void select_all(const WaveTask& t, int lane) {
+  for (int32_t p0 = 0; p0 < t.k; p0 += 8 * 64) {
+    int32_t id[8];
+    float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int32_t e = p0 + i * 64 + lane;
-        const int32_t ec = e < n ? e : 0;
-        id[i] = HAS_IDX ? (n > 0 ? ridx[ec] : -1) : static_cast<int32_t>(base_e + ec);
-        v[i] = n > 0 ? row[ec] : 0.0f;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int32_t e = p0 + i * 64 + lane;
+      const int32_t ec = e < t.n ? e : 0;
+      id[i] = HAS_IDX ? (t.n > 0 ? t.ridx[ec] : -1) : static_cast<int32_t>(t.base_e + ec);
+      v[i] = t.n > 0 ? t.row[ec] : 0.0f;
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int32_t e = p0 + i * 64 + lane;
-        if (e < k) {
-          oi[e] = e < n ? id[i] : -1;
-          if (ov) ov[e] = e < n ? v[i] : pad_val;
-        }
+    for (int i = 0; i < 8; ++i) {
+      const int32_t e = p0 + i * 64 + lane;
+      if (e < t.k) {
+        t.oi[e] = e < t.n ? id[i] : -1;
+        if (t.ov) t.ov[e] = e < t.n ? v[i] : t.pad_val;
       }
     }
-    return;
   }
+}
 
-  // 1. keys in registers, all loads first (buffer loads, in range or returning 0) so that they are
-  //    in flight together.  Slots past the end hold key 0 like padding entries.  Key 0 is the lowest
-  //    key, and equal keys are taken in index order, so a slot past the end is never selected
-  //    (n > k real entries precede it); whole 64-slot groups past the end are skipped below with
-  //    a wave-uniform test, and the group holding the end is processed like any other.
-  uint32_t u[E];
+// The key range of a task, and the histogram scaling derived from it.
+struct KeyRange {
+  uint32_t kbase;   // smallest real key - 1: offsets are key - kbase (key 0 -> 0, others >= 1)
+  int shift;        // (largest offset >> shift) < kWaveBins
+  int32_t groups;   // 64-slot groups holding entries
+};
+
+// 1. keys in registers, all loads first (buffer loads, in range or returning 0) so that they are
+//    in flight together.  Slots past the end hold key 0 like padding entries.  Key 0 is the lowest
+//    key, and equal keys are taken in index order, so a slot past the end is never selected (n > k
+//    real entries precede it); whole 64-slot groups past the end are never looked at again (every
+//    later loop tests its group index against the wave-uniform group count), and only the group
+//    holding the end needs a per-lane test.  Scores hold no padding and take a plain minimum with
+//    the lanes past the end left out; candidate lists may hold padding (key 0) anywhere, and there
+//    key - 1 wraps key 0 to the top, out of the minimum.
+template <int E, bool HAS_IDX>
+__device__ __forceinline__ KeyRange load_keys(uint32_t (&u)[E], const WaveTask& t, int lane) {
   {
-    const __amdgpu_buffer_rsrc_t view = buffer_view(row, n);
+    const __amdgpu_buffer_rsrc_t view = buffer_view(t.row, t.n);
+    // an opaque lane offset: each call's loads form their addresses in place (immediate offsets
+    // from few bases) instead of sharing per-load address registers with another call
+    const uint32_t lane4 = after(static_cast<uint32_t>(lane) * 4u, 0u);
 #pragma unroll
     for (int j = 0; j < E; ++j)
-      u[j] = __builtin_amdgcn_raw_buffer_load_b32(view, lane * 4 + j * 256, 0, 0);
+      u[j] = __builtin_amdgcn_raw_buffer_load_b32(view, lane4 + j * 256, 0, 0);
   }
   launder(u);
+  KeyRange kr;
+  kr.groups = (t.n + 63) >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  {
+    const int32_t ng = fresh(kr.groups);
+    const int32_t rem = t.n - 64 * (ng - 1);    // entries in the last group, 1..64
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    u[j] = j * 64 + lane < n ? order_key(__uint_as_float(u[j])) : 0u;
-    kmin = min(kmin, u[j] ? u[j] : 0xFFFFFFFFu);
-    kmax = max(kmax, u[j]);
+    for (int j = 0; j < E; ++j) {
+      if (j < ng) {
+        uint32_t key = HAS_IDX ? order_key(__uint_as_float(u[j])) : score_key(__uint_as_float(u[j]));
+        uint32_t for_min = HAS_IDX ? key - 1u : key;
+        if (j == ng - 1) {
+          asm volatile("");   // a branch: only the group holding the end tests its lanes
+          key = lane < rem ? key : 0u;
+          for_min = lane < rem ? for_min : 0xFFFFFFFFu;
+        }
+        u[j] = key;
+        kmin = min(kmin, for_min);
+        kmax = max(kmax, key);
+      }
+    }
   }
-  // offsets: key 0 -> 0, other keys -> key - kmin + 1 >= 1 (order preserved)
-  const uint32_t kbase = wave_min(kmin) - 1u;
+  kr.kbase = HAS_IDX ? wave_min(kmin) : wave_min(kmin) - 1u;
   kmax = wave_max(kmax);
-  const uint32_t top_off = kmax ? kmax - kbase : 0u;
-  const int span = top_off ? 32 - __builtin_clz(top_off) : 0;
-  const int shift = span > kBinBits ? span - kBinBits : 0;   // (top_off >> shift) < kBins
-  auto off_of = [&](uint32_t key) { return key ? key - kbase : 0u; };
-  const int32_t groups = (n + 63) >> 6;       // 64-slot groups holding entries
+  const uint32_t top_off = kmax - kr.kbase;   // kmax is a real key: top_off >= 1
+  const int span = 32 - __builtin_clz(top_off);
+  kr.shift = span > kWaveBinBits ? span - kWaveBinBits : 0;
+  return kr;
+}
 
-  // 2. fine histogram of the offsets
+__device__ __forceinline__ uint32_t key_offset(uint32_t key, uint32_t kbase) {
+  return __builtin_elementwise_sub_sat(key, kbase);   // key 0 -> 0
+}
+
+// 2. histogram of the offsets (kWaveBins 32-bit bins filling the area), then the bin B holding
+//    the k-th largest key, the number of keys in higher bins and B's own count.
+template <int E>
+__device__ __forceinline__ void bin_of_kth(uint32_t (&u)[E], const KeyRange& kr, int32_t k,
+                                           uint32_t* area, int lane, uint32_t* bB,
+                                           uint32_t* above, uint32_t* c_b) {
 #pragma unroll
   for (int i = 0; i < kAreaWords / 256; ++i)
     reinterpret_cast<u32x4*>(area)[i * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
   launder(u);
   {
-    const int32_t ng = fresh(groups);
+    const int32_t ng = fresh(kr.groups);
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (j < ng) {
-      const uint32_t b = off_of(after(u[j], 0u)) >> shift;   // computed here, not hoisted
-      atomicAdd(&area[b >> 1], 1u << ((b & 1u) << 4));
-    }
+    for (int j = 0; j < E; ++j)   // after(): computed here, not hoisted
+      if (j < ng) atomicAdd(&area[key_offset(after(u[j], 0u), kr.kbase) >> kr.shift], 1u);
   }
-  }
-  uint32_t bB, above, c_b;
-  wave_find_bin(area, static_cast<uint32_t>(k), lane, &bB, &above, &c_b);
-  const uint32_t k_rem = static_cast<uint32_t>(k) - above;    // 1 <= k_rem <= c_b
+  wave_find_bin32<kWaveBins>(area, static_cast<uint32_t>(k), lane, bB, above, c_b);
+}
 
-  // 3. exact threshold among the offsets in bin B: gathered into the area (ballot compaction)
-  //    when they fit, otherwise filtered in registers.
+// 3-5. selection in index order: the exact threshold T among bin B's offsets (gathered into the
+// area by ballot compaction when they fit, otherwise filtered in registers on every radix pass),
+// then one compaction pass writing every key > T and the lowest-indexed keys == T, in index
+// order, so that each output row is sorted by index (candidate lists rely on this for ties).
+template <int E, bool HAS_IDX>
+__device__ __forceinline__ void select_ordered(uint32_t (&u)[E], const KeyRange& kr,
+                                               const WaveTask& t, uint32_t bB, uint32_t above,
+                                               uint32_t c_b, uint32_t* area, uint32_t* sub,
+                                               int lane) {
+  const uint32_t kbase = kr.kbase;
+  const int shift = kr.shift;
+  const uint32_t k_rem = static_cast<uint32_t>(t.k) - above;    // 1 <= k_rem <= c_b
   uint32_t t_off, eq_take;
   launder(u);
   if (c_b <= static_cast<uint32_t>(kWaveCand)) {
     uint32_t cnt = 0;
-    const int32_t ng = fresh(groups);
+    const int32_t ng = fresh(kr.groups);
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       if (j < ng) {
-        const uint32_t o = off_of(after(u[j], cnt));
+        const uint32_t o = key_offset(after(u[j], cnt), kbase);
         const bool ind = (o >> shift) == bB;
         const uint64_t m = __ballot(ind);
         if (ind) area[cnt + lanes_below(m)] = o;
@@ -348,11 +398,11 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
            bB, shift, k_rem, sub, lane, &t_off, &eq_take);
   } else {
     refine([&](auto add) {
-             const int32_t ng = fresh(groups);
+             const int32_t ng = fresh(kr.groups);
 #pragma unroll
              for (int j = 0; j < E; ++j) {
                if (j < ng) {
-                 const uint32_t o = off_of(after(u[j], 0u));   // recomputed every pass
+                 const uint32_t o = key_offset(after(u[j], 0u), kbase);   // recomputed every pass
                  if ((o >> shift) == bB) add(o);
                }
              }
@@ -361,13 +411,13 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
   }
   const uint32_t T = t_off ? t_off + kbase : 0u;
 
-  // 4. compaction in index order: a key > T goes to (#keys > T before it) + (#selected keys == T
-  //    before it); a key == T is selected while fewer than eq_take equal keys precede it.  Values
-  //    come from the keys (-0 is returned as +0); candidate lists record positions for step 5.
+  // a key > T goes to (#keys > T before it) + (#selected keys == T before it); a key == T is
+  // selected while fewer than eq_take equal keys precede it.  Values come from the keys (-0 is
+  // returned as +0); candidate lists record positions for the index gather below.
   uint16_t* sel = reinterpret_cast<uint16_t*>(area);
   launder(u);
   uint32_t gt_seen = 0, eq_seen = 0;
-  const int32_t ng = fresh(groups);
+  const int32_t ng = fresh(kr.groups);
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     if (j < ng) {
@@ -382,32 +432,213 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
       uint32_t pos = 0xFFFFFFFFu;
       if (gtv) pos = gpre + (epre < eq_take ? epre : eq_take);
       else if (eqv && epre < eq_take) pos = gpre + epre;
-      if (pos < static_cast<uint32_t>(k)) {
+      if (pos < static_cast<uint32_t>(t.k)) {
         if constexpr (HAS_IDX)   // the slot number is formed here rather than kept per key
           sel[pos] = static_cast<uint16_t>(after(static_cast<uint32_t>(lane), 0u) + j * 64);
-        else oi[pos] = static_cast<int32_t>(base_e + e);
-        if (ov) ov[pos] = uj ? key_value(uj) : pad_val;   // key 0: a padding entry
+        else t.oi[pos] = static_cast<int32_t>(t.base_e + e);
+        if (t.ov) t.ov[pos] = uj ? key_value(uj) : t.pad_val;   // key 0: a padding entry
       }
       gt_seen += static_cast<uint32_t>(__popcll(mg));
       eq_seen += static_cast<uint32_t>(__popcll(me));
     }
   }
-  // 5. candidate lists: the winners' original indices, gathered 8 per lane at a time
+  // candidate lists: the winners' original indices, gathered 8 per lane at a time
   if constexpr (HAS_IDX) {
-    for (int32_t p0 = 0; p0 < k; p0 += 8 * 64) {
+    for (int32_t p0 = 0; p0 < t.k; p0 += 8 * 64) {
       int32_t id[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int32_t p = p0 + i * 64 + lane;
-        id[i] = ridx[p < k ? sel[p] : 0];
+        id[i] = t.ridx[p < t.k ? sel[p] : 0];
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int32_t p = p0 + i * 64 + lane;
-        if (p < k) oi[p] = id[i];
+        if (p < t.k) t.oi[p] = id[i];
       }
     }
   }
+}
+
+// 3f-5f. selection of a whole row in any order, when bin B fits the list (c_b <= kFastCand):
+// one pass over the keys writes those in bins above B straight to the output (positions
+// 0..above-1, in index order) and lists bin B's offsets with their slots, in index order; the
+// radix passes then run over the list alone, and the list's winners (offsets > t_off, then the
+// first eq_take offsets == t_off in list order) fill positions above..k-1.  This takes one pass
+// over the registers fewer than select_ordered.
+template <int E, bool VALS>
+__device__ __forceinline__ void select_listed(uint32_t (&u)[E], const KeyRange& kr,
+                                              const WaveTask& t, uint32_t bB, uint32_t above,
+                                              uint32_t c_b, uint32_t* area, uint32_t* sub,
+                                              int lane) {
+  const uint32_t kbase = kr.kbase;
+  const int shift = kr.shift;
+  const uint32_t k_rem = static_cast<uint32_t>(t.k) - above;    // 1 <= k_rem <= c_b
+  uint32_t* cand = area;
+  uint16_t* slot = reinterpret_cast<uint16_t*>(area + kFastCand);
+  const __amdgpu_buffer_rsrc_t vi = buffer_view(reinterpret_cast<const float*>(t.oi), t.k);
+  const __amdgpu_buffer_rsrc_t vv = buffer_view(t.ov, VALS ? t.k : 0);
+  uint32_t n_gt = 0, n_in = 0;
+  launder(u);
+  const int32_t ng = fresh(kr.groups);
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (j < ng) {
+      const uint32_t uj = after(u[j], n_gt + n_in);
+      const uint32_t o = key_offset(uj, kbase);
+      const uint32_t b = o >> shift;
+      const bool gtv = b > bB;
+      const bool inv = b == bB;
+      const uint64_t mg = __ballot(gtv);
+      const uint64_t mi = __ballot(inv);
+      // the slot number is formed here rather than kept per key
+      const uint32_t e = after(static_cast<uint32_t>(lane), n_gt) + static_cast<uint32_t>(j * 64);
+      if (gtv) {
+        const uint32_t at = 4u * (n_gt + lanes_below(mg));
+        __builtin_amdgcn_raw_buffer_store_b32(e, vi, at, 0, 0);
+        if constexpr (VALS)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(uj)), vv, at, 0, 0);
+      }
+      if (inv) {
+        const uint32_t c = n_in + lanes_below(mi);
+        cand[c] = o;
+        slot[c] = static_cast<uint16_t>(e);
+      }
+      n_gt += static_cast<uint32_t>(__popcll(mg));
+      n_in += static_cast<uint32_t>(__popcll(mi));
+    }
+  }
+  uint32_t t_off, eq_take;
+  refine([&](auto add) {
+           for (uint32_t i = lane; i < c_b; i += 64) add(cand[i]);
+         },
+         bB, shift, k_rem, sub, lane, &t_off, &eq_take);
+  // t_off >= 1 (n > k real keys), so the 0 taken for a lane past the list is never selected
+  uint32_t gt_seen = 0, eq_seen = 0;
+  for (uint32_t i0 = 0; i0 < c_b; i0 += 64) {
+    const uint32_t i = i0 + static_cast<uint32_t>(lane);
+    const uint32_t o = i < c_b ? cand[i] : 0u;
+    const bool gtv = o > t_off;
+    const bool eqv = o == t_off;
+    const uint64_t mg = __ballot(gtv);
+    const uint64_t me = __ballot(eqv);
+    const uint32_t gpre = gt_seen + lanes_below(mg);
+    const uint32_t epre = eq_seen + lanes_below(me);
+    uint32_t pos = 0xFFFFFFFFu;
+    if (gtv) pos = gpre + (epre < eq_take ? epre : eq_take);
+    else if (eqv && epre < eq_take) pos = gpre + epre;
+    if (pos < k_rem) {
+      const uint32_t at = 4u * (above + pos);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(slot[i]), vi, at, 0, 0);
+      if constexpr (VALS)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(o + kbase)), vv, at, 0, 0);
+    }
+    gt_seen += static_cast<uint32_t>(__popcll(mg));
+    eq_seen += static_cast<uint32_t>(__popcll(me));
+  }
+}
+
+// The same selection when bin B does not fit the list (many equal keys): rolled loops that read
+// the row again (from cache) instead of the registers, so that this rare case adds little code.
+// The radix passes filter the row, then one pass in index order writes the keys above bin B to
+// positions 0..above-1 and bin B's winners (offsets > t_off, and the lowest-indexed offsets ==
+// t_off) to positions above..k-1.
+template <bool VALS>
+__device__ __forceinline__ void select_from_memory(const KeyRange& kr, const WaveTask& t, uint32_t bB,
+                                                uint32_t above, uint32_t* sub, int lane) {
+  const uint32_t kbase = kr.kbase;
+  const int shift = kr.shift;
+  const uint32_t k_rem = static_cast<uint32_t>(t.k) - above;
+  const __amdgpu_buffer_rsrc_t view = buffer_view(t.row, t.n);
+  auto key_at = [&](int32_t e) {   // key 0 past the end
+    const uint32_t key = score_key(__uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(view, static_cast<uint32_t>(e) * 4u, 0, 0)));
+    return e < t.n ? key : 0u;
+  };
+  uint32_t t_off, eq_take;
+  refine([&](auto add) {
+#pragma unroll 1
+           for (int32_t e = lane; e < t.n; e += 64) {
+             const uint32_t o = key_offset(key_at(e), kbase);
+             if ((o >> shift) == bB) add(o);
+           }
+         },
+         bB, shift, k_rem, sub, lane, &t_off, &eq_take);
+  const __amdgpu_buffer_rsrc_t vi = buffer_view(reinterpret_cast<const float*>(t.oi), t.k);
+  const __amdgpu_buffer_rsrc_t vv = buffer_view(t.ov, VALS ? t.k : 0);
+  uint32_t n_gt = 0, n_take = 0, eq_seen = 0;
+#pragma unroll 1
+  for (int32_t e0 = 0; e0 < t.n; e0 += 64) {
+    const int32_t e = e0 + lane;
+    const uint32_t key = key_at(e);
+    const uint32_t o = key_offset(key, kbase);
+    const bool gtv = (o >> shift) > bB;
+    const bool inv = (o >> shift) == bB;
+    const bool eqv = inv && o == t_off;
+    const uint64_t mg = __ballot(gtv);
+    const uint64_t me = __ballot(eqv);
+    const uint32_t epre = eq_seen + lanes_below(me);
+    const bool take = (inv && o > t_off) || (eqv && epre < eq_take);
+    const uint64_t mt = __ballot(take);
+    uint32_t at = 0xFFFFFFFFu;
+    if (gtv) at = 4u * (n_gt + lanes_below(mg));
+    if (take) at = 4u * (above + n_take + lanes_below(mt));
+    if (gtv || take) {
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(e), vi, at, 0, 0);
+      if constexpr (VALS)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key)), vv, at, 0, 0);
+    }
+    n_gt += static_cast<uint32_t>(__popcll(mg));
+    n_take += static_cast<uint32_t>(__popcll(mt));
+    eq_seen += static_cast<uint32_t>(__popcll(me));
+  }
+}
+
+// Row segments and candidate lists: output rows sorted by index.
+template <int E, bool HAS_IDX>
+__global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t area_all[4][kAreaWords];
+  __shared__ uint32_t sub_all[4][kSubBins];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+  if (task >= a.n_rows * a.n_seg) return;
+  const WaveTask t = wave_task(a, task);
+  if (t.n <= t.k) {
+    select_all<HAS_IDX>(t, lane);
+    return;
+  }
+  uint32_t u[E];
+  const KeyRange kr = load_keys<E, HAS_IDX>(u, t, lane);
+  uint32_t bB, above, c_b;
+  bin_of_kth<E>(u, kr, t.k, area_all[wid], lane, &bB, &above, &c_b);
+  select_ordered<E, HAS_IDX>(u, kr, t, bB, above, c_b, area_all[wid], sub_all[wid], lane);
+}
+
+// Whole rows of scores straight to the caller's output (order within a row unspecified), with
+// (VALS) or without their values.
+template <int E, bool VALS>
+__global__ __launch_bounds__(256) void topk_row_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t area_all[4][kAreaWords];
+  __shared__ uint32_t sub_all[4][kSubBins];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+  if (task >= a.n_rows) return;
+  WaveTask t = wave_task(a, task);
+  if constexpr (!VALS) t.ov = nullptr;
+  if (t.n <= t.k) {
+    select_all<false>(t, lane);
+    return;
+  }
+  uint32_t u[E];
+  const KeyRange kr = load_keys<E, false>(u, t, lane);
+  uint32_t bB, above, c_b;
+  bin_of_kth<E>(u, kr, t.k, area_all[wid], lane, &bB, &above, &c_b);
+  if (c_b <= static_cast<uint32_t>(kFastCand))
+    select_listed<E, VALS>(u, kr, t, bB, above, c_b, area_all[wid], sub_all[wid], lane);
+  else
+    select_from_memory<VALS>(kr, t, bB, above, sub_all[wid], lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -422,37 +653,6 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a) {
 constexpr int kBlockWaves = 16;
 constexpr int kBlockRowsMax = 128;     // batches with at most this many rows use the block kernel
 constexpr int kBlockMaxE = 32;        // 1024-lane groups leave 128 VGPRs: up to 32 keys per lane
-
-// Descending scan of nb 32-bit bins (nb a multiple of 64): the bin holding the want-th largest
-// entry, the count above it and its own count.  Lane l sums bins [nb - per (l+1), nb - per l);
-// then the crossing lane's bins are spread over the wave.
-template <int NB>
-__device__ __forceinline__ void wave_find_bin32(const uint32_t* bins, uint32_t want, int lane,
-                                                uint32_t* bin, uint32_t* above, uint32_t* count) {
-  constexpr int per = NB / 64;
-  static_assert(per % 4 == 0 && per <= 64 && ((per / 4) & (per / 4 - 1)) == 0, "bins per lane");
-  const u32x4* blk = reinterpret_cast<const u32x4*>(bins + NB - per * (lane + 1));
-  uint32_t local = 0;
-  // rotated chunk order: blocks are per * 4 B apart, so reading chunk i in every lane at once
-  // would put a whole 16-lane group on the same banks
-#pragma unroll
-  for (int i = 0; i < per / 4; ++i) {
-    const u32x4 v = blk[(i + lane) & (per / 4 - 1)];
-    local += (v.x + v.y) + (v.z + v.w);
-  }
-  const uint32_t run = wave_excl_scan(local, lane);
-  const uint64_t hm = __ballot(run < want && run + local >= want);
-  const int L = __builtin_amdgcn_readfirstlane(hm ? __builtin_ctzll(hm) : 0);
-  const uint32_t run_l = lane_value(run, L);
-  const int bi = NB - per * L - 1 - lane;               // lane i < per: the i-th bin from the top
-  const uint32_t c = lane < per ? bins[bi] : 0u;
-  const uint32_t r2 = run_l + wave_excl_scan(c, lane);
-  const uint64_t m = __ballot(lane < per && r2 < want && r2 + c >= want);
-  const int src = __builtin_amdgcn_readfirstlane(m ? __builtin_ctzll(m) : 0);
-  *bin = static_cast<uint32_t>(NB - per * L - 1 - src);
-  *above = lane_value(r2, src);
-  *count = lane_value(c, src);
-}
 
 constexpr int kBlockCand = 4096;       // threshold-bin keys refined from an LDS list
 
@@ -663,7 +863,13 @@ template <int E>
 hipError_t launch_wave(const TopkArgs& a, hipStream_t stream) {
   const int64_t tasks = a.n_rows * a.n_seg;
   const int64_t blocks = (tasks + 3) / 4;
-  if (a.src_idx)
+  if (a.n_seg == 1 && !a.src_idx && !a.pad_bits && a.out_val)
+    hipLaunchKernelGGL((topk_row_kernel<E, true>), dim3(static_cast<uint32_t>(blocks)), dim3(256),
+                       0, stream, a);
+  else if (a.n_seg == 1 && !a.src_idx && !a.pad_bits)
+    hipLaunchKernelGGL((topk_row_kernel<E, false>), dim3(static_cast<uint32_t>(blocks)), dim3(256),
+                       0, stream, a);
+  else if (a.src_idx)
     hipLaunchKernelGGL((topk_wave_kernel<E, true>), dim3(static_cast<uint32_t>(blocks)), dim3(256),
                        0, stream, a);
   else
