@@ -38,8 +38,11 @@ constexpr int kWaveBinBits = 11;
 constexpr int kWaveBins = 1 << kWaveBinBits;  // histogram bins of a wave (32-bit counts)
 constexpr int kAreaWords = kWaveBins;         // 8 KiB per wave: histogram, then candidates, then slots
 constexpr int kWaveCand = kAreaWords;         // candidate keys that fit the area
-// candidates of the one-pass path: offset (4 B) and slot (2 B) each
-constexpr int kFastCand = (kAreaWords * 4 / 6) / 16 * 16;
+// Whole-row selection works on blocks of kRowBlk groups of 64 keys without per-lane branches, so
+// that the scheduler can overlap the groups of a block.  Its list holds (offset, slot) pairs of
+// 8 B; the last 64 pairs of the area take the writes of lanes with nothing to list.
+constexpr int kRowBlk = 8;
+constexpr int kRowCand = kAreaWords / 2 - 64;
 constexpr int kMaxTopk = 2048;
 constexpr int kSubBits = 7;                   // refinement digit width
 constexpr int kSubBins = 1 << kSubBits;
@@ -103,11 +106,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const float* p, in
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, n * 4, 0x00020000);
 }
 
-// Number of lanes below this one whose bit is set in `mask` (wave64).
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+// Number of lanes below this one whose bit is set in `mask` (wave64), plus `base`.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask, uint32_t base = 0u) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), base));
 }
+
+// A wave-uniform constant the compiler cannot see through (emits nothing): per-group values
+// formed from it stay where they are used.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// A per-lane value the compiler cannot see through (emits nothing): a select between it and
+// another value stays a select instead of becoming a predicated block that computes it.
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// s_waitcnt operand: vector memory counter 0, the others left alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8)
+constexpr int kVmcnt0 = (7 << 4) | (15 << 8);
 
 // Cross-lane steps with DPP (no LDS traffic).  dpp<ctrl, row_mask>(x, id) returns, per lane, x of
 // the lane the control selects, or id where there is none (outside the 16-lane row, or in a row
@@ -460,64 +481,148 @@ __device__ __forceinline__ void select_ordered(uint32_t (&u)[E], const KeyRange&
   }
 }
 
-// 3f-5f. selection of a whole row in any order, when bin B fits the list (c_b <= kFastCand):
-// one pass over the keys writes those in bins above B straight to the output (positions
+// All E loads of a row in flight together (buffer loads: past the end they return 0).
+template <int E>
+__device__ __forceinline__ void issue_loads(uint32_t (&u)[E], const float* row, int32_t n,
+                                            int lane) {
+  const __amdgpu_buffer_rsrc_t view = buffer_view(row, n);
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    u[j] = __builtin_amdgcn_raw_buffer_load_b32(view, static_cast<uint32_t>(lane) * 4u + j * 256,
+                                                0, 0);
+}
+
+// 1r. keys of a whole row, block by block; only the block holding the row end tests its lanes,
+// and there every slot past the end (the rest of the block included) gets key 0 and stays out of
+// the minimum.  Blocks past the end are never looked at again.
+template <int E>
+__device__ __forceinline__ KeyRange row_keys(uint32_t (&u)[E], const WaveTask& t, int lane) {
+  static_assert(E % kRowBlk == 0, "whole blocks");
+  KeyRange kr;
+  kr.groups = (t.n + 63) >> 6;
+  const int32_t nb = fresh((kr.groups + kRowBlk - 1) / kRowBlk);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int b = 0; b < E / kRowBlk; ++b) {
+    if (b < nb) {
+      if (b == nb - 1) {
+        asm volatile("");   // a branch: only this block tests its lanes
+        const int32_t rem = t.n - b * kRowBlk * 64 - lane;   // slots of this lane left in the row
+#pragma unroll
+        for (int i = 0; i < kRowBlk; ++i) {
+          const int j = b * kRowBlk + i;
+          const bool valid = i * 64 < rem;
+          const uint32_t key = score_key(__uint_as_float(u[j]));
+          u[j] = valid ? key : 0u;
+          kmin = min(kmin, valid ? key : 0xFFFFFFFFu);
+          kmax = max(kmax, u[j]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRowBlk; ++i) {
+          const int j = b * kRowBlk + i;
+          u[j] = score_key(__uint_as_float(u[j]));
+          kmin = min(kmin, u[j]);
+          kmax = max(kmax, u[j]);
+        }
+      }
+    }
+  }
+  // every load has been used: say so explicitly, or the compiler, unable to prove it on every
+  // path, keeps waiting on the memory counter later, where it also counts the output stores
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  kr.kbase = wave_min(kmin) - 1u;
+  kmax = wave_max(kmax);
+  const uint32_t top_off = kmax - kr.kbase;   // kmax is a real key: top_off >= 1
+  const int span = 32 - __builtin_clz(top_off);
+  kr.shift = span > kWaveBinBits ? span - kWaveBinBits : 0;
+  return kr;
+}
+
+// 2r. histogram of a whole row's offsets, block by block (slots past the end count in bin 0),
+// then bin B as in bin_of_kth.  The offset base is made opaque per block so that no block's
+// arithmetic is moved ahead of the block.
+template <int E>
+__device__ __forceinline__ void row_bin_of_kth(uint32_t (&u)[E], const KeyRange& kr, int32_t k,
+                                               uint32_t* area, int lane, uint32_t* bB,
+                                               uint32_t* above, uint32_t* c_b) {
+#pragma unroll
+  for (int i = 0; i < kAreaWords / 256; ++i)
+    reinterpret_cast<u32x4*>(area)[i * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+  const int32_t nb = fresh((kr.groups + kRowBlk - 1) / kRowBlk);
+#pragma unroll
+  for (int b = 0; b < E / kRowBlk; ++b) {
+    if (b < nb) {
+      const uint32_t kb = opaque_s(kr.kbase);
+#pragma unroll
+      for (int i = 0; i < kRowBlk; ++i)
+        atomicAdd(&area[key_offset(u[b * kRowBlk + i], kb) >> kr.shift], 1u);
+    }
+  }
+  wave_find_bin32<kWaveBins>(area, static_cast<uint32_t>(k), lane, bB, above, c_b);
+}
+
+// 3r-5r. selection of a whole row in any order, when bin B > 0 fits the list: one pass over the
+// keys, block by block, writes those in bins above B straight to the output (positions
 // 0..above-1, in index order) and lists bin B's offsets with their slots, in index order; the
 // radix passes then run over the list alone, and the list's winners (offsets > t_off, then the
-// first eq_take offsets == t_off in list order) fill positions above..k-1.  This takes one pass
-// over the registers fewer than select_ordered.
+// first eq_take offsets == t_off in list order) fill positions above..k-1.  Lanes with nothing
+// to store write past the output view (dropped) or to their own spare list entry, so that no
+// group branches.  Slots past the row end hold key 0: bin 0 < B, never written.
 template <int E, bool VALS>
-__device__ __forceinline__ void select_listed(uint32_t (&u)[E], const KeyRange& kr,
-                                              const WaveTask& t, uint32_t bB, uint32_t above,
-                                              uint32_t c_b, uint32_t* area, uint32_t* sub,
-                                              int lane) {
-  const uint32_t kbase = kr.kbase;
+__device__ __forceinline__ void row_select(uint32_t (&u)[E], const KeyRange& kr,
+                                           const WaveTask& t, uint32_t bB, uint32_t above,
+                                           uint32_t c_b, uint32_t* area, uint32_t* sub, int lane) {
   const int shift = kr.shift;
   const uint32_t k_rem = static_cast<uint32_t>(t.k) - above;    // 1 <= k_rem <= c_b
-  uint32_t* cand = area;
-  uint16_t* slot = reinterpret_cast<uint16_t*>(area + kFastCand);
+  uint2* cand = reinterpret_cast<uint2*>(area);                  // (offset, slot)
   const __amdgpu_buffer_rsrc_t vi = buffer_view(reinterpret_cast<const float*>(t.oi), t.k);
   const __amdgpu_buffer_rsrc_t vv = buffer_view(t.ov, VALS ? t.k : 0);
+  // past every output view (k <= 2048 values); the bit pattern of 4.0f, which the hardware takes
+  // as an inline constant
+  constexpr uint32_t kDrop = 0x40800000u;
+  const uint32_t spare = static_cast<uint32_t>(kRowCand + lane);
   uint32_t n_gt = 0, n_in = 0;
-  launder(u);
-  const int32_t ng = fresh(kr.groups);
+  const int32_t nb = fresh((kr.groups + kRowBlk - 1) / kRowBlk);
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (j < ng) {
-      const uint32_t uj = after(u[j], n_gt + n_in);
-      const uint32_t o = key_offset(uj, kbase);
-      const uint32_t b = o >> shift;
-      const bool gtv = b > bB;
-      const bool inv = b == bB;
-      const uint64_t mg = __ballot(gtv);
-      const uint64_t mi = __ballot(inv);
-      // the slot number is formed here rather than kept per key
-      const uint32_t e = after(static_cast<uint32_t>(lane), n_gt) + static_cast<uint32_t>(j * 64);
-      if (gtv) {
-        const uint32_t at = 4u * (n_gt + lanes_below(mg));
+  for (int b = 0; b < E / kRowBlk; ++b) {
+    if (b < nb) {
+      const uint32_t kb = opaque_s(kr.kbase);
+#pragma unroll
+      for (int i = 0; i < kRowBlk; ++i) {
+        const int j = b * kRowBlk + i;
+        const uint32_t o = key_offset(u[j], kb);
+        const uint32_t bin = o >> shift;
+        const bool gtv = bin > bB;
+        const bool inv = bin == bB;
+        const uint64_t mg = __ballot(gtv);
+        const uint64_t mi = __ballot(inv);
+        // the slot number is formed here rather than kept per key (lane < 64: an OR)
+        const uint32_t e = static_cast<uint32_t>(lane) | opaque_s(static_cast<uint32_t>(j * 64));
+        // both positions are formed in every lane, then selected
+        const uint32_t pg = opaque_v(lanes_below(mg, n_gt));
+        const uint32_t pi = opaque_v(lanes_below(mi, n_in));
+        const uint32_t at = gtv ? 4u * pg : kDrop;
         __builtin_amdgcn_raw_buffer_store_b32(e, vi, at, 0, 0);
         if constexpr (VALS)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(uj)), vv, at, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(u[j])), vv, at, 0, 0);
+        cand[inv ? pi : spare] = make_uint2(o, e);
+        n_gt += static_cast<uint32_t>(__popcll(mg));
+        n_in += static_cast<uint32_t>(__popcll(mi));
       }
-      if (inv) {
-        const uint32_t c = n_in + lanes_below(mi);
-        cand[c] = o;
-        slot[c] = static_cast<uint16_t>(e);
-      }
-      n_gt += static_cast<uint32_t>(__popcll(mg));
-      n_in += static_cast<uint32_t>(__popcll(mi));
     }
   }
   uint32_t t_off, eq_take;
   refine([&](auto add) {
-           for (uint32_t i = lane; i < c_b; i += 64) add(cand[i]);
+           for (uint32_t i = lane; i < c_b; i += 64) add(cand[i].x);
          },
          bB, shift, k_rem, sub, lane, &t_off, &eq_take);
   // t_off >= 1 (n > k real keys), so the 0 taken for a lane past the list is never selected
   uint32_t gt_seen = 0, eq_seen = 0;
   for (uint32_t i0 = 0; i0 < c_b; i0 += 64) {
     const uint32_t i = i0 + static_cast<uint32_t>(lane);
-    const uint32_t o = i < c_b ? cand[i] : 0u;
+    const uint2 ce = i < c_b ? cand[i] : make_uint2(0u, 0u);
+    const uint32_t o = ce.x;
     const bool gtv = o > t_off;
     const bool eqv = o == t_off;
     const uint64_t mg = __ballot(gtv);
@@ -529,9 +634,9 @@ __device__ __forceinline__ void select_listed(uint32_t (&u)[E], const KeyRange& 
     else if (eqv && epre < eq_take) pos = gpre + epre;
     if (pos < k_rem) {
       const uint32_t at = 4u * (above + pos);
-      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(slot[i]), vi, at, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(ce.y, vi, at, 0, 0);
       if constexpr (VALS)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(o + kbase)), vv, at, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(o + kr.kbase)), vv, at, 0, 0);
     }
     gt_seen += static_cast<uint32_t>(__popcll(mg));
     eq_seen += static_cast<uint32_t>(__popcll(me));
@@ -632,11 +737,12 @@ __global__ __launch_bounds__(256) void topk_row_kernel(TopkArgs a) {
     return;
   }
   uint32_t u[E];
-  const KeyRange kr = load_keys<E, false>(u, t, lane);
+  issue_loads<E>(u, t.row, t.n, lane);
+  const KeyRange kr = row_keys<E>(u, t, lane);
   uint32_t bB, above, c_b;
-  bin_of_kth<E>(u, kr, t.k, area_all[wid], lane, &bB, &above, &c_b);
-  if (c_b <= static_cast<uint32_t>(kFastCand))
-    select_listed<E, VALS>(u, kr, t, bB, above, c_b, area_all[wid], sub_all[wid], lane);
+  row_bin_of_kth<E>(u, kr, t.k, area_all[wid], lane, &bB, &above, &c_b);
+  if (bB > 0 && c_b <= static_cast<uint32_t>(kRowCand))
+    row_select<E, VALS>(u, kr, t, bB, above, c_b, area_all[wid], sub_all[wid], lane);
   else
     select_from_memory<VALS>(kr, t, bB, above, sub_all[wid], lane);
 }
