@@ -53,7 +53,13 @@ def lib():
         L.oracle_rope_inv_freq.argtypes = [_p]
         L.oracle_store_keys.restype = _i64
         L.oracle_store_keys.argtypes = [_p, _p, ctypes.c_float, _p, _p, _i64, _p, _i32, _i32,
-                                        ctypes.c_int, _p, _i64, _p]
+                                        ctypes.c_int, _p, _i64, _p, ctypes.c_int]
+        L.oracle_hadamard_scale.restype = ctypes.c_double
+        L.oracle_hadamard_scale.argtypes = []
+        L.oracle_hadamard128.restype = None
+        L.oracle_hadamard128.argtypes = [_p]
+        L.oracle_rotate_q.restype = None
+        L.oracle_rotate_q.argtypes = [_p, _i64, _p]
         L.oracle_logits.restype = None
         L.oracle_logits.argtypes = [_p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p, _p, _p,
                                     _i64, _i64, _p, _i64, _p, _p]
@@ -124,8 +130,30 @@ def new_pool(n_pages: int, dtype: int, fill: int = 0xA5) -> np.ndarray:
     return np.full(n_pages * page_bytes(dtype), fill, dtype=np.uint8)
 
 
-def store_keys(x, gamma, eps, key_idx, key_seq, page_table, dtype, pool, want_k32=False):
-    """Store rows of x into ``pool`` (modified in place).  Returns (skipped, k32 or None)."""
+def hadamard_scale() -> float:
+    return float(lib().oracle_hadamard_scale())
+
+
+def hadamard128(v) -> np.ndarray:
+    """The normalised 128-point Walsh-Hadamard transform of each fp64 row of v (a copy)."""
+    v = np.array(v, dtype=np.float64, copy=True).reshape(-1, D)
+    for row in v:
+        lib().oracle_hadamard128(_ptr(row))
+    return v
+
+
+def rotate_q(q_bits) -> np.ndarray:
+    """bf16 bit patterns [..., 128] rotated like the keys of the rotated store."""
+    q_bits = _c(q_bits, np.uint16)
+    out = np.zeros_like(q_bits)
+    lib().oracle_rotate_q(_ptr(q_bits), q_bits.size // D, _ptr(out))
+    return out
+
+
+def store_keys(x, gamma, eps, key_idx, key_seq, page_table, dtype, pool, want_k32=False,
+               hadamard=False):
+    """Store rows of x into ``pool`` (modified in place).  Returns (skipped, k32 or None).
+    ``hadamard``: the rotated store (normalised Walsh-Hadamard transform after RoPE)."""
     x = _c(x, np.float32)
     gamma = _c(gamma, np.float32)
     key_idx = _c(key_idx, np.int32)
@@ -136,16 +164,17 @@ def store_keys(x, gamma, eps, key_idx, key_seq, page_table, dtype, pool, want_k3
     k32 = np.zeros((x.shape[0], D), np.float32) if want_k32 else None
     skipped = lib().oracle_store_keys(_ptr(x), _ptr(gamma), float(eps), _ptr(key_idx),
                                       _ptr(key_seq), x.shape[0], _ptr(pt), n_seq, max_pages,
-                                      int(dtype), _ptr(pool), n_pool, _ptr(k32))
+                                      int(dtype), _ptr(pool), n_pool, _ptr(k32),
+                                      1 if hadamard else 0)
     return int(skipped), k32
 
 
-def store_workload(wl, dtype, pool=None, want_k32=False, mask=None):
+def store_workload(wl, dtype, pool=None, want_k32=False, mask=None, hadamard=False):
     if pool is None:
         pool = new_pool(wl.n_pages_pool, dtype)
     sel = slice(None) if mask is None else mask
     skipped, k32 = store_keys(wl.x[sel], wl.gamma, wl.eps, wl.key_idx[sel], wl.key_seq[sel],
-                              wl.page_table, dtype, pool, want_k32)
+                              wl.page_table, dtype, pool, want_k32, hadamard)
     return pool, k32
 
 

@@ -34,6 +34,14 @@
  *    padded with index -1 and value -inf.
  *  - keys whose page-table entry lies outside the pool score -inf; keys with an out-of-range
  *    sequence, index or page are not stored.
+ *  - the rotated store ("The Fused Kernel Decision", Assumptions: the Hadamard transform's output
+ *    order is kept through the pipeline so that q and k stay aligned; "When the Fused Kernel
+ *    Isn't Enough", the fused vs. non-fused paths: normalisation, RoPE, Hadamard transform and
+ *    store in one kernel): after RoPE, the 128 dims are multiplied by the normalised Sylvester
+ *    Walsh-Hadamard matrix H / sqrt(128), H[i][j] = (-1)^popcount(i & j), computed in fp64 as the
+ *    fast transform (butterfly stages of spans 1, 2, ..., 64, (a, b) -> (a + b, a - b)) followed
+ *    by one multiplication with the fp64 value of 2^-3.5; the canonical key is the fp32 rounding
+ *    of that.  q is rotated by the same map (fp64, then fp32, then bf16 RNE) so that q.k is kept.
  */
 #include <math.h>
 #include <omp.h>
@@ -131,10 +139,43 @@ void oracle_rope_inv_freq(float out[32]) {
     for (int j = 0; j < 32; j++) out[j] = (float)pow(10000.0, -(2.0 * j) / 64.0);
 }
 
+/* 2^-3.5 = sqrt(2^-7): the square root of an exact power of two, correctly rounded. */
+double oracle_hadamard_scale(void) { return sqrt(1.0 / 128.0); }
+
+/* In-place normalised Walsh-Hadamard transform of 128 fp64 values (Sylvester order): butterfly
+ * stages of span h = 1, 2, 4, ..., 64, each mapping (v[i], v[i+h]) to (v[i] + v[i+h],
+ * v[i] - v[i+h]) for every i whose bit h is clear, then one multiplication by 2^-3.5. */
+void oracle_hadamard128(double* v) {
+    const double c = oracle_hadamard_scale();
+    for (int h = 1; h < OR_D; h *= 2) {
+        if (g_mutation == 14 && h == 8) continue;                 /* planted: a stage skipped */
+        for (int i = 0; i < OR_D; i++) {
+            if (i & h) continue;
+            double a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = (g_mutation == 15) ? b - a : a - b;        /* planted: difference sign */
+        }
+    }
+    for (int i = 0; i < OR_D; i++) v[i] *= (g_mutation == 16) ? 1.0 / 128.0 : c;  /* planted */
+}
+
+/* q rotated like the keys: each 128-dim bf16 vector to fp64, transformed, rounded to fp32 and
+ * then to bf16 (nearest-even). */
+void oracle_rotate_q(const uint16_t* q, int64_t n_vec, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_vec; n++) {
+        double v[OR_D];
+        for (int i = 0; i < OR_D; i++) v[i] = bf16_bits_value(q[n * OR_D + i]);
+        oracle_hadamard128(v);
+        for (int i = 0; i < OR_D; i++) out[n * OR_D + i] = oracle_bf16_encode((float)v[i]);
+    }
+}
+
 /* The canonical key of one row: fp64 RMSNorm over the 128 dims, scaled by gamma, then rotation of
- * the interleaved pairs of dims 64..127 by angle (4s) * inv_freq_j, rounded once to fp32. */
+ * the interleaved pairs of dims 64..127 by angle (4s) * inv_freq_j, then (rotated store) the
+ * normalised Hadamard transform, rounded once to fp32. */
 static void canonical_key(const float* x, const float* gamma, float eps, int32_t s,
-                          const float* inv_freq, float* k32) {
+                          const float* inv_freq, int hadamard, float* k32) {
     double y[OR_D];
     double ss = 0.0;
     int n_norm = (g_mutation == 3) ? 64 : OR_D;  /* planted: mean over half the dims */
@@ -155,6 +196,7 @@ static void canonical_key(const float* x, const float* gamma, float eps, int32_t
         y[i0] = a * c - b * sn;
         y[i1] = a * sn + b * c;
     }
+    if (hadamard) oracle_hadamard128(y);
     for (int i = 0; i < OR_D; i++) k32[i] = (float)y[i];
 }
 
@@ -163,7 +205,7 @@ static void canonical_key(const float* x, const float* gamma, float eps, int32_t
 int64_t oracle_store_keys(const float* x, const float* gamma, float eps, const int32_t* key_idx,
                           const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
                           int32_t n_seq, int32_t max_pages, int dtype, uint8_t* pool,
-                          int64_t n_pages_pool, float* k32_out) {
+                          int64_t n_pages_pool, float* k32_out, int hadamard) {
     float inv_freq[32];
     oracle_rope_inv_freq(inv_freq);
     int64_t skipped = 0;
@@ -183,7 +225,7 @@ int64_t oracle_store_keys(const float* x, const float* gamma, float eps, const i
             skipped++;
             continue;
         }
-        canonical_key(x + n * OR_D, gamma, eps, s, inv_freq, k32);
+        canonical_key(x + n * OR_D, gamma, eps, s, inv_freq, hadamard, k32);
         if (k32_out) memcpy(k32_out + n * OR_D, k32, sizeof(float) * OR_D);
         uint8_t* pg = pool + (int64_t)page * pb;
         int slot = s % OR_PAGE;

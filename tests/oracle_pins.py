@@ -408,4 +408,99 @@ def pin_needle_planting():
         assert c > 1 - 1e-6, c
 
 
+# ---- rotated store: the normalised Walsh-Hadamard transform -------------------------------------
+
+def _sylvester_matrix(n=D) -> np.ndarray:
+    """H[i][j] = (-1)^popcount(i & j): the Sylvester-Hadamard matrix from its bit definition."""
+    i = np.arange(n)
+    bits = np.bitwise_and.outer(i, i)
+    pop = np.zeros_like(bits)
+    for b in range(7):
+        pop += (bits >> b) & 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def _exact_two_pow_minus_3_5() -> float:
+    """The fp64 nearest to 2^-3.5, from 60-digit decimal arithmetic (float() of a Decimal rounds
+    correctly)."""
+    import decimal
+    ctx = decimal.Context(prec=60)
+    return float(ctx.sqrt(ctx.divide(decimal.Decimal(1), decimal.Decimal(128))))
+
+
+def pin_hadamard_scale_is_nearest():
+    c = oracle.hadamard_scale()
+    assert c == _exact_two_pow_minus_3_5()
+    assert abs(c * c * 128.0 - 1.0) < 4e-16
+
+
+def pin_hadamard_vs_bit_definition():
+    Hm = _sylvester_matrix()
+    assert np.array_equal(Hm @ Hm.T, 128.0 * np.eye(D))
+    x = _rng(30).standard_normal((12, D))
+    got = oracle.hadamard128(x)
+    want = (x @ Hm.T) * _exact_two_pow_minus_3_5()
+    assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(x))
+
+
+def pin_hadamard_unit_vectors_exact():
+    """A unit vector's transform is a column of H times the scale, exactly (every butterfly sum
+    is of +-1 and 0); the all-ones vector maps to sqrt(128) e_0."""
+    c = _exact_two_pow_minus_3_5()
+    Hm = _sylvester_matrix()
+    e = np.eye(D)
+    got = oracle.hadamard128(e)
+    assert np.array_equal(got, Hm.T * c)
+    ones = oracle.hadamard128(np.ones(D))[0]
+    assert ones[0] == 128.0 * c and np.all(ones[1:] == 0.0)
+
+
+def pin_hadamard_orthogonal_involution():
+    r = _rng(31)
+    a, b = r.standard_normal(D), r.standard_normal(D) * 1e3
+    ha, hb = oracle.hadamard128(a)[0], oracle.hadamard128(b)[0]
+    assert abs(np.dot(ha, hb) - np.dot(a, b)) <= 1e-12 * np.linalg.norm(a) * np.linalg.norm(b)
+    assert abs(np.linalg.norm(ha) - np.linalg.norm(a)) <= 1e-14 * np.linalg.norm(a)
+    assert np.max(np.abs(oracle.hadamard128(ha)[0] - a)) <= 1e-14 * np.max(np.abs(a))
+
+
+def pin_rotate_q_vs_matrix_and_torch():
+    """bf16 q: the matrix product is exact in fp64 here (sums of 128 bf16 values of similar
+    magnitude), times the scale, then torch's fp32 and bf16 casts (round-to-nearest-even)."""
+    q = _torch_bf16_bits(_rng(32).standard_normal((6, 64, D)).astype(np.float32))
+    got = oracle.rotate_q(q)
+    v = (_bf16_to_f64(q).reshape(-1, D) @ _sylvester_matrix().T) * _exact_two_pow_minus_3_5()
+    want = _torch_bf16_bits(v.astype(np.float32)).reshape(q.shape)
+    assert np.array_equal(got, want)
+
+
+def pin_rotated_store_composes():
+    """The rotated store's canonical key is the unrotated one rotated (up to the fp32 rounding of
+    each), its bf16 bytes are torch's casts of it, and rotated q . rotated k = q . k."""
+    r = _rng(33)
+    x = (r.standard_normal((30, D)) * r.choice([0.1, 1.0, 30.0], (30, 1))).astype(np.float32)
+    s = np.arange(30, dtype=np.int32) * 5 + 2
+    _, k_plain, _ = _store_rows(x, s, dtype=BF16)
+    gamma = np.ones(D, np.float32)
+    max_pages = int(s.max()) // PAGE + 1
+    pt = np.arange(max_pages, dtype=np.int32)[None, :]
+    pool = oracle.new_pool(max_pages, BF16)
+    _, k_rot = oracle.store_keys(x, gamma, 1e-6, s, None, pt, BF16, pool, want_k32=True,
+                                 hadamard=True)
+    c = _exact_two_pow_minus_3_5()
+    want = (k_plain.astype(np.float64) @ _sylvester_matrix().T) * c
+    amax = np.abs(k_plain).max(axis=1, keepdims=True)
+    assert np.all(np.abs(k_rot - want) <= 2.0 ** -21 * amax)
+    pb = oracle.page_bytes(BF16)
+    for i, si in enumerate(s):
+        base = pt[0, si // PAGE] * pb + (si % PAGE) * 256
+        assert np.array_equal(pool[base:base + 256].view(np.uint16), _torch_bf16_bits(k_rot[i]))
+    q = _bf16_to_f64(_torch_bf16_bits(r.standard_normal((4, D)).astype(np.float32)))
+    qr = _bf16_to_f64(oracle.rotate_q(_torch_bf16_bits(q.astype(np.float32))))
+    d_plain = q @ k_plain.astype(np.float64).T
+    d_rot = qr @ k_rot.astype(np.float64).T
+    scale = np.abs(q).sum(axis=1, keepdims=True) * amax.T
+    assert np.all(np.abs(d_rot - d_plain) <= 2.0 ** -6 * scale)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

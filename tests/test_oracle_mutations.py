@@ -4,13 +4,14 @@ The mistakes (selected in oracle.c by a switch that is off everywhere else): rot
 rotation pairs shifted by one dim, RMS over half the dims, gamma dropped, ReLU dropped, q read as
 [128][64], head weights shifted by one head, ties broken toward the higher index, e4m3 ties away
 from zero, the FNUZ maximum 240 instead of 448, bf16 truncation, visibility off by one, fp8 scale
-dropped on dequantisation.
+dropped on dequantisation, a Hadamard butterfly stage skipped, the butterfly difference negated,
+the Hadamard scale 1/128 instead of 2^-3.5.
 """
 import pytest
 
 from tests.oracle_pins import ALL_PINS
 
-MUTATIONS = list(range(1, 14))
+MUTATIONS = list(range(1, 17))
 
 
 @pytest.mark.parametrize("m", MUTATIONS)
