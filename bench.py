@@ -81,9 +81,10 @@ def _pairs(wl) -> int:
     return int(nv.sum()), nv
 
 
-def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int) -> dict:
+def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int, rotate: bool = False) -> dict:
     """The oracle as it stands, on every (n_q / n_sample_rows)-th query row of the same batch,
-    plus the store of the step's keys scaled to the same fraction of the batch."""
+    plus the store of the step's keys (and, rotated, the rotation of q) scaled to the same
+    fraction of the batch."""
     import oracle  # noqa: PLC0415  (test infrastructure; only this leg uses it)
     oracle.lib()
     stride = max(1, wl.n_q // n_sample_rows)
@@ -91,12 +92,13 @@ def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int) -> dict:
     frac = rows.size / wl.n_q
     pool = oracle.new_pool(wl.n_pages_pool, dtype)
     if x_step_mask is not None:
-        oracle.store_workload(wl, dtype, pool=pool, mask=~x_step_mask)
+        oracle.store_workload(wl, dtype, pool=pool, mask=~x_step_mask, hadamard=rotate)
     t0 = time.perf_counter()
-    oracle.store_workload(wl, dtype, pool=pool, mask=x_step_mask)
+    oracle.store_workload(wl, dtype, pool=pool, mask=x_step_mask, hadamard=rotate)
+    q_bits = oracle.rotate_q(wl.q_bits) if rotate else wl.q_bits
     t_store = time.perf_counter() - t0
     t0 = time.perf_counter()
-    lg, nv = oracle.logits(wl.q_bits, wl.w, pool, dtype, wl.page_table, wl.seq_lens, wl.cu_q,
+    lg, nv = oracle.logits(q_bits, wl.w, pool, dtype, wl.page_table, wl.seq_lens, wl.cu_q,
                            rows=rows)
     oracle.topk(lg, wl.k, row_len=nv)
     t_read = time.perf_counter() - t0
@@ -155,7 +157,7 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
 
     def step():
         ix.store_keys(d["x"], d["gamma"], d["key_idx"], d["page_table"], pool, dtype, eps=wl.eps,
-                      key_seq=d["key_seq"])
+                      key_seq=d["key_seq"], rotate=args.rotate)
 
     for _ in range(args.warmup):
         step()
@@ -172,13 +174,14 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
     algo = wl.n_keys * (512 + 8 + key_bytes)
     achieved = algo / (kms * 1e-3) / 1e9
     print(json.dumps({
-        "metric": "keys stored/s (S1: RMSNorm + RoPE + quantise + paged store)",
+        "metric": "keys stored/s (S1: RMSNorm + RoPE + " + ("Hadamard + " if args.rotate else "")
+                  + "quantise + paged store)",
         "value": wl.n_keys / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": wl.name + "-store-population", "keys": wl.n_keys,
-                   "kv_dtype": "fp8" if dtype == 0 else "bf16"},
+        "config": {"workload": wl.name + ("-rotated" if args.rotate else "") + "-store-population",
+                   "keys": wl.n_keys, "kv_dtype": "fp8" if dtype == 0 else "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "store_keys_kernel", "kernel_ms": round(kms, 4)},
@@ -201,6 +204,9 @@ def main() -> int:
     ap.add_argument("--store-population", action="store_true",
                     help="time only the store of the workload's whole key population (S1 alone): "
                          "keys stored per second and the store kernel's HBM roofline")
+    ap.add_argument("--rotate", action="store_true",
+                    help="the rotated store (Hadamard transform after RoPE): keys stored rotated "
+                         "and the batch's q rotated inside every step")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure what this GPU delivers to plain library code: torch's bf16 "
                          "GEMM at 8192^3 (TFLOP/s) and torch's read of a 512 MiB tensor (GB/s), "
@@ -255,7 +261,7 @@ def main() -> int:
     if pre.size:
         ix.store_keys(d["x"][pre].contiguous(), d["gamma"], d["key_idx"][pre].contiguous(),
                       d["page_table"], pool, dtype, eps=wl.eps,
-                      key_seq=d["key_seq"][pre].contiguous())
+                      key_seq=d["key_seq"][pre].contiguous(), rotate=args.rotate)
     sx = d["x"][stp].contiguous()
     sidx = d["key_idx"][stp].contiguous()
     sseq = d["key_seq"][stp].contiguous()
@@ -273,10 +279,13 @@ def main() -> int:
     flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     flush_sink = torch.empty((), dtype=torch.uint8, device=dev)
 
+    q_rot = torch.empty_like(d["q"]) if args.rotate else None
+
     def step(events=None):
         ix.store_keys(sx, d["gamma"], sidx, d["page_table"], pool, dtype, eps=wl.eps,
-                      key_seq=sseq)
-        ix.logits_topk(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"], d["cu_q"],
+                      key_seq=sseq, rotate=args.rotate)
+        q = ix.rotate_q(d["q"], out=q_rot) if args.rotate else d["q"]
+        ix.logits_topk(q, d["w"], pool, dtype, d["page_table"], d["seq_lens"], d["cu_q"],
                        wl.k, out_idx=out_idx, workspace=ws, events=events)
 
     for _ in range(args.warmup):
@@ -316,7 +325,8 @@ def main() -> int:
     prefill_shaped = wl.n_q >= 1024 and wl.n_q >= 4 * wl.n_seq
     kernel = ("score_kernel" if not prefill_shaped else
               "score_rows_bf16_kernel" if dtype == 1 else "score_rows_kernel")
-    roof["traffic"] = committed_traffic(kernel, wl.name)
+    name = wl.name + ("-rotated" if args.rotate else "")
+    roof["traffic"] = committed_traffic(kernel, name)
     roof["kernel"] = kernel
     roof["kernel_ms"] = round(score_ms, 4)
 
@@ -333,7 +343,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic" + (", MALL flushed before every step" if args.cold else ""),
-        "config": {"workload": wl.name, "queries": wl.n_q, "keys": int(wl.max_keys),
+        "config": {"workload": name, "queries": wl.n_q, "keys": int(wl.max_keys),
                    "visible_pairs": pairs, "k": wl.k, "kv_dtype": "fp8" if dtype == 0 else "bf16",
                    "keys_stored_in_step": int(stp.size), "heads": 64, "head_dim": 128,
                    "workspace_bytes": int(ws.numel())},
@@ -342,7 +352,8 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, dtype, wl.step_keys, args.cpu_sample_rows)
+        line["cpu_baseline"] = cpu_baseline(wl, dtype, wl.step_keys, args.cpu_sample_rows,
+                                            args.rotate)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -102,6 +102,29 @@ int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t*
                    int64_t n_pages_pool, void* stream);
 
 /*
+ * S1, rotated store: as idx_store_keys, with the key multiplied after RoPE (still in fp64, before
+ * the rounding to fp32) by the normalised 128-point Walsh-Hadamard matrix H / sqrt(128),
+ * H[i][j] = (-1)^popcount(i & j) ("When the Fused Kernel Isn't Enough", the fused vs. non-fused
+ * paths: the fused kernel applies normalisation, RoPE and the Hadamard transform before the
+ * store; "The Fused Kernel Decision", Assumptions: q and k must go through the same transform and
+ * element order).  Scores against such a cache need q rotated by idx_rotate_q; q.k is then the
+ * unrotated product up to the roundings.  Arguments and errors as idx_store_keys.
+ */
+int idx_store_keys_rotated(const float* x, const float* gamma, float eps, const int32_t* key_idx,
+                           const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
+                           int32_t n_seq, int32_t max_pages, int dtype, void* kcache,
+                           int64_t n_pages_pool, void* stream);
+
+/*
+ * q for a rotated cache: each of n_vec 128-dim bf16 vectors (a [n_q, 64, 128] q is n_q * 64
+ * vectors) multiplied by H / sqrt(128) in fp64, rounded to fp32 and then to bf16 (nearest-even).
+ * q          device bf16 [n_vec, 128]
+ * out        device bf16 [n_vec, 128]; may be q itself (in place)
+ * Errors: IDX_EINVAL (null pointer with n_vec > 0, n_vec < 0), IDX_EHIP.  n_vec == 0 is a no-op.
+ */
+int idx_rotate_q(const void* q, void* out, int64_t n_vec, void* stream);
+
+/*
  * Bytes of workspace idx_logits_topk uses for a call of this shape when the caller wants all
  * queries scored in one pass.  Any workspace of at least idx_logits_topk_min_workspace() bytes
  * works: the call then processes the queries in chunks that fit.  The bound never depends on
@@ -120,8 +143,9 @@ size_t idx_logits_topk_min_workspace(int32_t n_seq, int32_t max_pages, int32_t k
  * s < n_vis = min(floor((t+1)/4), max_pages*64) (key s covers tokens 4s..4s+3; t < 0 sees none).
  *   logit(i, s) = sum_h w[i,h] * max(0, sum_d q[i,h,d] * k[s,d])
  * with k the stored key (bf16, or e4m3 code * scale), computed with fp32 accumulation.
- * out_idx[i, :] receives the k keys s with the largest logits (ties to the lower s) in increasing
- * s order, then -1 padding when n_vis < k; out_val (optional) their logits, -inf for padding.
+ * out_idx[i, :] receives the k keys s with the largest logits (ties to the lower s), in an
+ * unspecified order within the row, then -1 padding when n_vis < k; out_val (optional) their
+ * logits in the same order, -inf for padding.
  * Keys whose page id lies outside [0, n_pages_pool) score -inf.
  *
  * q          device bf16 [n_q, 64, 128]
@@ -174,11 +198,12 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
  *          [0, row_stride]; row_len NULL = row_stride each).  Values must not be NaN; -0 and +0
  *          compare equal.
  * out_idx  device int32 [n_rows, k]: the column indices of the k largest values (ties to the lower
- *          index) in increasing index order, then -1; out_val (optional) device fp32 [n_rows, k]
- *          their values, then -inf.
+ *          index), in an unspecified order within the row, then -1; out_val (optional) device
+ *          fp32 [n_rows, k] their values in the same order, then -inf.
  * workspace device, at least idx_topk_rows_workspace_size(n_rows, row_stride, k) bytes (that size
- *          is 0, and workspace may be NULL, when every row is selected in one pass: rows of at most
- *          8192 scores in batches large enough to fill the GPU).
+ *          is 0, and workspace may be NULL, when every row is selected in one pass: batches of at
+ *          most 128 rows of at most 32768 scores, or rows of at most 6144 scores in batches large
+ *          enough to fill the GPU).
  * Errors: IDX_EINVAL (null pointer, n_rows < 0, row_stride < 1, k < 1 or k > IDX_MAX_TOPK),
  * IDX_EWORKSPACE, IDX_EHIP.
  */

@@ -35,6 +35,9 @@ SIGNATURES = [
     ("idx_page_bytes", _sz, [ctypes.c_int]),
     ("idx_store_keys", ctypes.c_int,
      [_p, _p, ctypes.c_float, _p, _p, _i64, _p, _i32, _i32, ctypes.c_int, _p, _i64, _p]),
+    ("idx_store_keys_rotated", ctypes.c_int,
+     [_p, _p, ctypes.c_float, _p, _p, _i64, _p, _i32, _i32, ctypes.c_int, _p, _i64, _p]),
+    ("idx_rotate_q", ctypes.c_int, [_p, _p, _i64, _p]),
     ("idx_logits_topk_workspace_size", _sz, [_i64, _i32, _i32, _i32]),
     ("idx_logits_topk_min_workspace", _sz, [_i32, _i32, _i32]),
     ("idx_logits_topk", ctypes.c_int,
@@ -114,8 +117,10 @@ def min_workspace(n_seq: int, max_pages: int, k: int) -> int:
 
 def store_keys(x: torch.Tensor, gamma: torch.Tensor, key_idx: torch.Tensor,
                page_table: torch.Tensor, kcache: torch.Tensor, dtype: int, *, eps: float = 1e-6,
-               key_seq: Optional[torch.Tensor] = None, stream=None) -> None:
-    """S1: RMSNorm + RoPE + quantise/store rows of x [n, 128] fp32 into the paged cache."""
+               key_seq: Optional[torch.Tensor] = None, rotate: bool = False,
+               stream=None) -> None:
+    """S1: RMSNorm + RoPE + quantise/store rows of x [n, 128] fp32 into the paged cache.
+    ``rotate``: the rotated store (Hadamard transform after RoPE); q then needs rotate_q."""
     n = x.shape[0] if x.dim() == 2 else -1
     if x.dim() != 2 or x.shape[1] != HEAD_DIM:
         raise ValueError("x must be [n_keys, 128]")
@@ -126,12 +131,28 @@ def store_keys(x: torch.Tensor, gamma: torch.Tensor, key_idx: torch.Tensor,
     if pb == 0:
         raise ValueError(f"unknown dtype {dtype}")
     n_pool = kcache.numel() // pb
-    st = lib().idx_store_keys(
+    fn = lib().idx_store_keys_rotated if rotate else lib().idx_store_keys
+    st = fn(
         _dev(x, "x", torch.float32), _dev(gamma, "gamma", torch.float32, HEAD_DIM), float(eps),
         _dev(key_idx, "key_idx", torch.int32, n), _dev(key_seq, "key_seq", torch.int32, n), n,
         _dev(page_table, "page_table", torch.int32), n_seq, max_pages, int(dtype),
         _dev(kcache, "kcache", torch.uint8), n_pool, _stream(stream))
-    _check(st, "idx_store_keys")
+    _check(st, "idx_store_keys_rotated" if rotate else "idx_store_keys")
+
+
+def rotate_q(q: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q (bf16, last dim 128) for a rotated cache; ``out`` may be q itself."""
+    if q.shape[-1] != HEAD_DIM:
+        raise ValueError("the last dim of q must be 128")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    n_vec = q.numel() // HEAD_DIM
+    st = lib().idx_rotate_q(_dev(q, "q", torch.bfloat16), _dev(out, "out", torch.bfloat16),
+                            n_vec, _stream(stream))
+    _check(st, "idx_rotate_q")
+    return out
 
 
 def _logits_args(q, w, kcache, dtype, page_table, seq_lens, cu_q):

@@ -204,10 +204,10 @@ size_t idx_page_bytes(int dtype) {
   return 0;
 }
 
-int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t* key_idx,
-                   const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
-                   int32_t n_seq, int32_t max_pages, int dtype, void* kcache,
-                   int64_t n_pages_pool, void* stream) {
+static int store_keys(const float* x, const float* gamma, float eps, const int32_t* key_idx,
+                      const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
+                      int32_t n_seq, int32_t max_pages, int dtype, void* kcache,
+                      int64_t n_pages_pool, void* stream, bool hadamard) {
   if (n_keys < 0 || n_seq < 0 || max_pages < 0 || n_pages_pool < 0) return IDX_EINVAL;
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return IDX_EINVAL;
   if (!dtype_ok(dtype)) return IDX_EUNSUPPORTED;
@@ -227,7 +227,32 @@ int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t*
   a.kcache = static_cast<uint8_t*>(kcache);
   a.n_pages_pool = n_pages_pool;
   a.rope = rope_table();
-  return hip_status(launch_store(a, dtype, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_store(a, dtype, hadamard, static_cast<hipStream_t>(stream)));
+}
+
+int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t* key_idx,
+                   const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
+                   int32_t n_seq, int32_t max_pages, int dtype, void* kcache,
+                   int64_t n_pages_pool, void* stream) {
+  return store_keys(x, gamma, eps, key_idx, key_seq, n_keys, page_table, n_seq, max_pages, dtype,
+                    kcache, n_pages_pool, stream, false);
+}
+
+int idx_store_keys_rotated(const float* x, const float* gamma, float eps, const int32_t* key_idx,
+                           const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,
+                           int32_t n_seq, int32_t max_pages, int dtype, void* kcache,
+                           int64_t n_pages_pool, void* stream) {
+  return store_keys(x, gamma, eps, key_idx, key_seq, n_keys, page_table, n_seq, max_pages, dtype,
+                    kcache, n_pages_pool, stream, true);
+}
+
+int idx_rotate_q(const void* q, void* out, int64_t n_vec, void* stream) {
+  if (n_vec < 0) return IDX_EINVAL;
+  if (n_vec == 0) return IDX_OK;
+  if (!q || !out) return IDX_EINVAL;
+  if (n_vec > (static_cast<int64_t>(INT32_MAX) - 255) / 8) return IDX_EINVAL;
+  return hip_status(launch_rotate_q(static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                                    n_vec, static_cast<hipStream_t>(stream)));
 }
 
 size_t idx_logits_topk_workspace_size(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t k) {

@@ -37,7 +37,8 @@ struct StoreArgs {
   RopeFreq rope;
 };
 
-hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_store(const StoreArgs& a, int dtype, bool hadamard, hipStream_t stream);
+hipError_t launch_rotate_q(const uint16_t* in, uint16_t* out, int64_t n_vec, hipStream_t stream);
 
 // One launch scores rows [q_begin, q_begin + n_rows) of the query batch against key columns
 // [0, n_cols).  Each wave owns one (row, chunk of chunk_keys columns) work item.

@@ -6,6 +6,12 @@
 // scale per key, 132 B/token; bf16 keys are 256 B/token ("When the Fused Kernel Isn't Enough",
 // Input Knowledge Required).
 //
+// The rotated store ("When the Fused Kernel Isn't Enough", the fused vs. non-fused paths: one
+// kernel normalises, applies RoPE and the Hadamard transform, and stores; "The Fused Kernel
+// Decision", Assumptions: q and k share the transform's output order) multiplies the key by the
+// normalised 128-point Walsh-Hadamard matrix after RoPE, before the rounding; q goes through the
+// same map (rotate_q_kernel), so q.k is kept.
+//
 // Work mapping: one half-wave (32 lanes) per key.  Lane j owns the unrotated dims 2j, 2j+1 and the
 // rotated pair (64+2j, 65+2j), so every lane evaluates exactly one sincos.  The arithmetic before
 // the format rounding is fp64 so that the stored bytes are a function of the inputs alone, not of
@@ -58,7 +64,51 @@ __device__ __forceinline__ float half_wave_max(float v) {
   return v;
 }
 
-template <int DT>
+// The nearest double to 2^-3.5 (sqrt(2) / 16): the normalisation of the 128-point transform.
+constexpr double kHadamardScale = 0x1.6a09e667f3bcdp-4;
+
+// Normalised 128-point Walsh-Hadamard transform (Sylvester order) of the vector a half-wave holds,
+// lane j (0..31) owning dims 2j, 2j+1 (v0, v1) and 64+2j, 65+2j (v2, v3).  Butterfly stages of
+// span h = 1, 2, ..., 64 map (x_i, x_{i+h}) to (x_i + x_{i+h}, x_i - x_{i+h}) for the i whose bit
+// h is clear; spans 1 and 64 pair values inside a lane, spans 2..32 pair lane j with lane
+// j ^ (h/2), the lower lane taking the sum and the upper one the difference.  The operations are
+// those of the definition, in a fixed order, so the fp64 result does not depend on the lane
+// mapping.  Then one multiplication by 2^-3.5.
+__device__ __forceinline__ void hadamard128(double& v0, double& v1, double& v2, double& v3,
+                                            int j) {
+#pragma clang fp contract(off)
+  double a = v0, b = v1;
+  v0 = a + b;
+  v1 = a - b;
+  a = v2;
+  b = v3;
+  v2 = a + b;
+  v3 = a - b;
+#pragma unroll
+  for (int m = 1; m <= 16; m <<= 1) {
+    const bool upper = (j & m) != 0;
+    const double p0 = __shfl_xor(v0, m, 64), p1 = __shfl_xor(v1, m, 64);
+    const double p2 = __shfl_xor(v2, m, 64), p3 = __shfl_xor(v3, m, 64);
+    v0 = upper ? p0 - v0 : v0 + p0;
+    v1 = upper ? p1 - v1 : v1 + p1;
+    v2 = upper ? p2 - v2 : v2 + p2;
+    v3 = upper ? p3 - v3 : v3 + p3;
+  }
+  a = v0;
+  b = v2;
+  v0 = a + b;
+  v2 = a - b;
+  a = v1;
+  b = v3;
+  v1 = a + b;
+  v3 = a - b;
+  v0 *= kHadamardScale;
+  v1 *= kHadamardScale;
+  v2 *= kHadamardScale;
+  v3 *= kHadamardScale;
+}
+
+template <int DT, bool HAD>
 __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
 #pragma clang fp contract(off)
   const int64_t n_raw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
@@ -87,8 +137,8 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
   double ss = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
   ss = half_wave_sum(ss);
   const double r = 1.0 / sqrt(ss / 128.0 + static_cast<double>(a.eps));
-  const double y0 = x0 * r * static_cast<double>(ga.x);
-  const double y1 = x1 * r * static_cast<double>(ga.y);
+  double y0 = x0 * r * static_cast<double>(ga.x);
+  double y1 = x1 * r * static_cast<double>(ga.y);
   double y2 = x2 * r * static_cast<double>(gb.x);
   double y3 = x3 * r * static_cast<double>(gb.y);
 
@@ -97,8 +147,10 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
                      static_cast<double>(a.rope.f[j]);
   double sn, cs;
   sincos(phi, &sn, &cs);
-  const double r2 = y2 * cs - y3 * sn;
-  const double r3 = y2 * sn + y3 * cs;
+  double r2 = y2 * cs - y3 * sn;
+  double r3 = y2 * sn + y3 * cs;
+  // the rotated store: the Hadamard transform of the whole key, still in fp64
+  if constexpr (HAD) hadamard128(y0, y1, r2, r3, j);
 
   const float k0 = static_cast<float>(y0), k1 = static_cast<float>(y1);
   const float k2 = static_cast<float>(r2), k3 = static_cast<float>(r3);
@@ -135,18 +187,99 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
   }
 }
 
+// Value of lane (lane ^ M) of the same quad, M = 1 or 2 (DPP quad permutation; no LDS).
+template <int M>
+__device__ __forceinline__ double quad_xor(double v) {
+  constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  const uint64_t u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, 0xF, 0xF,
+                                             false);
+  return __longlong_as_double((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                              static_cast<uint32_t>(lo));
+}
+
+// q of the rotated store: each 128-dim bf16 vector to fp64, the same transform as the keys, then
+// rounded to fp32 and to bf16 (nearest-even).  Four lanes (a quad) per vector, lane l holding
+// dims 32l..32l+31: butterfly spans 1..16 pair values inside a lane, spans 32 and 64 pair lane l
+// with lanes l ^ 1 and l ^ 2 (the lower taking the sum, the upper the difference), in the order
+// of hadamard128, so the fp64 result is the same.  Each quad reads its whole vector before it
+// writes, so in and out may be the same buffer.
+__global__ __launch_bounds__(256) void rotate_q_kernel(const uint16_t* in, uint16_t* out,
+                                                       int64_t n_vec) {
+#pragma clang fp contract(off)
+  const int64_t v = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 2;
+  const int l = threadIdx.x & 3;
+  if (v >= n_vec) return;   // whole quads leave together: the exchanges stay in a quad
+  const uint4* src = reinterpret_cast<const uint4*>(in + v * kHeadDim + 32 * l);
+  uint4 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = src[i];
+  double x[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[8 * i + 2 * k] = __uint_as_float(word[k] << 16);
+      x[8 * i + 2 * k + 1] = __uint_as_float(word[k] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i & h) continue;
+      const double a = x[i], b = x[i + h];
+      x[i] = a + b;
+      x[i + h] = a - b;
+    }
+  }
+  const bool up1 = (l & 1) != 0, up2 = (l & 2) != 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double p = quad_xor<1>(x[i]);
+    x[i] = up1 ? p - x[i] : x[i] + p;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double p = quad_xor<2>(x[i]);
+    x[i] = up2 ? p - x[i] : x[i] + p;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + v * kHeadDim + 32 * l);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t word[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      word[k] = bf16_rne(static_cast<float>(x[8 * i + 2 * k] * kHadamardScale)) |
+                (bf16_rne(static_cast<float>(x[8 * i + 2 * k + 1] * kHadamardScale)) << 16);
+    dst[i] = make_uint4(word[0], word[1], word[2], word[3]);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t stream) {
+hipError_t launch_store(const StoreArgs& a, int dtype, bool hadamard, hipStream_t stream) {
   if (a.n_keys <= 0) return hipSuccess;
   const int64_t keys_per_block = 256 / 32;
-  const int64_t blocks = (a.n_keys + keys_per_block - 1) / keys_per_block;
-  if (dtype == kBf16)
-    hipLaunchKernelGGL(store_keys_kernel<kBf16>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
+  const dim3 grid(static_cast<uint32_t>((a.n_keys + keys_per_block - 1) / keys_per_block));
+  if (dtype == kBf16 && hadamard)
+    hipLaunchKernelGGL((store_keys_kernel<kBf16, true>), grid, dim3(256), 0, stream, a);
+  else if (dtype == kBf16)
+    hipLaunchKernelGGL((store_keys_kernel<kBf16, false>), grid, dim3(256), 0, stream, a);
+  else if (hadamard)
+    hipLaunchKernelGGL((store_keys_kernel<kFp8, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(store_keys_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((store_keys_kernel<kFp8, false>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_q(const uint16_t* in, uint16_t* out, int64_t n_vec, hipStream_t stream) {
+  if (n_vec <= 0) return hipSuccess;
+  const int64_t vec_per_block = 256 / 4;
+  const dim3 grid(static_cast<uint32_t>((n_vec + vec_per_block - 1) / vec_per_block));
+  hipLaunchKernelGGL(rotate_q_kernel, grid, dim3(256), 0, stream, in, out, n_vec);
   return hipGetLastError();
 }
 

@@ -45,17 +45,17 @@ def dev_inputs(wl, x=None, device="cuda"):
     }
 
 
-def gpu_store(ix, wl, dtype, d, mask=None, pool=None):
+def gpu_store(ix, wl, dtype, d, mask=None, pool=None, rotate=False):
     if pool is None:
         pool = ix.new_cache(wl.n_pages_pool, dtype)
     if mask is None:
         ix.store_keys(d["x"], d["gamma"], d["key_idx"], d["page_table"], pool, dtype,
-                      eps=wl.eps, key_seq=d["key_seq"])
+                      eps=wl.eps, key_seq=d["key_seq"], rotate=rotate)
     else:
         m = torch.from_numpy(np.nonzero(mask)[0]).to(d["x"].device)
         ix.store_keys(d["x"][m].contiguous(), d["gamma"], d["key_idx"][m].contiguous(),
                       d["page_table"], pool, dtype, eps=wl.eps,
-                      key_seq=d["key_seq"][m].contiguous())
+                      key_seq=d["key_seq"][m].contiguous(), rotate=rotate)
     return pool
 
 
@@ -116,9 +116,9 @@ def check_topk_sets(gpu_idx: np.ndarray, ora_logits: np.ndarray, n_vis: np.ndarr
     return mean, n_exact_rows
 
 
-def oracle_rows(oracle, wl, pool, dtype, rows, row_len=None):
-    return oracle.logits(wl.q_bits, wl.w, pool, dtype, wl.page_table, wl.seq_lens, wl.cu_q,
-                         rows=rows, row_len=row_len)
+def oracle_rows(oracle, wl, pool, dtype, rows, row_len=None, q_bits=None):
+    return oracle.logits(wl.q_bits if q_bits is None else q_bits, wl.w, pool, dtype,
+                         wl.page_table, wl.seq_lens, wl.cu_q, rows=rows, row_len=row_len)
 
 
 def by_index(idx: torch.Tensor, val: torch.Tensor = None):
