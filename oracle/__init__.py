@@ -54,6 +54,11 @@ def lib():
         L.oracle_store_keys.restype = _i64
         L.oracle_store_keys.argtypes = [_p, _p, ctypes.c_float, _p, _p, _i64, _p, _i32, _i32,
                                         ctypes.c_int, _p, _i64, _p, ctypes.c_int]
+        L.oracle_logits_fp8q.restype = None
+        L.oracle_logits_fp8q.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p,
+                                         _p, _p, _i64, _i64, _p, _p]
+        L.oracle_quantize_q.restype = None
+        L.oracle_quantize_q.argtypes = [_p, _i64, _p, _p]
         L.oracle_hadamard_scale.restype = ctypes.c_double
         L.oracle_hadamard_scale.argtypes = []
         L.oracle_hadamard128.restype = None
@@ -200,6 +205,36 @@ def logits(q_bits, w, pool, dtype, page_table, seq_lens, cu_q, rows=None, row_le
                         max_pages, _ptr(_c(seq_lens, np.int32)), _ptr(_c(cu_q, np.int32)),
                         _ptr(rows), rows.size, row_len, _ptr(kr),
                         0 if ref_stride is None else int(ref_stride), _ptr(out), _ptr(nv))
+    return out, nv
+
+
+def quantize_q(q_bits):
+    """bf16 q [..., 128] -> (e4m3 codes [..., 128] uint8, fp32 scales [...]) per 128-dim vector."""
+    q_bits = _c(q_bits, np.uint16)
+    codes = np.zeros(q_bits.shape, np.uint8)
+    scales = np.zeros(q_bits.shape[:-1], np.float32)
+    lib().oracle_quantize_q(_ptr(q_bits), q_bits.size // D, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def logits_fp8q(q_codes, q_scales, w, pool, page_table, seq_lens, cu_q, rows=None,
+                row_len=None):
+    """fp64 logits with fp8 q (codes [n_q, 64, 128], scales [n_q, 64]) against an fp8 pool."""
+    q_codes = _c(q_codes, np.uint8)
+    q_scales = _c(q_scales, np.float32)
+    w = _c(w, np.float32)
+    pt = _c(page_table, np.int32)
+    n_seq, max_pages = pt.shape
+    n_q = q_codes.shape[0]
+    rows = np.arange(n_q, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    row_len = max_pages * PAGE if row_len is None else int(row_len)
+    out = np.empty((rows.size, row_len), np.float64)
+    nv = np.empty(rows.size, np.int64)
+    n_pool = pool.size // page_bytes(FP8)
+    lib().oracle_logits_fp8q(_ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(pool), FP8, n_pool,
+                             _ptr(pt), n_seq, max_pages, _ptr(_c(seq_lens, np.int32)),
+                             _ptr(_c(cu_q, np.int32)), _ptr(rows), rows.size, row_len,
+                             _ptr(out), _ptr(nv))
     return out, nv
 
 

@@ -42,6 +42,11 @@
  *    fast transform (butterfly stages of spans 1, 2, ..., 64, (a, b) -> (a + b, a - b)) followed
  *    by one multiplication with the fp64 value of 2^-3.5; the canonical key is the fp32 rounding
  *    of that.  q is rotated by the same map (fp64, then fp32, then bf16 RNE) so that q.k is kept.
+ *  - fp8 x fp8 scoring ("The Crash That Changed Direction", Experiment: fp8 keys go into the
+ *    product; the read path as a matrix product over heads): q of each (query, head) is quantised
+ *    like a key (one fp32 scale = absmax / 448, e4m3 codes of q_i / scale) and the logit is
+ *    sum_h w_h * max(0, sum_i (code_q * scale_q) * (code_k * scale_k)) with both operands taken
+ *    exactly in fp64.  The pages never quantise q; this variant is the fp8 product itself.
  */
 #include <math.h>
 #include <omp.h>
@@ -297,6 +302,19 @@ int64_t oracle_n_visible(int64_t t, int32_t max_pages) {
     return n < cap ? n : cap;
 }
 
+/* fp8 x fp8 scoring: q of query i, head h is e4m3 codes times one fp32 scale, taken exactly in
+ * fp64. */
+static double score_one_fp8q(const uint8_t* qc, const float* qs, const float* w, const double* k) {
+    double l = 0.0;
+    for (int h = 0; h < OR_H; h++) {
+        double sq = (g_mutation == 18) ? 1.0 : (double)qs[h];      /* planted: q scale dropped */
+        double d = 0.0;
+        for (int i = 0; i < OR_D; i++) d += oracle_e4m3_decode(qc[h * OR_D + i]) * sq * k[i];
+        l += (double)w[h] * fmax(0.0, d);
+    }
+    return l;
+}
+
 static double score_one(const uint16_t* q, const float* w, const double* k) {
     double l = 0.0;
     for (int h = 0; h < OR_H; h++) {
@@ -317,11 +335,13 @@ static double score_one(const uint16_t* q, const float* w, const double* k) {
  * logit of visible key s, -inf otherwise (and for keys on out-of-pool pages).  n_vis_out[r]
  * (nullable) receives the row's visible count.  If keys_ref is non-NULL the keys are read from
  * it ([n_seq][ref_stride][128] fp32) instead of the pool. */
-void oracle_logits(const uint16_t* q, const float* w, const uint8_t* pool, int dtype,
-                   int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
-                   int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q,
-                   const int64_t* rows, int64_t n_rows, int64_t row_len, const float* keys_ref,
-                   int64_t ref_stride, double* out, int64_t* n_vis_out) {
+/* Rows of logits; q is bf16 (q) or fp8 codes with per-(query, head) scales (qc, qs). */
+static void logits_rows(const uint16_t* q, const uint8_t* qc, const float* qs, const float* w,
+                        const uint8_t* pool, int dtype, int64_t n_pages_pool,
+                        const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                        const int32_t* seq_lens, const int32_t* cu_q, const int64_t* rows,
+                        int64_t n_rows, int64_t row_len, const float* keys_ref, int64_t ref_stride,
+                        double* out, int64_t* n_vis_out) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < n_rows; r++) {
         int64_t i = rows[r];
@@ -343,7 +363,46 @@ void oracle_logits(const uint16_t* q, const float* w, const uint8_t* pool, int d
             } else if (!fetch_key(pool, dtype, n_pages_pool, page_table, max_pages, b, (int32_t)s, k)) {
                 continue;
             }
-            o[s] = score_one(q + i * OR_H * OR_D, w + i * OR_H, k);
+            o[s] = q ? score_one(q + i * OR_H * OR_D, w + i * OR_H, k)
+                     : score_one_fp8q(qc + i * OR_H * OR_D, qs + i * OR_H, w + i * OR_H, k);
+        }
+    }
+}
+
+void oracle_logits(const uint16_t* q, const float* w, const uint8_t* pool, int dtype,
+                   int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                   int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q,
+                   const int64_t* rows, int64_t n_rows, int64_t row_len, const float* keys_ref,
+                   int64_t ref_stride, double* out, int64_t* n_vis_out) {
+    logits_rows(q, NULL, NULL, w, pool, dtype, n_pages_pool, page_table, n_seq, max_pages,
+                seq_lens, cu_q, rows, n_rows, row_len, keys_ref, ref_stride, out, n_vis_out);
+}
+
+void oracle_logits_fp8q(const uint8_t* q_codes, const float* q_scales, const float* w,
+                        const uint8_t* pool, int dtype, int64_t n_pages_pool,
+                        const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                        const int32_t* seq_lens, const int32_t* cu_q, const int64_t* rows,
+                        int64_t n_rows, int64_t row_len, double* out, int64_t* n_vis_out) {
+    logits_rows(NULL, q_codes, q_scales, w, pool, dtype, n_pages_pool, page_table, n_seq,
+                max_pages, seq_lens, cu_q, rows, n_rows, row_len, NULL, 0, out, n_vis_out);
+}
+
+/* q for fp8 x fp8 scoring: each 128-dim bf16 vector (one query head) gets one fp32 scale,
+ * fp32(absmax / 448), and e4m3 codes of the correctly rounded fp32 quotients q_i / scale, the
+ * rule of the fp8 key store; an all-zero vector gets scale 0 and codes 0. */
+void oracle_quantize_q(const uint16_t* q, int64_t n_vec, uint8_t* codes, float* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_vec; n++) {
+        double amax = 0.0;
+        for (int i = 0; i < OR_D; i++) amax = fmax(amax, fabs(bf16_bits_value(q[n * OR_D + i])));
+        float scale = (float)(amax / 448.0);
+        scales[n] = scale;
+        for (int i = 0; i < OR_D; i++) {
+            double v = bf16_bits_value(q[n * OR_D + i]);
+            uint8_t c = 0;
+            if (scale > 0.0f)
+                c = oracle_e4m3_encode(g_mutation == 17 ? (float)v : (float)(v / (double)scale));
+            codes[n * OR_D + i] = c;   /* planted (17): the quotient skipped */
         }
     }
 }

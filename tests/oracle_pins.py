@@ -503,4 +503,104 @@ def pin_rotated_store_composes():
     assert np.all(np.abs(d_rot - d_plain) <= 2.0 ** -6 * scale)
 
 
+# ---- fp8 x fp8 scoring: q quantised per (query, head) ----------------------------------------
+
+def pin_quantize_q_vs_torch():
+    """The scale is numpy's correctly rounded fp32 division absmax / 448; the codes are torch's
+    e4m3 cast of numpy's fp32 quotients; an all-zero vector gives scale 0 and codes 0."""
+    r = _rng(40)
+    v = (r.standard_normal((50, D)) * r.choice([1e-4, 1.0, 300.0], (50, 1))).astype(np.float32)
+    v[7] = 0.0
+    q = _torch_bf16_bits(v)
+    codes, scales = oracle.quantize_q(q)
+    qf = _bf16_to_f64(q).astype(np.float32)
+    amax = np.abs(qf).max(axis=1)
+    want_s = (amax / np.float32(448.0)).astype(np.float32)
+    assert np.array_equal(scales, want_s)
+    for n in range(50):
+        if want_s[n] == 0:
+            assert scales[n] == 0 and np.all(codes[n] == 0)
+            continue
+        quot = (qf[n] / want_s[n]).astype(np.float32)
+        want = torch.from_numpy(quot).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes[n], want), n
+
+
+def pin_quantize_q_error_bound():
+    q = _torch_bf16_bits(_rng(41).standard_normal((40, D)).astype(np.float32))
+    codes, scales = oracle.quantize_q(q)
+    deq = _torch_e4m3_to_f64(codes) * scales[:, None].astype(np.float64)
+    qf = _bf16_to_f64(q)
+    # half an e4m3 step (2^-4 relative) plus half the subnormal step, times the scale
+    assert np.all(np.abs(deq - qf) <= 2.0 ** -4 * np.abs(qf) + 2.0 ** -10 * scales[:, None])
+    # the largest element maps to the code 448 (up to the scale's own fp32 rounding)
+    amax = np.abs(qf).max(axis=1)
+    assert np.all(np.abs(np.abs(deq).max(axis=1) - amax) <= 2.0 ** -23 * amax)
+    assert np.all((codes & 0x7F).max(axis=1) == 0x7E)
+
+
+def _fp8q_case(seed):
+    r = _rng(seed)
+    n_keys, n_q = 130, 3
+    x = r.standard_normal((n_keys, D)).astype(np.float32)
+    pool, _, pt = _store_rows(x, np.arange(n_keys), dtype=FP8)
+    seq_lens = np.array([4 * n_keys + 3], np.int32)
+    cu_q = np.array([0, n_q], np.int32)
+    w = (r.standard_normal((n_q, H)) / 8).astype(np.float32)
+    return r, pool, pt, seq_lens, cu_q, w
+
+
+def pin_logits_fp8q_equals_bf16_path_on_exact_q():
+    """With power-of-two q scales, code * scale is a bf16 value: the fp8-q logits must equal the
+    bf16-q logits of those values exactly (same fp64 products, same order)."""
+    r, pool, pt, seq_lens, cu_q, w = _fp8q_case(42)
+    codes = r.integers(0, 0x7F, (3, H, D)).astype(np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes |= (r.integers(0, 2, codes.shape) << 7).astype(np.uint8)
+    scales = (2.0 ** r.integers(-6, 2, (3, H))).astype(np.float32)
+    qv = _torch_e4m3_to_f64(codes) * scales[:, :, None]
+    q_bits = _torch_bf16_bits(qv.astype(np.float32))
+    assert np.array_equal(_bf16_to_f64(q_bits), qv)
+    a, nva = oracle.logits(q_bits, w, pool, FP8, pt, seq_lens, cu_q)
+    b, nvb = oracle.logits_fp8q(codes, scales, w, pool, pt, seq_lens, cu_q)
+    assert np.array_equal(nva, nvb)
+    assert np.array_equal(a, b)
+
+
+def pin_logits_fp8q_scale_linear():
+    """Doubling every q scale doubles every logit exactly; a head with scale 0 drops out."""
+    r, pool, pt, seq_lens, cu_q, w = _fp8q_case(43)
+    q = _torch_bf16_bits(r.standard_normal((3, H, D)).astype(np.float32))
+    codes, scales = oracle.quantize_q(q)
+    a, _ = oracle.logits_fp8q(codes, scales, w, pool, pt, seq_lens, cu_q)
+    b, _ = oracle.logits_fp8q(codes, scales * 2, w, pool, pt, seq_lens, cu_q)
+    fin = np.isfinite(a)
+    assert np.array_equal(b[fin], 2 * a[fin])
+    w0 = w.copy()
+    w0[:, 5] = 0.0
+    s0 = scales.copy()
+    s0[:, 5] = 0.0
+    c, _ = oracle.logits_fp8q(codes, s0, w, pool, pt, seq_lens, cu_q)
+    d, _ = oracle.logits_fp8q(codes, scales, w0, pool, pt, seq_lens, cu_q)
+    assert np.allclose(c[fin], d[fin], rtol=1e-12, atol=1e-9)
+
+
+def pin_logits_fp8q_close_to_bf16_q():
+    """Quantising q moves each logit by at most the e4m3 rounding of q (2^-4 relative per
+    element), bounded per head by 2^-4 * sum_i |q_i| |k_i|."""
+    r, pool, pt, seq_lens, cu_q, w = _fp8q_case(44)
+    q = _torch_bf16_bits(r.standard_normal((3, H, D)).astype(np.float32))
+    codes, scales = oracle.quantize_q(q)
+    a, _ = oracle.logits(q, w, pool, FP8, pt, seq_lens, cu_q)
+    b, _ = oracle.logits_fp8q(codes, scales, w, pool, pt, seq_lens, cu_q)
+    kd = _pool_keys(pool, pt, FP8, 0, 130)
+    qf = np.abs(_bf16_to_f64(q))
+    bound = 2.0 ** -4 * np.einsum("nhd,sd->nhs", qf, np.abs(kd)) + 1e-6
+    bound = np.einsum("nh,nhs->ns", np.abs(w.astype(np.float64)), bound)
+    a, b = a[:, :130], b[:, :130]
+    fin = np.isfinite(a)
+    assert fin.sum() > 300
+    assert np.all(np.abs(a - b)[fin] <= bound[fin])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

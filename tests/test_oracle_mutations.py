@@ -5,13 +5,14 @@ rotation pairs shifted by one dim, RMS over half the dims, gamma dropped, ReLU d
 [128][64], head weights shifted by one head, ties broken toward the higher index, e4m3 ties away
 from zero, the FNUZ maximum 240 instead of 448, bf16 truncation, visibility off by one, fp8 scale
 dropped on dequantisation, a Hadamard butterfly stage skipped, the butterfly difference negated,
-the Hadamard scale 1/128 instead of 2^-3.5.
+the Hadamard scale 1/128 instead of 2^-3.5, q quantised without dividing by its scale, the q
+scale dropped from the fp8 x fp8 logit.
 """
 import pytest
 
 from tests.oracle_pins import ALL_PINS
 
-MUTATIONS = list(range(1, 17))
+MUTATIONS = list(range(1, 19))
 
 
 @pytest.mark.parametrize("m", MUTATIONS)
