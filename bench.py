@@ -28,11 +28,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 WORKLOADS = {
     # name: (config id, kv dtype)
     "prefill-22k-chunk8192-bf16": (3, 1),
+    "prefill-22k-chunk8192-fp8": (3, 0),
     "prefill-4k-fp8": (0, 0),
     "prefill-4k-bf16-needles": (1, 1),
     "decode-64x4k-22k-fp8": (2, 0),
@@ -49,6 +51,7 @@ KERNEL_SOURCES = {
     "score_rows_bf16_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "score_rows_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "score_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
+    "score_rows_fp8q_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
 }
 
 
@@ -180,7 +183,7 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": wl.name + ("-rotated" if args.rotate else "") + "-store-population",
+        "config": {"workload": args.workload + ("-rotated" if args.rotate else "") + "-store-population",
                    "keys": wl.n_keys, "kv_dtype": "fp8" if dtype == 0 else "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
@@ -207,6 +210,10 @@ def main() -> int:
     ap.add_argument("--rotate", action="store_true",
                     help="the rotated store (Hadamard transform after RoPE): keys stored rotated "
                          "and the batch's q rotated inside every step")
+    ap.add_argument("--fp8q", action="store_true",
+                    help="fp8 x fp8 scoring (fp8 cache only): the batch's q quantised per head "
+                         "inside every step, scored on the fp8 matrix cores; roofline against the "
+                         "fp8 peak")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure what this GPU delivers to plain library code: torch's bf16 "
                          "GEMM at 8192^3 (TFLOP/s) and torch's read of a 512 MiB tensor (GB/s), "
@@ -240,6 +247,9 @@ def main() -> int:
 
     ix.lib()
     cfg, dtype = WORKLOADS[args.workload]
+    if args.fp8q and (dtype != 0 or args.rotate):
+        print("--fp8q needs an fp8 workload and no --rotate", file=sys.stderr)
+        return 2
     wl = W.CONFIGS[cfg]() if cfg != 4 else W.cfg4(needles=False)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -284,6 +294,11 @@ def main() -> int:
     def step(events=None):
         ix.store_keys(sx, d["gamma"], sidx, d["page_table"], pool, dtype, eps=wl.eps,
                       key_seq=sseq, rotate=args.rotate)
+        if args.fp8q:
+            codes, scales = ix.quantize_q(d["q"])
+            ix.logits_topk_fp8q(codes, scales, d["w"], pool, d["page_table"], d["seq_lens"],
+                                d["cu_q"], wl.k, out_idx=out_idx, workspace=ws, events=events)
+            return
         q = ix.rotate_q(d["q"], out=q_rot) if args.rotate else d["q"]
         ix.logits_topk(q, d["w"], pool, dtype, d["page_table"], d["seq_lens"], d["cu_q"],
                        wl.k, out_idx=out_idx, workspace=ws, events=events)
@@ -318,14 +333,17 @@ def main() -> int:
     else:
         flops = 2.0 * 64 * 128 * pairs
         achieved = flops / (score_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+        peak = PEAK_FP8_TFLOPS if args.fp8q else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
     # prefill-shaped batches (>= 1024 queries, >= 4 per sequence) run a rows kernel (the bf16 one
     # stages pages straight into LDS), the others the split kernel
     prefill_shaped = wl.n_q >= 1024 and wl.n_q >= 4 * wl.n_seq
-    kernel = ("score_kernel" if not prefill_shaped else
+    kernel = ("score_rows_fp8q_kernel" if args.fp8q else
+              "score_kernel" if not prefill_shaped else
               "score_rows_bf16_kernel" if dtype == 1 else "score_rows_kernel")
-    name = wl.name + ("-rotated" if args.rotate else "")
+    # the bench's workload name (it names the cache dtype; the headline's equals wl.name)
+    name = args.workload + ("-rotated" if args.rotate else "") + ("-fp8q" if args.fp8q else "")
     roof["traffic"] = committed_traffic(kernel, name)
     roof["kernel"] = kernel
     roof["kernel_ms"] = round(score_ms, 4)
@@ -341,7 +359,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if args.fp8q else "bf16",
         "data": "synthetic" + (", MALL flushed before every step" if args.cold else ""),
         "config": {"workload": name, "queries": wl.n_q, "keys": int(wl.max_keys),
                    "visible_pairs": pairs, "k": wl.k, "kv_dtype": "fp8" if dtype == 0 else "bf16",
@@ -351,7 +369,7 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fp8q:
         line["cpu_baseline"] = cpu_baseline(wl, dtype, wl.step_keys, args.cpu_sample_rows,
                                             args.rotate)
     print(json.dumps(line), flush=True)

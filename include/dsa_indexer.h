@@ -191,6 +191,46 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
                      int32_t n_heads, float* out_logits, int32_t max_keys, void* stream);
 
 /*
+ * fp8 x fp8 scoring (the fp8 product of "The Crash That Changed Direction", Experiment, taken
+ * with q in fp8 as well, on the gfx950 fp8 matrix cores at twice the bf16 rate).
+ *
+ * idx_quantize_q: each 128-dim bf16 vector of q (one query head; a [n_q, 64, 128] q is n_q * 64
+ * vectors) gets one fp32 scale = fp32(max_i |q_i| / 448) and e4m3fn codes = RNE, saturating, of
+ * fp32(q_i / scale), the rule of the fp8 key store; an all-zero vector gets scale 0, codes 0.
+ * q        device bf16 [n_vec, 128]
+ * q_codes  device uint8 [n_vec, 128]
+ * q_scales device fp32 [n_vec]
+ * Errors: IDX_EINVAL (null pointer with n_vec > 0, n_vec < 0), IDX_EHIP.
+ *
+ * idx_logits_topk_fp8q / idx_logits_dense_fp8q: as idx_logits_topk / idx_logits_dense against an
+ * fp8 cache (IDX_KV_FP8_E4M3; there is no dtype argument), with
+ *   logit(i, s) = sum_h w[i,h] * max(0, sum_d (qc[i,h,d] * qs[i,h]) * (kc[s,d] * ks[s]))
+ * accumulated in fp32 from the exact products of e4m3 values.  q_codes is uint8 [n_q, 64, 128]
+ * and q_scales fp32 [n_q, 64] from idx_quantize_q (or any codes and non-negative scales).  The
+ * workspace rules and errors are those of idx_logits_topk; _timed records the two events around
+ * the scoring launches like idx_logits_topk_timed.
+ */
+int idx_quantize_q(const void* q, void* q_codes, float* q_scales, int64_t n_vec, void* stream);
+int idx_logits_topk_fp8q(const void* q_codes, const float* q_scales, const float* w,
+                         const void* kcache, int64_t n_pages_pool, const int32_t* page_table,
+                         int32_t n_seq, int32_t max_pages, const int32_t* seq_lens,
+                         const int32_t* cu_q, int64_t n_q, int32_t n_heads, int32_t k,
+                         int32_t* out_idx, float* out_val, void* workspace,
+                         size_t workspace_bytes, void* stream);
+int idx_logits_topk_fp8q_timed(const void* q_codes, const float* q_scales, const float* w,
+                               const void* kcache, int64_t n_pages_pool,
+                               const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                               const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                               int32_t n_heads, int32_t k, int32_t* out_idx, float* out_val,
+                               void* workspace, size_t workspace_bytes, void* ev_score_begin,
+                               void* ev_score_end, void* stream);
+int idx_logits_dense_fp8q(const void* q_codes, const float* q_scales, const float* w,
+                          const void* kcache, int64_t n_pages_pool, const int32_t* page_table,
+                          int32_t n_seq, int32_t max_pages, const int32_t* seq_lens,
+                          const int32_t* cu_q, int64_t n_q, int32_t n_heads, float* out_logits,
+                          int32_t max_keys, void* stream);
+
+/*
  * S3 alone: top-k of each row of a score matrix ("The Crash That Changed Direction", Context and
  * Pivot: the top-k op over indexer logits, k = 512 or 1024).
  *

@@ -303,13 +303,19 @@ int64_t oracle_n_visible(int64_t t, int32_t max_pages) {
 }
 
 /* fp8 x fp8 scoring: q of query i, head h is e4m3 codes times one fp32 scale, taken exactly in
- * fp64. */
-static double score_one_fp8q(const uint8_t* qc, const float* qs, const float* w, const double* k) {
-    double l = 0.0;
+ * fp64 (decoded once per query row). */
+static void decode_q_fp8(const uint8_t* qc, const float* qs, double* qd) {
     for (int h = 0; h < OR_H; h++) {
         double sq = (g_mutation == 18) ? 1.0 : (double)qs[h];      /* planted: q scale dropped */
+        for (int i = 0; i < OR_D; i++) qd[h * OR_D + i] = oracle_e4m3_decode(qc[h * OR_D + i]) * sq;
+    }
+}
+
+static double score_one_f64(const double* qd, const float* w, const double* k) {
+    double l = 0.0;
+    for (int h = 0; h < OR_H; h++) {
         double d = 0.0;
-        for (int i = 0; i < OR_D; i++) d += oracle_e4m3_decode(qc[h * OR_D + i]) * sq * k[i];
+        for (int i = 0; i < OR_D; i++) d += qd[h * OR_D + i] * k[i];
         l += (double)w[h] * fmax(0.0, d);
     }
     return l;
@@ -356,6 +362,8 @@ static void logits_rows(const uint16_t* q, const uint8_t* qc, const float* qs, c
         }
         if (n_vis_out) n_vis_out[r] = n_vis;
         double k[OR_D];
+        double qd[OR_H * OR_D];
+        if (!q) decode_q_fp8(qc + i * OR_H * OR_D, qs + i * OR_H, qd);
         for (int64_t s = 0; s < n_vis && s < row_len; s++) {
             if (keys_ref) {
                 const float* kr = keys_ref + ((int64_t)b * ref_stride + s) * OR_D;
@@ -364,7 +372,7 @@ static void logits_rows(const uint16_t* q, const uint8_t* qc, const float* qs, c
                 continue;
             }
             o[s] = q ? score_one(q + i * OR_H * OR_D, w + i * OR_H, k)
-                     : score_one_fp8q(qc + i * OR_H * OR_D, qs + i * OR_H, w + i * OR_H, k);
+                     : score_one_f64(qd, w + i * OR_H, k);
         }
     }
 }

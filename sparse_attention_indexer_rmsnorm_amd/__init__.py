@@ -48,6 +48,14 @@ SIGNATURES = [
       _p, _p, _p]),
     ("idx_logits_dense", ctypes.c_int,
      [_p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _p, _i32, _p]),
+    ("idx_quantize_q", ctypes.c_int, [_p, _p, _p, _i64, _p]),
+    ("idx_logits_topk_fp8q", ctypes.c_int,
+     [_p, _p, _p, _p, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _i32, _p, _p, _p, _sz, _p]),
+    ("idx_logits_topk_fp8q_timed", ctypes.c_int,
+     [_p, _p, _p, _p, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _i32, _p, _p, _p, _sz, _p, _p,
+      _p]),
+    ("idx_logits_dense_fp8q", ctypes.c_int,
+     [_p, _p, _p, _p, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _p, _i32, _p]),
     ("idx_topk_rows_workspace_size", _sz, [_i64, _i64, _i32]),
     ("idx_topk_rows", ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p]),
 ]
@@ -175,7 +183,8 @@ def logits_topk(q: torch.Tensor, w: torch.Tensor, kcache: torch.Tensor, dtype: i
                 out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
                 want_values: bool = False, workspace: Optional[torch.Tensor] = None,
                 events=None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """S2+S3: top-k key indices (and optionally logits) per query row, sorted by key index."""
+    """S2+S3: top-k key indices (and optionally logits) per query row, in an unspecified order
+    within the row."""
     args = _logits_args(q, w, kcache, dtype, page_table, seq_lens, cu_q)
     n_q = q.shape[0]
     n_seq, max_pages = page_table.shape
@@ -197,6 +206,79 @@ def logits_topk(q: torch.Tensor, w: torch.Tensor, kcache: torch.Tensor, dtype: i
                                          ctypes.c_void_p(ev1.cuda_event), _stream(stream))
     _check(st, "idx_logits_topk")
     return out_idx, out_val
+
+
+def quantize_q(q: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """q (bf16, [..., 128]) -> (e4m3 codes uint8 [..., 128], fp32 scales [...]) per 128-dim vector,
+    for fp8 x fp8 scoring."""
+    if q.shape[-1] != HEAD_DIM:
+        raise ValueError("the last dim of q must be 128")
+    codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    scales = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    n_vec = q.numel() // HEAD_DIM
+    st = lib().idx_quantize_q(_dev(q, "q", torch.bfloat16), _dev(codes, "q_codes", torch.uint8),
+                              _dev(scales, "q_scales", torch.float32, n_vec), n_vec,
+                              _stream(stream))
+    _check(st, "idx_quantize_q")
+    return codes, scales
+
+
+def _fp8q_args(q_codes, q_scales, w, kcache, page_table, seq_lens, cu_q):
+    if q_codes.dim() != 3 or q_codes.shape[1:] != (N_HEADS, HEAD_DIM):
+        raise ValueError("q_codes must be [n_q, 64, 128]")
+    n_q = q_codes.shape[0]
+    n_seq, max_pages = page_table.shape
+    return (_dev(q_codes, "q_codes", torch.uint8), _dev(q_scales, "q_scales", torch.float32,
+                                                         n_q * N_HEADS),
+            _dev(w, "w", torch.float32, n_q * N_HEADS), _dev(kcache, "kcache", torch.uint8),
+            kcache.numel() // page_bytes(0), _dev(page_table, "page_table", torch.int32), n_seq,
+            max_pages, _dev(seq_lens, "seq_lens", torch.int32, n_seq),
+            _dev(cu_q, "cu_q", torch.int32, n_seq + 1), n_q, N_HEADS)
+
+
+def logits_topk_fp8q(q_codes: torch.Tensor, q_scales: torch.Tensor, w: torch.Tensor,
+                     kcache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                     cu_q: torch.Tensor, k: int, *, out_idx: Optional[torch.Tensor] = None,
+                     out_val: Optional[torch.Tensor] = None, want_values: bool = False,
+                     workspace: Optional[torch.Tensor] = None, events=None,
+                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """S2+S3 with fp8 q (from quantize_q) against an fp8 cache."""
+    args = _fp8q_args(q_codes, q_scales, w, kcache, page_table, seq_lens, cu_q)
+    n_q = q_codes.shape[0]
+    n_seq, max_pages = page_table.shape
+    if out_idx is None:
+        out_idx = torch.empty((n_q, k), dtype=torch.int32, device=q_codes.device)
+    if out_val is None and want_values:
+        out_val = torch.empty((n_q, k), dtype=torch.float32, device=q_codes.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_size(n_q, n_seq, max_pages, k), dtype=torch.uint8,
+                                device=q_codes.device)
+    common = args + (int(k), _dev(out_idx, "out_idx", torch.int32, n_q * k),
+                     _dev(out_val, "out_val", torch.float32, n_q * k),
+                     _dev(workspace, "workspace", torch.uint8), workspace.numel())
+    if events is None:
+        st = lib().idx_logits_topk_fp8q(*common, _stream(stream))
+    else:
+        ev0, ev1 = events
+        st = lib().idx_logits_topk_fp8q_timed(*common, ctypes.c_void_p(ev0.cuda_event),
+                                              ctypes.c_void_p(ev1.cuda_event), _stream(stream))
+    _check(st, "idx_logits_topk_fp8q")
+    return out_idx, out_val
+
+
+def logits_dense_fp8q(q_codes: torch.Tensor, q_scales: torch.Tensor, w: torch.Tensor,
+                      kcache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                      cu_q: torch.Tensor, max_keys: int, *, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """S2 only with fp8 q, for checking: logits [n_q, max_keys], -inf where not visible."""
+    args = _fp8q_args(q_codes, q_scales, w, kcache, page_table, seq_lens, cu_q)
+    n_q = q_codes.shape[0]
+    if out is None:
+        out = torch.empty((n_q, max_keys), dtype=torch.float32, device=q_codes.device)
+    st = lib().idx_logits_dense_fp8q(*args, _dev(out, "out", torch.float32, n_q * max_keys),
+                                     int(max_keys), _stream(stream))
+    _check(st, "idx_logits_dense_fp8q")
+    return out
 
 
 def logits_dense(q: torch.Tensor, w: torch.Tensor, kcache: torch.Tensor, dtype: int,

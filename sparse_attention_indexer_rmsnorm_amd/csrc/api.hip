@@ -32,6 +32,7 @@ bool prefill_shaped(int64_t n_rows, int32_t n_seq) {
 }
 
 hipError_t score_launch(const ScoreArgs& a, int dtype, hipStream_t s) {
+  if (a.q8) return launch_score_fp8q(a, s);   // fp8 x fp8: one kernel for every batch shape
   // the rows kernel stages pages unconditionally, so it needs at least one page in the pool
   return prefill_shaped(a.n_rows, a.n_seq) && a.n_pages_pool > 0
              ? launch_score_rows(a, dtype, s)
@@ -128,8 +129,8 @@ ScoreArgs score_args(const void* q, const float* w, const void* kcache, int64_t 
   return s;
 }
 
-int logits_topk_impl(const void* q, const float* w, const void* kcache, int dtype,
-                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+int logits_topk_impl(const void* q, const float* q_scale, const float* w, const void* kcache,
+                     int dtype, int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
                      int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
                      int32_t n_heads, int32_t k, int32_t* out_idx, float* out_val,
                      void* workspace, size_t workspace_bytes, void* ev_begin, void* ev_end,
@@ -149,6 +150,11 @@ int logits_topk_impl(const void* q, const float* w, const void* kcache, int dtyp
   char* ws = static_cast<char*>(workspace);
   ScoreArgs sa = score_args(q, w, kcache, n_pages_pool, page_table, n_seq, max_pages, seq_lens,
                             cu_q);
+  if (q_scale) {   // fp8 x fp8: q is codes
+    sa.q = nullptr;
+    sa.q8 = static_cast<const uint8_t*>(q);
+    sa.q_scale = q_scale;
+  }
   sa.n_cols = cols;
   sa.out_stride = cols;
   sa.fill_invisible = 0;
@@ -276,8 +282,8 @@ int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype
                     int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
                     int32_t n_heads, int32_t k, int32_t* out_idx, float* out_val,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return logits_topk_impl(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
-                          seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, workspace,
+  return logits_topk_impl(q, nullptr, w, kcache, dtype, n_pages_pool, page_table, n_seq,
+                          max_pages, seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, workspace,
                           workspace_bytes, nullptr, nullptr, stream);
 }
 
@@ -287,15 +293,53 @@ int idx_logits_topk_timed(const void* q, const float* w, const void* kcache, int
                           int64_t n_q, int32_t n_heads, int32_t k, int32_t* out_idx,
                           float* out_val, void* workspace, size_t workspace_bytes,
                           void* ev_score_begin, void* ev_score_end, void* stream) {
-  return logits_topk_impl(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
-                          seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, workspace,
+  return logits_topk_impl(q, nullptr, w, kcache, dtype, n_pages_pool, page_table, n_seq,
+                          max_pages, seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, workspace,
                           workspace_bytes, ev_score_begin, ev_score_end, stream);
 }
 
-int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtype,
-                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
-                     int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
-                     int32_t n_heads, float* out_logits, int32_t max_keys, void* stream) {
+int idx_quantize_q(const void* q, void* q_codes, float* q_scales, int64_t n_vec, void* stream) {
+  if (n_vec < 0) return IDX_EINVAL;
+  if (n_vec == 0) return IDX_OK;
+  if (!q || !q_codes || !q_scales) return IDX_EINVAL;
+  if (n_vec > (static_cast<int64_t>(INT32_MAX) - 255) / 8) return IDX_EINVAL;
+  return hip_status(launch_quantize_q(static_cast<const uint16_t*>(q),
+                                      static_cast<uint8_t*>(q_codes), q_scales, n_vec,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int idx_logits_topk_fp8q(const void* q_codes, const float* q_scales, const float* w,
+                         const void* kcache, int64_t n_pages_pool, const int32_t* page_table,
+                         int32_t n_seq, int32_t max_pages, const int32_t* seq_lens,
+                         const int32_t* cu_q, int64_t n_q, int32_t n_heads, int32_t k,
+                         int32_t* out_idx, float* out_val, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (n_q > 0 && !q_scales) return IDX_EINVAL;
+  return logits_topk_impl(q_codes, n_q > 0 ? q_scales : nullptr, w, kcache, IDX_KV_FP8_E4M3,
+                          n_pages_pool, page_table, n_seq, max_pages, seq_lens, cu_q, n_q,
+                          n_heads, k, out_idx, out_val, workspace, workspace_bytes, nullptr,
+                          nullptr, stream);
+}
+
+int idx_logits_topk_fp8q_timed(const void* q_codes, const float* q_scales, const float* w,
+                               const void* kcache, int64_t n_pages_pool,
+                               const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                               const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                               int32_t n_heads, int32_t k, int32_t* out_idx, float* out_val,
+                               void* workspace, size_t workspace_bytes, void* ev_score_begin,
+                               void* ev_score_end, void* stream) {
+  if (n_q > 0 && !q_scales) return IDX_EINVAL;
+  return logits_topk_impl(q_codes, n_q > 0 ? q_scales : nullptr, w, kcache, IDX_KV_FP8_E4M3,
+                          n_pages_pool, page_table, n_seq, max_pages, seq_lens, cu_q, n_q,
+                          n_heads, k, out_idx, out_val, workspace, workspace_bytes,
+                          ev_score_begin, ev_score_end, stream);
+}
+
+static int logits_dense_impl(const void* q, const float* q_scale, const float* w,
+                             const void* kcache, int dtype, int64_t n_pages_pool,
+                             const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                             const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                             int32_t n_heads, float* out_logits, int32_t max_keys, void* stream) {
   int st = validate_logits_common(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
                                   seq_lens, cu_q, n_q, n_heads);
   if (st != IDX_OK) return st;
@@ -304,6 +348,11 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
   if (n_q == 0) return IDX_OK;
   ScoreArgs sa = score_args(q, w, kcache, n_pages_pool, page_table, n_seq, max_pages, seq_lens,
                             cu_q);
+  if (q_scale) {   // fp8 x fp8: q is codes
+    sa.q = nullptr;
+    sa.q8 = static_cast<const uint8_t*>(q);
+    sa.q_scale = q_scale;
+  }
   sa.q_begin = 0;
   sa.n_rows = n_q;
   sa.n_cols = max_keys;
@@ -313,6 +362,25 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
   sa.fill_invisible = 1;
   sa.row_nvis = nullptr;
   return hip_status(score_launch(sa, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtype,
+                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                     int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q, int64_t n_q,
+                     int32_t n_heads, float* out_logits, int32_t max_keys, void* stream) {
+  return logits_dense_impl(q, nullptr, w, kcache, dtype, n_pages_pool, page_table, n_seq,
+                           max_pages, seq_lens, cu_q, n_q, n_heads, out_logits, max_keys, stream);
+}
+
+int idx_logits_dense_fp8q(const void* q_codes, const float* q_scales, const float* w,
+                          const void* kcache, int64_t n_pages_pool, const int32_t* page_table,
+                          int32_t n_seq, int32_t max_pages, const int32_t* seq_lens,
+                          const int32_t* cu_q, int64_t n_q, int32_t n_heads, float* out_logits,
+                          int32_t max_keys, void* stream) {
+  if (n_q > 0 && !q_scales) return IDX_EINVAL;
+  return logits_dense_impl(q_codes, n_q > 0 ? q_scales : nullptr, w, kcache, IDX_KV_FP8_E4M3,
+                           n_pages_pool, page_table, n_seq, max_pages, seq_lens, cu_q, n_q,
+                           n_heads, out_logits, max_keys, stream);
 }
 
 size_t idx_topk_rows_workspace_size(int64_t n_rows, int64_t row_stride, int32_t k) {

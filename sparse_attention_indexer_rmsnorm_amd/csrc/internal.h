@@ -61,12 +61,19 @@ struct ScoreArgs {
   int64_t out_stride;
   int32_t fill_invisible;    // 1: write -inf to invisible columns < n_cols
   int32_t* row_nvis;         // [n_rows] visible-key count per row, or null
+  const uint8_t* q8;         // fp8 x fp8 scoring: q e4m3 codes [n_q, 64, 128], or null
+  const float* q_scale;      // [n_q, 64] scales of q8
 };
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 // Prefill-shaped variant: 4 query rows per workgroup share LDS-staged key pages; covers all
 // columns [0, n_cols) of each row (chunk_keys / n_chunks unused).
 hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream);
+// fp8 x fp8 scoring (q8 / q_scale set, fp8 cache): every batch shape, 4 rows per workgroup.
+hipError_t launch_score_fp8q(const ScoreArgs& a, hipStream_t stream);
+// q quantised per 128-dim vector: e4m3 codes and one fp32 scale each.
+hipError_t launch_quantize_q(const uint16_t* q, uint8_t* codes, float* scales, int64_t n_vec,
+                             hipStream_t stream);
 
 struct TopkArgs {
   const float* scores;       // [n_rows, row_stride]

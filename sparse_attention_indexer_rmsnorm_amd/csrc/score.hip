@@ -742,6 +742,233 @@ void score_rows_bf16_kernel(ScoreArgs a) {
   wait_counts<0, 0>();
 }
 
+// fp8 x fp8 scoring, prefill-shaped and any other batch: q arrives quantised per (query, head)
+// (e4m3 codes plus one fp32 scale) and the key codes go into v_mfma_f32_32x32x64_f8f6f4 as they
+// are, at twice the bf16 matrix rate.  The q scale is folded into the head weight and the key
+// scale multiplies the head-reduced sum (both are non-negative, so they commute with the ReLU).
+// The work split and the page pipeline are those of score_rows_bf16_kernel with W = 4: a page
+// buffer holds 64 key rows of 128 code bytes (the 16-byte chunks of row kk at chunk ^ (kk & 7))
+// and then the page's 64 scales; a page is 8 requests of 1 KiB (8 rows each) plus 256 B of
+// scales, each wave issuing two row requests and one scale request (4 lanes).
+//   Operand layout (by probe): in the 32x32x64 fp8 MFMA, lane (m, g) holds row / column m and the
+// 32 bytes of K half g, and A byte j of half g meets B byte j of half g.  Lane (m, g) therefore
+// holds dims 64 c + 32 g .. 64 c + 32 g + 31 of K chunk c (c = 0, 1) for q and keys alike.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kFp8PageCodes = kTileKeys * kHeadDim;              // 8192
+constexpr int kFp8Buf = kFp8PageCodes + kTileKeys * 4;          // 8448: codes then scales
+
+union Frag8 {
+  i32x8 v;
+  u32x4 h[2];
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void score_rows_fp8q_kernel(ScoreArgs a) {
+  constexpr int W = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t pg0[kFp8Buf];
+  __shared__ __attribute__((aligned(16))) uint8_t pg1[kFp8Buf];
+  __shared__ __attribute__((aligned(16))) uint8_t pg2[kFp8Buf];
+  __shared__ __attribute__((aligned(16))) float wsh[W][kHeads];
+  __shared__ int32_t seg_b[W];
+  __shared__ int32_t seg_nvis[W];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31;
+  const int g = lane >> 5;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * W + wid;
+  const bool row_ok = r < a.n_rows;
+  const int64_t i = a.q_begin + (row_ok ? r : a.n_rows - 1);
+
+  int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
+  int64_t n_vis = 0;
+  if (b >= 0) {
+    const int64_t q_len = a.cu_q[b + 1] - a.cu_q[b];
+    const int64_t t = static_cast<int64_t>(a.seq_lens[b]) - q_len + (i - a.cu_q[b]);
+    if (t >= 0) {
+      n_vis = (t + 1) / kRatio;
+      const int64_t cap = static_cast<int64_t>(a.max_pages) * kPageKeys;
+      n_vis = n_vis < cap ? n_vis : cap;
+    }
+  }
+  if (!row_ok) {
+    b = -1;
+    n_vis = 0;
+  }
+  const int32_t nv_own = static_cast<int32_t>(min<int64_t>(n_vis, a.n_cols));
+  float* out_row = a.out + (row_ok ? r : 0) * a.out_stride;
+  if (row_ok) {
+    if (a.row_nvis && lane == 0) a.row_nvis[r] = static_cast<int32_t>(n_vis);
+    if (a.fill_invisible)
+      for (int32_t s = nv_own + lane; s < a.n_cols; s += 64) out_row[s] = -INFINITY;
+  }
+  if (lane == 0) {
+    seg_b[wid] = nv_own > 0 ? b : -1;
+    seg_nvis[wid] = nv_own;
+  }
+
+  // A operand: this wave's q codes (both 32-head tiles, both K chunks); the head weights times
+  // the q scales wait in LDS.
+  Frag8 qa[2][2];
+  if (nv_own > 0) {
+    const uint8_t* qrow = a.q8 + i * (kHeads * kHeadDim);
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4* src =
+            reinterpret_cast<const u32x4*>(qrow + (32 * ht + m) * kHeadDim + 64 * c + 32 * g);
+        qa[ht][c].h[0] = src[0];
+        qa[ht][c].h[1] = src[1];
+      }
+    wsh[wid][lane] = a.w[i * kHeads + lane] * a.q_scale[i * kHeads + lane];
+  }
+  __syncthreads();
+
+  // Page staging: row request q (0..7) fills LDS rows 8 q .. 8 q + 7; lane L writes physical
+  // chunk L % 8 of row 8 q + L / 8, i.e. logical chunk (L % 8) ^ (L / 8) of that key.  The scale
+  // request of wave w copies scale bytes 64 w .. 64 w + 63 (lanes 0..3).
+  constexpr int n_req = 3;
+  const int dma_chunk = (lane & 7) ^ (lane >> 3);
+
+  for (int j = 0; j < W; ++j) {
+    const int32_t bj = seg_b[j];
+    if (bj < 0) continue;
+    bool seen = false;
+    int32_t nmax = 0;
+    for (int jj = 0; jj < W; ++jj) {
+      if (jj < j && seg_b[jj] == bj) seen = true;
+      if (seg_b[jj] == bj) nmax = max(nmax, seg_nvis[jj]);
+    }
+    if (seen) continue;
+    const bool mine = (b == bj) && nv_own > 0;
+    const int32_t bu = __builtin_amdgcn_readfirstlane(bj);
+    const int32_t* pt_row = a.page_table + static_cast<int64_t>(bu) * a.max_pages;
+    const int n_tiles = (nmax + kTileKeys - 1) / kTileKeys;
+    const int last = n_tiles - 1;
+    const __amdgpu_buffer_rsrc_t out_view = buffer_view(out_row, mine ? nv_own : 0);
+
+    auto page_id = [&](int tt) {
+      int idx = min(tt, last);
+      asm volatile("" : "+v"(idx));
+      return pt_row[idx];
+    };
+    auto valid = [&](int32_t pid) { return pid >= 0 && pid < a.n_pages_pool; };
+    auto stage = [&](uint8_t* dst, int32_t pu) {
+      if (a.n_pages_pool <= 0) return;   // no page to read (every key scores -inf)
+      const uint8_t* src = a.kcache + static_cast<int64_t>(pu) * kFp8PageBytes;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int q = wid + W * c;
+        __builtin_amdgcn_global_load_lds(src + (8 * q + (lane >> 3)) * kHeadDim + 16 * dma_chunk,
+                                         (lds_void*)(dst + q * 1024), 16, 0, 0);
+      }
+      if (lane < 4)
+        __builtin_amdgcn_global_load_lds(src + kFp8ScaleOffset + 64 * wid + 16 * lane,
+                                         (lds_void*)(dst + kFp8PageCodes + 64 * wid), 16, 0, 0);
+    };
+
+    int32_t pend_s = -kTileKeys;
+    float pend_v = 0.0f;
+    bool ok0, ok1;
+    int32_t pu2;
+    {
+      const int32_t p0 = __builtin_amdgcn_readfirstlane(page_id(0));
+      const int32_t p1 = __builtin_amdgcn_readfirstlane(page_id(1));
+      ok0 = valid(p0);
+      ok1 = valid(p1);
+      stage(pg0, ok0 ? p0 : 0);
+      const int32_t pid2 = page_id(2);
+      stage(pg1, ok1 ? p1 : 0);
+      wait_vmcnt_lgkm0(n_req);
+      __builtin_amdgcn_s_barrier();
+      pu2 = uniform_after_wait(pid2);
+    }
+
+    auto tile = [&](int t, const uint8_t* cur, uint8_t* nxt2) {
+      const int32_t p2 = pu2;
+      const bool ok2 = valid(p2);
+      const int32_t pid3 = page_id(t + 3);
+      stage(nxt2, ok2 ? p2 : 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), out_view,
+                                            (pend_s + lane) * 4, 0, 0);
+      pend_s = -kTileKeys;
+      const int32_t s_tile = t * kTileKeys;
+      if (mine && s_tile < nv_own) {
+        int mx = m & 7;                     // opaque: formed here, per page
+        asm volatile("" : "+v"(mx));
+        floatx16 acc[2][2] = {};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag8 kf[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const uint8_t* row = cur + (32 * kb + m) * kHeadDim;
+            kf[kb].h[0] = *reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + 2 * g) ^ mx));
+            kf[kb].h[1] = *reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + 2 * g + 1) ^ mx));
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+              acc[kb][ht] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  qa[ht][c].v, kf[kb].v, acc[kb][ht], 0, 0, 0, 0, 0, 0);
+        }
+        float p[2][4] = {};
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          float wv[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 w4 = *reinterpret_cast<const float4*>(&wsh[wid][32 * ht + 8 * q4 + 4 * g]);
+            wv[4 * q4 + 0] = w4.x;
+            wv[4 * q4 + 1] = w4.y;
+            wv[4 * q4 + 2] = w4.z;
+            wv[4 * q4 + 3] = w4.w;
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+              p[h][rr & 3] = fmaf(relu(acc[h][ht][rr]), wv[rr], p[h][rr & 3]);
+        }
+        float tot[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float part = (p[h][0] + p[h][1]) + (p[h][2] + p[h][3]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                           __float_as_uint(part), false, false);
+          tot[h] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        // lane (m, g) keeps key 32 g + m, times that key's scale
+        const float kscale = *reinterpret_cast<const float*>(cur + kFp8PageCodes + 4 * lane);
+        const float v = (g ? tot[1] : tot[0]) * kscale;
+        pend_v = ok0 ? v : -INFINITY;
+        pend_s = s_tile;
+      }
+      ok0 = ok1;
+      ok1 = ok2;
+      wait_vmcnt_lgkm0(n_req + 1);
+      __builtin_amdgcn_s_barrier();
+      pu2 = uniform_after_wait(pid3);
+    };
+
+    for (int t = 0; t < n_tiles; t += 3) {
+      tile(t, pg0, pg2);
+      if (t + 1 >= n_tiles) break;
+      tile(t + 1, pg1, pg0);
+      if (t + 2 >= n_tiles) break;
+      tile(t + 2, pg2, pg1);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), out_view, (pend_s + lane) * 4,
+                                          0, 0);
+    wait_counts<0, 0>();
+    __builtin_amdgcn_s_barrier();
+  }
+  wait_counts<0, 0>();
+}
+
 }  // namespace
 
 hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream) {
@@ -754,6 +981,14 @@ hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream) 
   }
   const int64_t blocks = (a.n_rows + 3) / 4;
   hipLaunchKernelGGL(score_rows_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_fp8q(const ScoreArgs& a, hipStream_t stream) {
+  if (a.n_rows <= 0) return hipSuccess;
+  const int64_t groups = (a.n_rows + 3) / 4;
+  hipLaunchKernelGGL(score_rows_fp8q_kernel, dim3(static_cast<uint32_t>(groups)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
 }

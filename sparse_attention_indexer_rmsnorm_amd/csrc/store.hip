@@ -258,7 +258,78 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(const uint16_t* in, uint1
   }
 }
 
+// e4m3_rne_sat without branches (the same code for every finite input of magnitude <= 2^15):
+// the normal-range and subnormal-range codes are both formed and one is selected, so lanes of
+// different magnitudes do not split the wave.
+__device__ __forceinline__ uint32_t e4m3_rne_sat_nb(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t m = ua & 0x7FFFFFu;
+  const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
+  const uint32_t nrm = min((((ua >> 23) - 120u) << 3) + r, 0x7Eu);
+  return (a < 0.015625f ? sub : nrm) | sign;
+}
+
+// q for fp8 x fp8 scoring, quantised like an fp8 key: four lanes (a quad) per 128-dim vector,
+// lane l holding dims 32l..32l+31; scale = fp32(absmax / 448) and codes = e4m3 RNE of
+// RN32(q_i / scale) (computed as RN32(q_i * RN64(1 / scale)), equal as for the keys: q_i is a
+// bf16 value, and |q_i / scale| <= 448 (1 + 2^-23) stays in e4m3_rne_sat_nb's range).
+__global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* q, uint8_t* codes,
+                                                         float* scales, int64_t n_vec) {
+  const int64_t v = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 2;
+  const int l = threadIdx.x & 3;
+  if (v >= n_vec) return;   // whole quads leave together
+  const uint4* src = reinterpret_cast<const uint4*>(q + v * kHeadDim + 32 * l);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 x = src[i];
+    w[4 * i] = x.x;
+    w[4 * i + 1] = x.y;
+    w[4 * i + 2] = x.z;
+    w[4 * i + 3] = x.w;
+  }
+  // |q| as bit patterns: the max of non-negative floats is the max of their patterns
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    amax = max(amax, max((w[i] << 16) & 0x7FFF0000u, w[i] & 0x7FFF0000u));
+  amax = max(amax, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                       0, static_cast<int>(amax), 0xB1, 0xF, 0xF, false)));   // quad xor 1
+  amax = max(amax, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                       0, static_cast<int>(amax), 0x4E, 0xF, 0xF, false)));   // quad xor 2
+  const float scale = static_cast<float>(static_cast<double>(__uint_as_float(amax)) / 448.0);
+  const double inv = scale > 0.0f ? 1.0 / static_cast<double>(scale) : 0.0;
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t bits = w[2 * i + k / 2];
+      const float f = __uint_as_float(k & 1 ? bits & 0xFFFF0000u : bits << 16);
+      word |= e4m3_rne_sat_nb(static_cast<float>(static_cast<double>(f) * inv)) << (8 * k);
+    }
+    c[i] = word;   // scale 0: every quotient is 0 (or -0 -> 0x80), replaced below
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + v * kHeadDim + 32 * l);
+  const bool zero = !(scale > 0.0f);
+  dst[0] = zero ? make_uint4(0, 0, 0, 0) : make_uint4(c[0], c[1], c[2], c[3]);
+  dst[1] = zero ? make_uint4(0, 0, 0, 0) : make_uint4(c[4], c[5], c[6], c[7]);
+  if (l == 0) scales[v] = scale;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_q(const uint16_t* q, uint8_t* codes, float* scales, int64_t n_vec,
+                             hipStream_t stream) {
+  if (n_vec <= 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>((n_vec + 63) / 64));
+  hipLaunchKernelGGL(quantize_q_kernel, grid, dim3(256), 0, stream, q, codes, scales, n_vec);
+  return hipGetLastError();
+}
 
 hipError_t launch_store(const StoreArgs& a, int dtype, bool hadamard, hipStream_t stream) {
   if (a.n_keys <= 0) return hipSuccess;
