@@ -84,7 +84,8 @@ def _pairs(wl) -> int:
     return int(nv.sum()), nv
 
 
-def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int, rotate: bool = False) -> dict:
+def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int, rotate: bool = False,
+                 fp8q: bool = False) -> dict:
     """The oracle as it stands, on every (n_q / n_sample_rows)-th query row of the same batch,
     plus the store of the step's keys (and, rotated, the rotation of q) scaled to the same
     fraction of the batch."""
@@ -99,10 +100,15 @@ def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int, rotate: bool = Fals
     t0 = time.perf_counter()
     oracle.store_workload(wl, dtype, pool=pool, mask=x_step_mask, hadamard=rotate)
     q_bits = oracle.rotate_q(wl.q_bits) if rotate else wl.q_bits
+    q8 = oracle.quantize_q(wl.q_bits) if fp8q else None
     t_store = time.perf_counter() - t0
     t0 = time.perf_counter()
-    lg, nv = oracle.logits(q_bits, wl.w, pool, dtype, wl.page_table, wl.seq_lens, wl.cu_q,
-                           rows=rows)
+    if fp8q:
+        lg, nv = oracle.logits_fp8q(q8[0], q8[1], wl.w, pool, wl.page_table, wl.seq_lens,
+                                    wl.cu_q, rows=rows)
+    else:
+        lg, nv = oracle.logits(q_bits, wl.w, pool, dtype, wl.page_table, wl.seq_lens, wl.cu_q,
+                               rows=rows)
     oracle.topk(lg, wl.k, row_len=nv)
     t_read = time.perf_counter() - t0
     secs = t_store * frac + t_read
@@ -369,9 +375,9 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not args.fp8q:
+    if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, dtype, wl.step_keys, args.cpu_sample_rows,
-                                            args.rotate)
+                                            args.rotate, args.fp8q)
     print(json.dumps(line), flush=True)
     return 0
 
