@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liboracle.so")
 _lib = None
 
-FP8, BF16 = 0, 1
+FP8, BF16, FP4 = 0, 1, 2
 D, H, PAGE, RATIO = 128, 64, 64, 4
 
 _p = ctypes.c_void_p
@@ -43,6 +43,10 @@ def lib():
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_encode.restype = ctypes.c_uint8
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
         L.oracle_bf16_encode.restype = ctypes.c_uint16
         L.oracle_bf16_encode.argtypes = [ctypes.c_float]
         L.oracle_page_bytes.restype = _i64
@@ -113,6 +117,17 @@ def bf16_encode(v) -> np.ndarray:
     L = lib()
     v = np.asarray(v, dtype=np.float32).ravel()
     return np.array([L.oracle_bf16_encode(float(x)) for x in v], dtype=np.uint16)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    L = lib()
+    return np.array([L.oracle_e2m1_decode(int(c)) for c in np.asarray(codes).ravel()])
+
+
+def e2m1_encode(v) -> np.ndarray:
+    L = lib()
+    v = np.asarray(v, dtype=np.float32).ravel()
+    return np.array([L.oracle_e2m1_encode(float(x)) for x in v], dtype=np.uint8)
 
 
 def page_bytes(dtype: int) -> int:

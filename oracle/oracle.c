@@ -42,6 +42,11 @@
  *    fast transform (butterfly stages of spans 1, 2, ..., 64, (a, b) -> (a + b, a - b)) followed
  *    by one multiplication with the fp64 value of 2^-3.5; the canonical key is the fp32 rounding
  *    of that.  q is rotated by the same map (fp64, then fp32, then bf16 RNE) so that q.k is kept.
+ *  - fp4 keys ("The Fused Kernel Decision", Input Knowledge: the indexer also has an fp4 variant
+ *    for more aggressive compression; its format is not given): OCP e2m1 codes, RNE, saturating
+ *    at +-6, with one fp32 scale per key, fp32(absmax / 6), the fp8 rule with 6 for 448; dims 2i
+ *    and 2i+1 in the low and high nibble of byte i; page = 64 x 64 code bytes, then 64 scales
+ *    (4352 B, 68 B per key).
  *  - fp8 x fp8 scoring ("The Crash That Changed Direction", Experiment: fp8 keys go into the
  *    product; the read path as a matrix product over heads): q of each (query, head) is quantised
  *    like a key (one fp32 scale = absmax / 448, e4m3 codes of q_i / scale) and the logit is
@@ -60,6 +65,7 @@
 #define OR_RATIO 4        /* tokens per compressed key ("c4") */
 #define OR_FP8 0
 #define OR_BF16 1
+#define OR_FP4 2          /* e2m1 codes, two per byte, then one fp32 scale per key */
 
 /* Planted-mistake switch used only by the test that checks the pins catch mistakes. 0 = none. */
 static int g_mutation = 0;
@@ -70,6 +76,7 @@ int oracle_get_mutation(void) { return g_mutation; }
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 int64_t oracle_page_bytes(int dtype) {
+    if (dtype == OR_FP4) return (int64_t)OR_PAGE * (OR_D / 2 + 4);
     return dtype == OR_FP8 ? (int64_t)OR_PAGE * (OR_D + 4) : (int64_t)OR_PAGE * OR_D * 2;
 }
 
@@ -111,6 +118,36 @@ uint8_t oracle_e4m3_encode(float v) {
         else c = (lo % 2 == 0) ? lo : hi;
     }
     return (uint8_t)(c | (sign << 7));
+}
+
+/* OCP FP4 e2m1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; no infinities or NaN; largest 6.
+ * Normal (E > 0): 2^(E-1) * (1 + M/2); subnormal (E = 0): M / 2.  Code bits: S.EE.M. */
+double oracle_e2m1_decode(uint8_t c) {
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e ? ldexp(1.0 + (double)m / 2.0, e - 1) : (double)m / 2.0;
+    return s ? -v : v;
+}
+
+/* Nearest e2m1 value, ties to the even code, saturating at +-6: the 8 magnitudes increase with
+ * the code, so the bracketing pair is found by a scan; distances are exact in fp64. */
+uint8_t oracle_e2m1_encode(float v) {
+    double a = fabs((double)v);
+    int sign = signbit(v) ? 1 : 0;
+    int c;
+    if (a >= 6.0) {
+        c = 7;
+    } else {
+        int lo = 0;
+        while (lo < 6 && oracle_e2m1_decode((uint8_t)(lo + 1)) <= a) lo++;
+        int hi = lo + 1;                      /* mag(lo) <= a < mag(hi) */
+        double dlo = a - oracle_e2m1_decode((uint8_t)lo);
+        double dhi = oracle_e2m1_decode((uint8_t)hi) - a;
+        if (dlo < dhi) c = lo;
+        else if (dhi < dlo) c = hi;
+        else if (g_mutation == 19) c = hi;                /* planted: ties away from zero */
+        else c = (lo % 2 == 0) ? lo : hi;
+    }
+    return (uint8_t)(c | (sign << 3));
 }
 
 static double bf16_bits_value(uint16_t h) {
@@ -240,6 +277,22 @@ int64_t oracle_store_keys(const float* x, const float* gamma, float eps, const i
                 pg[slot * 256 + 2 * i] = (uint8_t)(h & 0xFF);
                 pg[slot * 256 + 2 * i + 1] = (uint8_t)(h >> 8);
             }
+        } else if (dtype == OR_FP4) {
+            /* fp4: scale = fp32(absmax / 6), codes e2m1 of fp32(k32 / scale); dims 2i and 2i+1
+             * in the low and high nibble of byte i; codes at slot * 64, scales after the 4096 */
+            double amax = 0.0;
+            for (int i = 0; i < OR_D; i++) amax = fmax(amax, fabs((double)k32[i]));
+            float scale = (float)(amax / 6.0);
+            for (int i = 0; i < OR_D / 2; i++) {
+                uint8_t c0 = 0, c1 = 0;
+                if (scale > 0.0f) {
+                    c0 = oracle_e2m1_encode((float)((double)k32[2 * i] / (double)scale));
+                    c1 = oracle_e2m1_encode((float)((double)k32[2 * i + 1] / (double)scale));
+                }
+                pg[slot * (OR_D / 2) + i] = (g_mutation == 20) ? (uint8_t)(c1 | (c0 << 4))
+                                                               : (uint8_t)(c0 | (c1 << 4));
+            }
+            memcpy(pg + OR_PAGE * (OR_D / 2) + slot * 4, &scale, 4);
         } else {
             double amax = 0.0;
             for (int i = 0; i < OR_D; i++) amax = fmax(amax, fabs((double)k32[i]));
@@ -273,6 +326,14 @@ static int fetch_key(const uint8_t* pool, int dtype, int64_t n_pages_pool, const
         for (int i = 0; i < OR_D; i++) {
             uint16_t h = (uint16_t)(pg[slot * 256 + 2 * i] | (pg[slot * 256 + 2 * i + 1] << 8));
             k[i] = bf16_bits_value(h);
+        }
+    } else if (dtype == OR_FP4) {
+        float scale;
+        memcpy(&scale, pg + OR_PAGE * (OR_D / 2) + slot * 4, 4);
+        for (int i = 0; i < OR_D / 2; i++) {
+            uint8_t byte = pg[slot * (OR_D / 2) + i];
+            k[2 * i] = oracle_e2m1_decode(byte & 15) * (double)scale;
+            k[2 * i + 1] = oracle_e2m1_decode(byte >> 4) * (double)scale;
         }
     } else {
         float scale;

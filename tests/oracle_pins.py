@@ -603,4 +603,93 @@ def pin_logits_fp8q_close_to_bf16_q():
     assert np.all(np.abs(a - b)[fin] <= bound[fin])
 
 
+# ---- fp4 keys (e2m1 codes, one fp32 scale per key) -------------------------------------------
+
+FP4 = oracle.FP4
+# The FP4 E2M1 magnitudes as tabulated in the OCP Microscaling Formats (MX) specification v1.0,
+# section 5.3.3 (codes 0..7; bit 3 is the sign).
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _e2m1_brute(v: np.ndarray) -> np.ndarray:
+    """Nearest magnitude by exhaustive distance, ties to the even code, saturating at 6."""
+    v = np.asarray(v, np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[:, None] - _E2M1_MAG[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    even = cand & (np.arange(8)[None, :] % 2 == 0)
+    code = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    return (code | (np.signbit(v).astype(np.int64) << 3)).astype(np.uint8)
+
+
+def pin_e2m1_table():
+    got = oracle.e2m1_decode(np.arange(16))
+    assert np.array_equal(got[:8], _E2M1_MAG)
+    assert np.array_equal(got[8:], -_E2M1_MAG)
+
+
+def pin_e2m1_encode_brute_force():
+    mids = (_E2M1_MAG[:-1] + _E2M1_MAG[1:]) / 2
+    m32 = mids.astype(np.float32)
+    v = np.concatenate([_E2M1_MAG, mids, np.nextafter(m32, np.float32(9)),
+                        np.nextafter(m32, np.float32(0)), [6.5, 7.0, 100.0, 1e-30],
+                        np.linspace(-8, 8, 4001)]).astype(np.float32)
+    v = np.concatenate([v, -v])
+    assert np.array_equal(oracle.e2m1_encode(v), _e2m1_brute(v))
+
+
+def pin_fp4_store_bytes():
+    """The stored bytes of fp4 keys, rebuilt in numpy from the canonical keys: scale = numpy's
+    fp32 division absmax / 6, codes by the brute-force encoder, low nibble = even dim."""
+    r = _rng(50)
+    x = (r.standard_normal((70, D)) * r.choice([1e-3, 1.0, 40.0], (70, 1))).astype(np.float32)
+    x[9] = 0.0
+    s = np.arange(70, dtype=np.int32) * 2
+    pool, k32, pt = _store_rows(x, s, dtype=FP4)
+    pb = oracle.page_bytes(FP4)
+    assert pb == 64 * 68
+    for n, sn in enumerate(s):
+        base = pt[0, sn // PAGE] * pb
+        slot = sn % PAGE
+        amax = np.abs(k32[n]).max()
+        scale = np.float32(amax) / np.float32(6.0)
+        if scale > 0:
+            codes = _e2m1_brute((k32[n] / scale).astype(np.float32))
+        else:
+            codes = np.zeros(D, np.uint8)
+        want = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+        assert np.array_equal(pool[base + 64 * slot: base + 64 * slot + 64], want), n
+        got_s = pool[base + 4096 + 4 * slot: base + 4096 + 4 * slot + 4].view(np.float32)[0]
+        assert got_s == scale
+
+
+def pin_fp4_logits_vs_numpy():
+    r = _rng(51)
+    n_keys = 100
+    x = r.standard_normal((n_keys, D)).astype(np.float32)
+    pool, _, pt = _store_rows(x, np.arange(n_keys), dtype=FP4)
+    pb = oracle.page_bytes(FP4)
+    keys = np.zeros((n_keys, D))
+    for sn in range(n_keys):
+        base = pt[0, sn // PAGE] * pb
+        slot = sn % PAGE
+        by = pool[base + 64 * slot: base + 64 * slot + 64]
+        sc = float(pool[base + 4096 + 4 * slot: base + 4096 + 4 * slot + 4].view(np.float32)[0])
+        codes = np.empty(D, np.uint8)
+        codes[0::2], codes[1::2] = by & 15, by >> 4
+        keys[sn] = np.where(codes & 8, -1.0, 1.0) * _E2M1_MAG[codes & 7] * sc
+    q = _torch_bf16_bits(r.standard_normal((2, H, D)).astype(np.float32))
+    w = (r.standard_normal((2, H)) / 8).astype(np.float32)
+    seq_lens = np.array([4 * n_keys + 1], np.int32)
+    cu_q = np.array([0, 2], np.int32)
+    got, nv = oracle.logits(q, w, pool, FP4, pt, seq_lens, cu_q)
+    d = np.einsum("nhd,sd->nhs", _bf16_to_f64(q), keys)
+    want = np.einsum("nh,nhs->ns", w.astype(np.float64), np.maximum(d, 0.0))
+    for row in range(2):
+        m = int(nv[row])
+        assert np.allclose(got[row, :m], want[row, :m], rtol=1e-12, atol=1e-9)
+        assert np.all(np.isneginf(got[row, m:]))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
