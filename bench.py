@@ -41,7 +41,12 @@ WORKLOADS = {
     "decode-64x4k-22k-bf16": (2, 1),
     "decode-32x128k-fp8": (4, 0),
     "decode-32x128k-bf16": (4, 1),
+    "decode-32x128k-fp4": (4, 2),
+    "decode-64x4k-22k-fp4": (2, 2),
+    "prefill-22k-chunk8192-fp4": (3, 2),
 }
+KV_NAMES = {0: "fp8", 1: "bf16", 2: "fp4"}
+KEY_BYTES = {0: 132, 1: 256, 2: 68}     # stored bytes per key: codes + scale, or bf16 values
 DEFAULT = "prefill-22k-chunk8192-bf16"
 
 
@@ -158,8 +163,8 @@ def ceilings(args, torch) -> int:
 
 def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
     """S1 alone: store every key of the workload, --steps times; keys stored per second and the
-    store kernel's HBM roofline (per key: 512 B of activations and 8 B of indices read, 132 or
-    256 B written)."""
+    store kernel's HBM roofline (per key: 512 B of activations and 8 B of indices read, 132,
+    256 or 68 B written for fp8, bf16 or fp4)."""
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -179,7 +184,7 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    key_bytes = 132 if dtype == 0 else 256
+    key_bytes = KEY_BYTES[dtype]
     algo = wl.n_keys * (512 + 8 + key_bytes)
     achieved = algo / (kms * 1e-3) / 1e9
     print(json.dumps({
@@ -190,7 +195,7 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": args.workload + ("-rotated" if args.rotate else "") + "-store-population",
-                   "keys": wl.n_keys, "kv_dtype": "fp8" if dtype == 0 else "bf16"},
+                   "keys": wl.n_keys, "kv_dtype": KV_NAMES[dtype]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "store_keys_kernel", "kernel_ms": round(kms, 4)},
@@ -330,7 +335,7 @@ def main() -> int:
         ms = float(np.mean([a.elapsed_time(b) for a, b in step_evs]))
     pairs, nv = _pairs(wl)
     score_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    key_bytes = 132 if dtype == 0 else 256
+    key_bytes = KEY_BYTES[dtype]
     if cfg in (2, 4):   # decode: one pass over the visible keys of every sequence
         algo_bytes = float(nv.sum()) * key_bytes + wl.n_q * (64 * 128 * 2 + 64 * 4)
         achieved = algo_bytes / (score_ms * 1e-3) / 1e9
@@ -368,7 +373,7 @@ def main() -> int:
         "dtype": "fp8" if args.fp8q else "bf16",
         "data": "synthetic" + (", MALL flushed before every step" if args.cold else ""),
         "config": {"workload": name, "queries": wl.n_q, "keys": int(wl.max_keys),
-                   "visible_pairs": pairs, "k": wl.k, "kv_dtype": "fp8" if dtype == 0 else "bf16",
+                   "visible_pairs": pairs, "k": wl.k, "kv_dtype": KV_NAMES[dtype],
                    "keys_stored_in_step": int(stp.size), "heads": 64, "head_dim": 128,
                    "workspace_bytes": int(ws.numel())},
         "topk_queries_per_s": wl.n_q / (ms * 1e-3),

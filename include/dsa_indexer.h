@@ -54,7 +54,8 @@ typedef enum {
 
 typedef enum {
   IDX_KV_FP8_E4M3 = 0,   /* page = 64 x 128 e4m3fn codes, then 64 fp32 scales: 8448 B */
-  IDX_KV_BF16 = 1        /* page = 64 x 128 bf16: 16384 B */
+  IDX_KV_BF16 = 1,       /* page = 64 x 128 bf16: 16384 B */
+  IDX_KV_FP4_E2M1 = 2    /* page = 64 x 64 bytes of e2m1 code pairs, then 64 fp32 scales: 4352 B */
 } idx_kv_dtype;
 
 /* IDX_ABI_VERSION of the built library. */
@@ -63,10 +64,14 @@ int idx_abi_version(void);
 /* Static text for a status code (never NULL). */
 const char* idx_status_string(int status);
 
-/* Bytes of one cache page for `dtype` (8448 for fp8, 16384 for bf16), 0 for an unknown dtype.
- * Per key: 128 code bytes + a 4 B fp32 scale, or 256 bf16 bytes ("When the Fused Kernel Isn't
- * Enough", Input Knowledge Required).  Inside an fp8 page the 64 code rows come first (16 B
- * aligned for vector loads), then the 64 scales. */
+/* Bytes of one cache page for `dtype` (8448 for fp8, 16384 for bf16, 4352 for fp4), 0 for an
+ * unknown dtype.  Per key: 128 code bytes + a 4 B fp32 scale, or 256 bf16 bytes ("When the Fused
+ * Kernel Isn't Enough", Input Knowledge Required).  Inside an fp8 page the 64 code rows come
+ * first (16 B aligned for vector loads), then the 64 scales.  fp4 ("The Fused Kernel Decision",
+ * Input Knowledge: an fp4 variant of the indexer for more compression; the format is this
+ * library's choice): OCP e2m1 codes (sign, 2 exponent bits with bias 1, 1 mantissa bit; largest
+ * 6), dims 2i and 2i+1 in the low and high nibble of byte i, 64 B per key, then the 64 fp32
+ * scales; 68 B per key. */
 size_t idx_page_bytes(int dtype);
 
 /*
@@ -80,6 +85,8 @@ size_t idx_page_bytes(int dtype);
  *   k32 = y rounded once to fp32
  *   bf16: code_i = RNE bf16 of k32_i
  *   fp8:  scale = fp32(max_i |k32_i| / 448); code_i = e4m3fn RNE, saturating, of fp32(k32_i/scale);
+ *         an all-zero key stores scale 0 and codes 0
+ *   fp4:  scale = fp32(max_i |k32_i| / 6); code_i = e2m1 RNE, saturating, of fp32(k32_i/scale);
  *         an all-zero key stores scale 0 and codes 0
  * and writes the key to slot s % 64 of page page_table[b * max_pages + s / 64] of `kcache`.
  *

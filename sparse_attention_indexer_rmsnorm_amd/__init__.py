@@ -21,6 +21,7 @@ COMPRESS_RATIO = 4
 MAX_TOPK = 2048
 FP8 = 0      # IDX_KV_FP8_E4M3
 BF16 = 1     # IDX_KV_BF16
+FP4 = 2      # IDX_KV_FP4_E2M1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")

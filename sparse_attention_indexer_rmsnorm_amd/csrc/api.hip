@@ -47,7 +47,9 @@ RopeFreq rope_table() {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_EHIP; }
 
-bool dtype_ok(int dtype) { return dtype == IDX_KV_FP8_E4M3 || dtype == IDX_KV_BF16; }
+bool dtype_ok(int dtype) {
+  return dtype == IDX_KV_FP8_E4M3 || dtype == IDX_KV_BF16 || dtype == IDX_KV_FP4_E2M1;
+}
 
 // Workspace layout for a chunk of `rows` query rows:
 //   [row_nvis int32 x rows | pad][scores fp32 rows x cols | pad][selection candidates]
@@ -207,6 +209,7 @@ const char* idx_status_string(int status) {
 size_t idx_page_bytes(int dtype) {
   if (dtype == IDX_KV_FP8_E4M3) return static_cast<size_t>(kFp8PageBytes);
   if (dtype == IDX_KV_BF16) return static_cast<size_t>(kBf16PageBytes);
+  if (dtype == IDX_KV_FP4_E2M1) return static_cast<size_t>(kFp4PageBytes);
   return 0;
 }
 

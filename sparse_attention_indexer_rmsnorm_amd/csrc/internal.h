@@ -13,9 +13,12 @@ constexpr int kPageKeys = 64;        // keys per cache page
 constexpr int kRatio = 4;            // tokens per compressed key
 constexpr int kFp8 = 0;
 constexpr int kBf16 = 1;
+constexpr int kFp4 = 2;
 constexpr int64_t kFp8PageBytes = kPageKeys * (kHeadDim + 4);   // 8448: codes, then scales
 constexpr int64_t kBf16PageBytes = kPageKeys * kHeadDim * 2;    // 16384
 constexpr int kFp8ScaleOffset = kPageKeys * kHeadDim;           // 8192
+constexpr int64_t kFp4PageBytes = kPageKeys * (kHeadDim / 2 + 4);   // 4352: codes, then scales
+constexpr int kFp4ScaleOffset = kPageKeys * kHeadDim / 2;           // 4096
 
 // RoPE inverse frequencies, rounded to fp32 on the host and passed by value.
 struct RopeFreq {

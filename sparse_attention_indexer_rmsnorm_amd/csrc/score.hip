@@ -100,6 +100,10 @@ __device__ __forceinline__ float head_sum(const floatx16& acc0, const floatx16& 
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// fp4 (e2m1) keys: like fp8, widened exactly to bf16 (every e2m1 value is a bf16 value) with
+// v_cvt_scalef32_pk_bf16_fp4 at scale 1, which converts the two codes of one byte, low nibble
+// first.
+
 // Load a 32-key column block of B fragments for the split kernel: lane (m, g) reads key s (its
 // column) at dims 64g.. from the pool; zeros when the key is not to be read.
 template <int DT>
@@ -154,6 +158,37 @@ struct KeyBlock<kFp8> {
       kb[jj].p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
       kb[jj].p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
       kb[jj].p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    }
+  }
+};
+
+template <>
+struct KeyBlock<kFp4> {
+  u32x4 raw[2];
+  float scale;
+  __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int slot, int g, bool ok) {
+    if (ok) {
+      const uint8_t* pg = kcache + page * kFp4PageBytes;
+      const u32x4* src = reinterpret_cast<const u32x4*>(pg + slot * (kHeadDim / 2) + 32 * g);
+      raw[0] = src[0];
+      raw[1] = src[1];
+      scale = *reinterpret_cast<const float*>(pg + kFp4ScaleOffset + slot * 4);
+    } else {
+      raw[0] = u32x4{0u, 0u, 0u, 0u};
+      raw[1] = u32x4{0u, 0u, 0u, 0u};
+      scale = 0.0f;
+    }
+  }
+  // k-step jj uses code bytes 4jj..4jj+3 of this lane's 32 (dims 8jj..8jj+7): word jj.
+  __device__ __forceinline__ void frags(Frag (&kb)[8]) const {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const u32x4 r = raw[jj >> 2];
+      const uint32_t w = (jj & 3) == 0 ? r.x : (jj & 3) == 1 ? r.y : (jj & 3) == 2 ? r.z : r.w;
+      kb[jj].p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+      kb[jj].p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+      kb[jj].p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+      kb[jj].p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
     }
   }
 };
@@ -237,7 +272,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc1, 0, 0, 0);
     }
     float tot = head_sum(acc0, acc1, wv);
-    if constexpr (DT == kFp8) tot *= b0.scale;
+    if constexpr (DT != kBf16) tot *= b0.scale;
     const int32_t s = s0 + m;
     if (g == 0 && s < s_end) out_row[s] = ok0 ? tot : -INFINITY;
     b0 = b1; ok0 = ok1;
@@ -295,6 +330,31 @@ struct Stage<kFp8> {
       f1.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[3], 1.0f, true);
       reinterpret_cast<u32x4*>(dst)[2 * c] = f0.u;
       reinterpret_cast<u32x4*>(dst)[2 * c + 1] = f1.u;
+    }
+    if (qq == 0) *scale_slot = scale;
+  }
+};
+
+template <>
+struct Stage<kFp4> {
+  u32x4 v;
+  float scale;
+  __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int kk, int qq) {
+    const uint8_t* pg = kcache + page * kFp4PageBytes;
+    v = *reinterpret_cast<const u32x4*>(pg + kk * (kHeadDim / 2) + qq * 16);
+    scale = qq == 0 ? *reinterpret_cast<const float*>(pg + kFp4ScaleOffset + kk * 4) : 0.0f;
+  }
+  // 32 codes (16 B) -> 32 bf16 (64 B), natural dim order
+  __device__ __forceinline__ void commit(uint8_t* dst, float* scale_slot, int qq) const {
+    const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Frag f;
+      f.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wds[c], 1.0f, 0);
+      f.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wds[c], 1.0f, 1);
+      f.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wds[c], 1.0f, 2);
+      f.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wds[c], 1.0f, 3);
+      reinterpret_cast<u32x4*>(dst)[c] = f.u;
     }
     if (qq == 0) *scale_slot = scale;
   }
@@ -467,7 +527,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           tot[h] = head_sum(acc[h][0], acc[h][1], wv);
-          if constexpr (DT == kFp8) tot[h] *= tscale[buf][32 * h + m];
+          if constexpr (DT != kBf16) tot[h] *= tscale[buf][32 * h + m];
           tot[h] = ok_cur ? tot[h] : -INFINITY;
         }
         // both lane halves hold both halves' sums: lane (m, g) keeps key 32 g + m
@@ -980,8 +1040,12 @@ hipError_t launch_score_rows(const ScoreArgs& a, int dtype, hipStream_t stream) 
     return hipGetLastError();
   }
   const int64_t blocks = (a.n_rows + 3) / 4;
-  hipLaunchKernelGGL(score_rows_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                     stream, a);
+  if (dtype == kFp4)
+    hipLaunchKernelGGL(score_rows_kernel<kFp4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(score_rows_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
@@ -999,6 +1063,9 @@ hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
   const int64_t blocks = (waves + 3) / 4;
   if (dtype == kBf16)
     hipLaunchKernelGGL(score_kernel<kBf16>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, a);
+  else if (dtype == kFp4)
+    hipLaunchKernelGGL(score_kernel<kFp4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                        stream, a);
   else
     hipLaunchKernelGGL(score_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,

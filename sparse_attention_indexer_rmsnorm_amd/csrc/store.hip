@@ -51,6 +51,21 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
   return code | sign;
 }
 
+// Round a finite fp32 to OCP e2m1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; largest
+// 6), nearest-even, saturating to 6.  |v| >= 1: keep 1 mantissa bit with round-half-even, a carry
+// moving to the next binade by plain addition of the code; |v| < 1: the code is the integer
+// round-half-even of |v| * 2 (0, 0.5 or 1.0).  Without branches.
+__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
+  const float a = fabsf(v);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(a * 2.0f));
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t m = ua & 0x7FFFFFu;
+  const uint32_t r = (m + 0x1FFFFFu + ((m >> 22) & 1u)) >> 22;
+  const uint32_t nrm = min((((ua >> 23) - 126u) << 1) + r, 7u);
+  return (a < 1.0f ? sub : nrm) | sign;
+}
+
 template <typename T>
 __device__ __forceinline__ T half_wave_sum(T v) {
 #pragma unroll
@@ -160,6 +175,25 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
     uint8_t* dst = a.kcache + page * kBf16PageBytes + (s % kPageKeys) * (kHeadDim * 2);
     *reinterpret_cast<uint32_t*>(dst + 4 * j) = bf16_rne(k0) | (bf16_rne(k1) << 16);
     *reinterpret_cast<uint32_t*>(dst + 128 + 4 * j) = bf16_rne(k2) | (bf16_rne(k3) << 16);
+  } else if constexpr (DT == kFp4) {
+    float amax = fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3)));
+    amax = half_wave_max(amax);
+    if (!ok) return;
+    // as for fp8 below, with the largest e2m1 value 6 for 448
+    const float scale = static_cast<float>(static_cast<double>(amax) / 6.0);
+    uint32_t c01 = 0, c23 = 0;
+    if (scale > 0.0f) {
+      const double inv = 1.0 / static_cast<double>(scale);
+      c01 = e2m1_rne_sat(static_cast<float>(static_cast<double>(k0) * inv)) |
+            (e2m1_rne_sat(static_cast<float>(static_cast<double>(k1) * inv)) << 4);
+      c23 = e2m1_rne_sat(static_cast<float>(static_cast<double>(k2) * inv)) |
+            (e2m1_rne_sat(static_cast<float>(static_cast<double>(k3) * inv)) << 4);
+    }
+    uint8_t* pg = a.kcache + page * kFp4PageBytes;
+    uint8_t* dst = pg + (s % kPageKeys) * (kHeadDim / 2);
+    dst[j] = static_cast<uint8_t>(c01);         // dims 2j, 2j+1: low, high nibble of byte j
+    dst[32 + j] = static_cast<uint8_t>(c23);    // dims 64+2j, 65+2j
+    if (j == 0) *reinterpret_cast<float*>(pg + kFp4ScaleOffset + (s % kPageKeys) * 4) = scale;
   } else {
     float amax = fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3)));
     amax = half_wave_max(amax);
@@ -339,6 +373,10 @@ hipError_t launch_store(const StoreArgs& a, int dtype, bool hadamard, hipStream_
     hipLaunchKernelGGL((store_keys_kernel<kBf16, true>), grid, dim3(256), 0, stream, a);
   else if (dtype == kBf16)
     hipLaunchKernelGGL((store_keys_kernel<kBf16, false>), grid, dim3(256), 0, stream, a);
+  else if (dtype == kFp4 && hadamard)
+    hipLaunchKernelGGL((store_keys_kernel<kFp4, true>), grid, dim3(256), 0, stream, a);
+  else if (dtype == kFp4)
+    hipLaunchKernelGGL((store_keys_kernel<kFp4, false>), grid, dim3(256), 0, stream, a);
   else if (hadamard)
     hipLaunchKernelGGL((store_keys_kernel<kFp8, true>), grid, dim3(256), 0, stream, a);
   else

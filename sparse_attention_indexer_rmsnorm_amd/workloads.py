@@ -31,6 +31,7 @@ PAGE_KEYS = 64
 COMPRESS = 4
 FP8 = 0
 BF16 = 1
+FP4 = 2
 EPS = 1e-6
 
 T_X, T_GAMMA, T_Q, T_W, T_LENS, T_PERM, T_NEEDLE_POS, T_NEEDLE_NOISE, T_NEEDLE_Q = range(9)
@@ -41,8 +42,13 @@ def rng(seed: int, tensor_id: int) -> np.random.Generator:
 
 
 def page_bytes(dtype: int) -> int:
-    """Bytes of one cache page: 64 keys x (128 codes + 4 B scale) for fp8, 64 x 256 B for bf16."""
-    return PAGE_KEYS * (HEAD_DIM + 4) if dtype == FP8 else PAGE_KEYS * HEAD_DIM * 2
+    """Bytes of one cache page: 64 keys x (128 codes + 4 B scale) for fp8, 64 x 256 B for bf16,
+    64 keys x (64 B of packed 4-bit codes + 4 B scale) for fp4."""
+    if dtype == FP8:
+        return PAGE_KEYS * (HEAD_DIM + 4)
+    if dtype == FP4:
+        return PAGE_KEYS * (HEAD_DIM // 2 + 4)
+    return PAGE_KEYS * HEAD_DIM * 2
 
 
 @dataclass

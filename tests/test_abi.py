@@ -36,7 +36,9 @@ def test_version_and_strings(L):
 def test_page_bytes(L):
     assert L.idx_page_bytes(0) == 8448      # 64 keys x (128 codes + 4 B scale)
     assert L.idx_page_bytes(1) == 16384     # 64 keys x 256 B
-    assert L.idx_page_bytes(2) == 0
+    assert L.idx_page_bytes(2) == 4352      # 64 keys x (64 B of 4-bit codes + 4 B scale)
+    assert L.idx_page_bytes(3) == 0
+    assert L.idx_page_bytes(-1) == 0
 
 
 def test_workspace_sizes(L):
