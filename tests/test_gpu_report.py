@@ -19,7 +19,7 @@ from sparse_attention_indexer_rmsnorm_amd import workloads as W
 from tests.helpers import dev_inputs, gpu_store, workload
 
 pytestmark = pytest.mark.gpu
-FP8, BF16 = W.FP8, W.BF16
+FP8, BF16, FP4 = W.FP8, W.BF16, W.FP4
 REPORT = {}
 
 
@@ -50,7 +50,7 @@ def test_accuracy_report(oracle_mod, cfg):
                                 rows=rows, keys_ref=ref, ref_stride=wl.max_keys)
     top32 = _topk_sets(o32, nv, wl.k, oracle_mod)
     rt = torch.from_numpy(rows).cuda()
-    for dtype, name in ((BF16, "bf16"), (FP8, "fp8")):
+    for dtype, name in ((BF16, "bf16"), (FP8, "fp8"), (FP4, "fp4")):
         pool = gpu_store(ix, wl, dtype, d)
         dense = ix.logits_dense(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
                                 d["cu_q"], wl.max_keys)[rt].cpu().numpy()
@@ -81,4 +81,4 @@ def test_accuracy_report(oracle_mod, cfg):
         print("  " + json.dumps(out), flush=True)
         _write()
         assert np.mean(ov) >= 0.999
-        assert np.mean(ov32) >= (0.99 if dtype == BF16 else 0.95)
+        assert np.mean(ov32) >= {BF16: 0.99, FP8: 0.95, FP4: 0.5}[dtype]
