@@ -76,6 +76,9 @@ def lib():
         L.oracle_topk.argtypes = [_p, _i64, _i64, _p, _i32, _p, _p]
         L.oracle_plant_keys.restype = None
         L.oracle_plant_keys.argtypes = [_p, _p, _i64, _p, _p]
+        L.oracle_sparse_attn.argtypes = [_p, _p, _i64, _p, _i32, _i32, _p, _p, _i32, _i32,
+                                         ctypes.c_double, _p, _i64, _p, _p]
+        L.oracle_sparse_attn.restype = None
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_set_mutation.restype = None
@@ -265,6 +268,31 @@ def topk(scores, k, row_len=None):
     val = np.empty((n_rows, k), np.float64)
     lib().oracle_topk(_ptr(s), n_rows, stride, _ptr(rl), int(k), _ptr(idx), _ptr(val))
     return idx, val
+
+
+# ---- sparse attention over the selected keys ---------------------------------------------------
+
+def sparse_attn(q_bits, kv_bits, kv_slot, cu_q, idx, scale, rows=None):
+    """fp64 sparse attention of the given query rows over their listed keys.
+
+    q_bits [n_q, n_heads, 512] and kv_bits [n_slots, 512] are bf16 bit patterns, kv_slot
+    [n_seq, max_keys] int32 maps a sequence's key index to a kv row, idx [n_q, k] int32 lists
+    each row's keys (-1 = none).  Returns (out [n_rows, n_heads, 512], lse [n_rows, n_heads])."""
+    q_bits = _c(q_bits, np.uint16)
+    kv_bits = _c(kv_bits, np.uint16)
+    kv_slot = _c(kv_slot, np.int32)
+    idx = _c(idx, np.int32)
+    n_q, n_heads, dv = q_bits.shape
+    assert dv == 512 and kv_bits.shape[1] == 512 and idx.shape[0] == n_q
+    n_seq, max_keys = kv_slot.shape
+    rows = np.arange(n_q, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    out = np.empty((rows.size, n_heads, 512), np.float64)
+    lse = np.empty((rows.size, n_heads), np.float64)
+    lib().oracle_sparse_attn(_ptr(q_bits), _ptr(kv_bits), kv_bits.shape[0], _ptr(kv_slot), n_seq,
+                             max_keys, _ptr(_c(cu_q, np.int32)), _ptr(idx), n_heads,
+                             idx.shape[1], float(scale), _ptr(rows), rows.size, _ptr(out),
+                             _ptr(lse))
+    return out, lse
 
 
 # ---- needle helpers (harness) -----------------------------------------------------------------

@@ -47,6 +47,14 @@
  *    at +-6, with one fp32 scale per key, fp32(absmax / 6), the fp8 rule with 6 for 448; dims 2i
  *    and 2i+1 in the low and high nibble of byte i; page = 64 x 64 code bytes, then 64 scales
  *    (4352 B, 68 B per key).
+ *  - sparse attention over the selected keys ("When the Fused Kernel Isn't Enough", Input
+ *    Knowledge: the sparse attention attends to the top-K entries the indexer picks, and the main
+ *    KV cache is bf16 with head_dim 512; "The Fused Kernel Decision", Message: that cache is
+ *    unpaged, [num_slots, 512] bf16, one slot per entry): for query row i of sequence b and head
+ *    h, each listed entry j with 0 <= idx[i][j] < max_keys whose slot kv_slot[b][idx] lies in
+ *    [0, n_slots) contributes the 512-dim latent v_j = kv[slot]; logit_j = scale * q[i][h] . v_j,
+ *    o[i][h] = sum_j softmax(logit)_j * v_j (the latent is key and value, shared by all heads),
+ *    lse[i][h] = log sum_j exp(logit_j).  No listed entry: o = 0, lse = -inf.
  *  - fp8 x fp8 scoring ("The Crash That Changed Direction", Experiment: fp8 keys go into the
  *    product; the read path as a matrix product over heads): q of each (query, head) is quantised
  *    like a key (one fp32 scale = absmax / 448, e4m3 codes of q_i / scale) and the logit is
@@ -66,6 +74,7 @@
 #define OR_FP8 0
 #define OR_BF16 1
 #define OR_FP4 2          /* e2m1 codes, two per byte, then one fp32 scale per key */
+#define OR_DV 512         /* main-KV latent dim of the sparse attention */
 
 /* Planted-mistake switch used only by the test that checks the pins catch mistakes. 0 = none. */
 static int g_mutation = 0;
@@ -539,5 +548,68 @@ void oracle_plant_keys(const double* kstar, const int32_t* key_idx, int64_t n, c
             y[i1] = -a * sn + b * c;
         }
         for (int i = 0; i < OR_D; i++) x_out[r * OR_D + i] = (float)(y[i] / (double)gamma[i]);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Sparse attention over the selected keys, for the query rows listed in rows[0..n_rows).
+ * q: [n_q][n_heads][512] bf16 bits; kv: [n_slots][512] bf16 bits; kv_slot: [n_seq][max_keys];
+ * idx: [n_q][k] logical key indices (-1 = none).  out: [n_rows][n_heads][512], lse:
+ * [n_rows][n_heads], both fp64.  Every product of two bf16 values is exact in fp64; the softmax
+ * subtracts the largest logit before exponentiating.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_sparse_attn(const uint16_t* q, const uint16_t* kv, int64_t n_slots,
+                        const int32_t* kv_slot, int32_t n_seq, int32_t max_keys,
+                        const int32_t* cu_q, const int32_t* idx, int32_t n_heads, int32_t k,
+                        double scale, const int64_t* rows, int64_t n_rows, double* out,
+                        double* lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; r++) {
+        int64_t i = rows[r];
+        int32_t b = seq_of_row(cu_q, n_seq, i);
+        /* the rows of kv this query attends to, in list order */
+        int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)(k > 0 ? k : 1));
+        int n = 0;
+        for (int32_t j = 0; j < k; j++) {
+            int32_t s = idx[i * k + j];
+            if (g_mutation == 22 && s < 0) s = 0;                 /* planted: -1 read as key 0 */
+            if (b < 0 || s < 0 || s >= max_keys) continue;
+            int64_t sl = kv_slot[(int64_t)b * max_keys + s];
+            if (g_mutation == 23) sl = kv_slot[(int64_t)b * max_keys + (s + 1) % max_keys];
+            if (sl < 0 || sl >= n_slots) continue;
+            slot[n++] = sl;
+        }
+        double* logit = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        for (int32_t h = 0; h < n_heads; h++) {
+            const uint16_t* qh = q + (i * n_heads + h) * OR_DV;
+            double* o = out + (r * n_heads + h) * OR_DV;
+            for (int d = 0; d < OR_DV; d++) o[d] = 0.0;
+            if (n == 0) {
+                lse[r * n_heads + h] = -INFINITY;
+                continue;
+            }
+            double mx = -INFINITY;
+            for (int j = 0; j < n; j++) {
+                const uint16_t* v = kv + slot[j] * OR_DV;
+                double dot = 0.0;
+                for (int d = 0; d < OR_DV; d++) {
+                    double qv = bf16_bits_value(qh[d]);
+                    if (g_mutation == 25) qv = bf16_bits_value(q[(i * OR_DV + d) * n_heads + h]);
+                    dot += qv * bf16_bits_value(v[d]);
+                }
+                logit[j] = (g_mutation == 21) ? dot : scale * dot;  /* planted: scale dropped */
+                if (logit[j] > mx) mx = logit[j];
+            }
+            double sum = 0.0;
+            for (int j = 0; j < n; j++) sum += exp(logit[j] - mx);
+            for (int j = 0; j < n; j++) {
+                double p = exp(logit[j] - mx) / sum;
+                const uint16_t* v = kv + slot[j] * OR_DV;
+                for (int d = 0; d < OR_DV; d++) o[d] += p * bf16_bits_value(v[d]);
+            }
+            lse[r * n_heads + h] = (g_mutation == 24) ? log(sum) : mx + log(sum);
+        }
+        free(logit);
+        free(slot);
     }
 }

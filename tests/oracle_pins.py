@@ -692,4 +692,135 @@ def pin_fp4_logits_vs_numpy():
         assert np.all(np.isneginf(got[row, m:]))
 
 
+# ---- sparse attention over the selected keys --------------------------------------------------
+
+def _attn_case(seed, n_seq=2, max_keys=9, n_slots=20, q_lens=(3, 2), n_heads=3, k=6):
+    """Small random attention inputs: bf16 q and kv, a permuted slot table with a hole, lists of
+    k entries per row drawn from the sequence's keys."""
+    r = _rng(seed)
+    n_q = int(sum(q_lens))
+    q = _torch_bf16_bits(r.standard_normal((n_q, n_heads, 512)).astype(np.float32))
+    kv = _torch_bf16_bits(r.standard_normal((n_slots, 512)).astype(np.float32))
+    kv_slot = r.permutation(n_slots)[:n_seq * max_keys].astype(np.int32).reshape(n_seq, max_keys)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    idx = np.stack([r.choice(max_keys, k, replace=False) for _ in range(n_q)]).astype(np.int32)
+    return q, kv, kv_slot, cu_q, idx
+
+
+def _attn_numpy(q, kv, kv_slot, cu_q, idx, scale):
+    """The same attention from scipy's softmax and logsumexp over numpy's matrix products."""
+    from scipy.special import logsumexp, softmax  # noqa: PLC0415
+    n_q, n_heads, _ = q.shape
+    out = np.zeros((n_q, n_heads, 512))
+    lse = np.full((n_q, n_heads), -np.inf)
+    qd, kvd = _bf16_to_f64(q), _bf16_to_f64(kv)
+    for i in range(n_q):
+        b = int(np.searchsorted(cu_q, i, side="right") - 1)
+        sl = [kv_slot[b, s] for s in idx[i] if 0 <= s < kv_slot.shape[1]]
+        sl = [x for x in sl if 0 <= x < kv.shape[0]]
+        if not sl:
+            continue
+        v = kvd[sl]                                    # [n, 512]
+        lg = scale * (qd[i] @ v.T)                     # [heads, n]
+        out[i] = softmax(lg, axis=1) @ v
+        lse[i] = logsumexp(lg, axis=1)
+    return out, lse
+
+
+def pin_attn_vs_scipy():
+    """Two sequences, permuted slots, distinct lists: equal to scipy's softmax of numpy's
+    products, times the same rows."""
+    q, kv, kv_slot, cu_q, idx = _attn_case(1)
+    scale = 512 ** -0.5
+    o, l = oracle.sparse_attn(q, kv, kv_slot, cu_q, idx, scale)
+    ro, rl = _attn_numpy(q, kv, kv_slot, cu_q, idx, scale)
+    assert np.allclose(o, ro, rtol=1e-12, atol=1e-13)
+    assert np.allclose(l, rl, rtol=1e-12, atol=1e-13)
+
+
+def pin_attn_single_key():
+    """One listed key: the weight is exactly 1, so the output is that latent exactly and the
+    log-sum-exp is its scaled logit."""
+    q, kv, kv_slot, cu_q, idx = _attn_case(2)
+    idx[:, 1:] = -1
+    scale = 0.37
+    o, l = oracle.sparse_attn(q, kv, kv_slot, cu_q, idx, scale)
+    for i in range(q.shape[0]):
+        b = int(np.searchsorted(cu_q, i, side="right") - 1)
+        v = _bf16_to_f64(kv[kv_slot[b, idx[i, 0]]])
+        assert np.array_equal(o[i], np.broadcast_to(v, o[i].shape))
+        assert np.allclose(l[i], scale * (_bf16_to_f64(q[i]) @ v), rtol=1e-13, atol=1e-13)
+
+
+def pin_attn_uniform_weights():
+    """q = 0: every logit is 0, the output is the plain mean of the listed latents and the
+    log-sum-exp is log n."""
+    q, kv, kv_slot, cu_q, idx = _attn_case(3)
+    q[:] = 0
+    o, l = oracle.sparse_attn(q, kv, kv_slot, cu_q, idx, 1.0)
+    for i in range(q.shape[0]):
+        b = int(np.searchsorted(cu_q, i, side="right") - 1)
+        mean = _bf16_to_f64(kv[kv_slot[b, idx[i]]]).mean(axis=0)
+        assert np.allclose(o[i], mean, rtol=1e-13, atol=1e-14)
+        assert np.allclose(l[i], np.log(idx.shape[1]), rtol=1e-14)
+
+
+def pin_attn_list_order_and_skipped_entries():
+    """The list is a set of terms: shuffling it changes nothing, and entries that are -1, beyond
+    max_keys, or whose slot is -1 or beyond the kv rows add nothing."""
+    q, kv, kv_slot, cu_q, idx = _attn_case(4, k=5)
+    kv_slot = kv_slot.copy()
+    kv_slot[:, 7] = -1
+    kv_slot[:, 8] = kv.shape[0] + 3
+    base = np.where(np.isin(idx, [7, 8]), 0, idx)      # lists without the bad keys
+    o0, l0 = oracle.sparse_attn(q, kv, kv_slot, cu_q, base, 0.5)
+    r = _rng(40)
+    junk = np.array([-1, 9, 12, -5, 7, 8], np.int32)
+    ext = np.concatenate([base, np.tile(junk, (base.shape[0], 1))], axis=1)
+    ext = np.stack([r.permutation(row) for row in ext]).astype(np.int32)
+    o1, l1 = oracle.sparse_attn(q, kv, kv_slot, cu_q, ext, 0.5)
+    assert np.allclose(o0, o1, rtol=1e-12, atol=1e-13)
+    assert np.allclose(l0, l1, rtol=1e-12, atol=1e-13)
+
+
+def pin_attn_duplicate_entry_counts_twice():
+    """A key listed twice gets twice the weight: with logits a, a, b the weights are
+    2e^a / (2e^a + e^b) and e^b / (2e^a + e^b)."""
+    q, kv, kv_slot, cu_q, idx = _attn_case(5, k=3)
+    idx[:, 1] = idx[:, 0]
+    scale = 0.11
+    o, _ = oracle.sparse_attn(q, kv, kv_slot, cu_q, idx, scale)
+    for i in range(q.shape[0]):
+        b = int(np.searchsorted(cu_q, i, side="right") - 1)
+        va = _bf16_to_f64(kv[kv_slot[b, idx[i, 0]]])
+        vb = _bf16_to_f64(kv[kv_slot[b, idx[i, 2]]])
+        for h in range(q.shape[1]):
+            qh = _bf16_to_f64(q[i, h])
+            a, c = scale * (qh @ va), scale * (qh @ vb)
+            wa = 2 / (2 + np.exp(c - a))
+            assert np.allclose(o[i, h], wa * va + (1 - wa) * vb, rtol=1e-12, atol=1e-13)
+
+
+def pin_attn_hardmax_limit():
+    """A huge scale turns the softmax into the argmax: the output is the latent with the largest
+    q . v (numpy's argmax of numpy's products)."""
+    q, kv, kv_slot, cu_q, idx = _attn_case(6)
+    o, _ = oracle.sparse_attn(q, kv, kv_slot, cu_q, idx, 1e6)
+    for i in range(q.shape[0]):
+        b = int(np.searchsorted(cu_q, i, side="right") - 1)
+        v = _bf16_to_f64(kv[kv_slot[b, idx[i]]])
+        for h in range(q.shape[1]):
+            best = int(np.argmax(v @ _bf16_to_f64(q[i, h])))
+            assert np.array_equal(o[i, h], v[best])
+
+
+def pin_attn_empty_list():
+    """No valid entry: output 0 and log-sum-exp -inf."""
+    q, kv, kv_slot, cu_q, idx = _attn_case(7)
+    idx[:] = -1
+    idx[0, 0] = 99                                       # beyond max_keys
+    o, l = oracle.sparse_attn(q, kv, kv_slot, cu_q, idx, 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -6,13 +6,15 @@ rotation pairs shifted by one dim, RMS over half the dims, gamma dropped, ReLU d
 from zero, the FNUZ maximum 240 instead of 448, bf16 truncation, visibility off by one, fp8 scale
 dropped on dequantisation, a Hadamard butterfly stage skipped, the butterfly difference negated,
 the Hadamard scale 1/128 instead of 2^-3.5, q quantised without dividing by its scale, the q
-scale dropped from the fp8 x fp8 logit, e2m1 ties away from zero, fp4 nibbles swapped.
+scale dropped from the fp8 x fp8 logit, e2m1 ties away from zero, fp4 nibbles swapped, the
+attention's softmax scale dropped, a -1 list entry read as key 0, the kv slot of the next key
+taken, the log-sum-exp without its maximum, q read as [512][heads].
 """
 import pytest
 
 from tests.oracle_pins import ALL_PINS
 
-MUTATIONS = list(range(1, 21))
+MUTATIONS = list(range(1, 26))
 
 
 @pytest.mark.parametrize("m", MUTATIONS)
