@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "score_rows_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "score_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "score_rows_fp8q_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
+    "sparse_attn_kernel": ["csrc/attn.hip", "csrc/attn.h", "build.py"],
 }
 
 
@@ -203,6 +204,83 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
     return 0
 
 
+def attn_bench(args, cfg, ix, torch, W) -> int:
+    """The sparse attention over the selected keys alone, on a workload's rows: q of
+    --attn-heads heads x 512 dims (bf16) against each row's listed 512-dim bf16 latents (a random
+    subset of min(k, visible) keys per row, workloads.attn_inputs).  Roofline: bf16 MFMA for
+    prefill-shaped batches (4 flops per (row, head, listed key, dim): q.v and p.v), HBM for
+    decode-shaped ones (1024 B per listed latent, plus q and the output)."""
+    wl = W.CONFIGS[cfg]() if cfg != 4 else W.cfg4(needles=False)
+    a = W.attn_inputs(wl, n_heads=args.attn_heads)
+    dev = torch.device("cuda:0")
+    q, kv, kv_slot, idx = a.torch_inputs(dev)
+    cu_q = torch.from_numpy(wl.cu_q).to(dev)
+    n_list = int((a.idx >= 0).sum())
+    H, k = a.n_heads, a.idx.shape[1]
+    out = torch.empty((wl.n_q, H, 512), dtype=torch.bfloat16, device=dev)
+    ws_bytes = ix.sparse_attn_workspace_size(wl.n_q, H, k)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+
+    def call():
+        ix.sparse_attn(q, kv, kv_slot, cu_q, idx, a.scale, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    decode = cfg in (2, 4)
+    flops = 4.0 * H * 512 * n_list
+    algo_bytes = n_list * 1024.0 + q.numel() * 2 + out.numel() * 2 + wl.n_q * H * 4 + idx.numel() * 4
+    if decode:
+        ach = algo_bytes / (kms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        ach = flops / (kms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    name = wl.name.rsplit("-", 1)[0] if wl.name.endswith(("-fp8", "-bf16")) else wl.name
+    name = f"{name}-attn-h{H}"
+    roof["traffic"] = committed_traffic("sparse_attn_kernel", name)
+    roof["kernel"] = "sparse_attn_kernel" + (" + sparse_attn_merge_kernel" if ws_bytes else "")
+    roof["kernel_ms"] = round(kms, 4)
+    line = {
+        "metric": "sparse attention listed keys/s ((query, listed key) pairs, all heads)",
+        "value": n_list / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "queries": wl.n_q, "heads": H, "latent_dim": 512, "k": k,
+                   "listed": n_list, "workspace_bytes": ws_bytes},
+        "roofline": roof, "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle  # noqa: PLC0415  (test infrastructure; only this leg uses it)
+        oracle.lib()
+        stride = max(1, wl.n_q // min(wl.n_q, args.cpu_sample_rows // 4))
+        rows = np.arange(0, wl.n_q, stride, dtype=np.int64)
+        c0 = time.perf_counter()
+        oracle.sparse_attn(a.q_bits, a.kv_bits, a.kv_slot, wl.cu_q, a.idx, a.scale, rows=rows)
+        secs = time.perf_counter() - c0
+        n_s = int((a.idx[rows] >= 0).sum())
+        line["cpu_baseline"] = {"value": n_s / secs, "unit": "keys/s", "cores": oracle.num_threads(),
+                                "kind": "oracle",
+                                "sample": f"{rows.size} of {wl.n_q} rows (every {stride}th), "
+                                          f"{n_s} listed keys, {secs:.2f} s of wall time"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +307,10 @@ def main() -> int:
                     help="only measure what this GPU delivers to plain library code: torch's bf16 "
                          "GEMM at 8192^3 (TFLOP/s) and torch's read of a 512 MiB tensor (GB/s), "
                          "the latter from HBM after a read of another 512 MiB")
+    ap.add_argument("--attn", action="store_true",
+                    help="only time the sparse attention over the selected keys on the "
+                         "workload's rows (the consumer of the top-k lists)")
+    ap.add_argument("--attn-heads", type=int, default=64, choices=(32, 64, 128))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (the "
                          "reference for scaling HBM byte counters); prints its bytes per copy")
@@ -258,6 +340,8 @@ def main() -> int:
 
     ix.lib()
     cfg, dtype = WORKLOADS[args.workload]
+    if args.attn:
+        return attn_bench(args, cfg, ix, torch, W)
     if args.fp8q and (dtype != 0 or args.rotate):
         print("--fp8q needs an fp8 workload and no --rotate", file=sys.stderr)
         return 2

@@ -259,6 +259,45 @@ int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const
                   int32_t k, int32_t* out_idx, float* out_val, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * Sparse attention over the selected keys: the consumer of the top-k lists ("When the Fused Kernel
+ * Isn't Enough", Input Knowledge: the sparse attention attends to the top-K entries the indexer
+ * picks; the main KV cache is bf16 with head_dim 512; "The Fused Kernel Decision", Message: that
+ * cache is unpaged, [num_slots, 512] bf16).  The 512-dim latent of an entry is its key and its
+ * value for every query head (multi-query attention on the shared latent).  For query row i of
+ * sequence b (cu_q[b] <= i < cu_q[b+1]) and head h, the listed entries j < k with
+ * 0 <= idx[i,j] < max_keys and slot = kv_slot[b, idx[i,j]] in [0, n_slots) give latents v_j and
+ *   logit_j = softmax_scale * sum_d q[i,h,d] * v_j[d]
+ *   out[i,h,:] = sum_j softmax_j(logit) * v_j        (bf16, round to nearest even)
+ *   out_lse[i,h] = log(sum_j exp(logit_j))           (natural log; optional)
+ * A list entry counts once per appearance.  A row with no valid entry gets out = 0 and
+ * out_lse = -inf.  Scores accumulate in fp32 from exact bf16 products; the softmax weights are
+ * rounded to bf16 for the weighted sum and normalised by the sum of the rounded weights.
+ *
+ * q        device bf16 [n_q, n_heads, 512], 16-byte aligned
+ * kv       device bf16 [n_slots, 512], 16-byte aligned
+ * kv_slot  device int32 [n_seq, max_keys]: the kv row of key s of sequence b (out of range: the
+ *          entry is skipped)
+ * cu_q     device int32 [n_seq + 1], non-decreasing; rows outside [cu_q[0], cu_q[n_seq]) attend
+ *          to nothing
+ * idx      device int32 [n_q, k], e.g. the output of idx_logits_topk (its -1 padding is skipped)
+ * out      device bf16 [n_q, n_heads, 512], 16-byte aligned; out_lse device fp32 [n_q, n_heads]
+ *          or NULL
+ * workspace device, at least idx_sparse_attn_workspace_size(n_q, n_heads, k) bytes (0, and
+ *          workspace may be NULL, for batches of 256 rows or more)
+ * n_heads is 32, 64 or 128.
+ * Errors: IDX_EINVAL (null pointer, misaligned q / kv / out, n_q < 0, n_seq < 1, max_keys < 1,
+ * n_slots < 0, k < 1, softmax_scale not finite and positive), IDX_EUNSUPPORTED (n_heads),
+ * IDX_EWORKSPACE,
+ * IDX_EHIP.
+ */
+#define IDX_LATENT_DIM 512
+size_t idx_sparse_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t k);
+int idx_sparse_attn(const void* q, const void* kv, int64_t n_slots, const int32_t* kv_slot,
+                    int32_t n_seq, int32_t max_keys, const int32_t* cu_q, const int32_t* idx,
+                    int64_t n_q, int32_t n_heads, int32_t k, float softmax_scale, void* out,
+                    float* out_lse, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,10 @@ SIGNATURES = [
      [_p, _p, _p, _p, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _p, _i32, _p]),
     ("idx_topk_rows_workspace_size", _sz, [_i64, _i64, _i32]),
     ("idx_topk_rows", ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _p, _p, _sz, _p]),
+    ("idx_sparse_attn_workspace_size", _sz, [_i64, _i32, _i32]),
+    ("idx_sparse_attn", ctypes.c_int,
+     [_p, _p, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _i32, ctypes.c_float, _p, _p, _p, _sz,
+      _p]),
 ]
 
 
@@ -314,3 +318,47 @@ def topk_rows(scores: torch.Tensor, k: int, row_len: Optional[torch.Tensor] = No
                              ws_bytes, _stream(stream))
     _check(st, "idx_topk_rows")
     return out_idx, out_val
+
+
+LATENT_DIM = 512
+
+
+def sparse_attn_workspace_size(n_q: int, n_heads: int, k: int) -> int:
+    return int(lib().idx_sparse_attn_workspace_size(int(n_q), int(n_heads), int(k)))
+
+
+def sparse_attn(q: torch.Tensor, kv: torch.Tensor, kv_slot: torch.Tensor, cu_q: torch.Tensor,
+                idx: torch.Tensor, softmax_scale: float, *, want_lse: bool = True,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None):
+    """Sparse attention of q [n_q, n_heads, 512] bf16 over the latents kv [n_slots, 512] bf16 of
+    the keys listed in idx [n_q, k] int32 (kv_slot [n_seq, max_keys] int32 maps a sequence's key
+    to its kv row).  Returns (out [n_q, n_heads, 512] bf16, lse [n_q, n_heads] fp32 or None)."""
+    if q.dim() != 3 or q.shape[2] != LATENT_DIM:
+        raise ValueError("q must be [n_q, n_heads, 512]")
+    if kv.dim() != 2 or kv.shape[1] != LATENT_DIM:
+        raise ValueError("kv must be [n_slots, 512]")
+    if idx.dim() != 2 or idx.shape[0] != q.shape[0]:
+        raise ValueError("idx must be [n_q, k]")
+    if kv_slot.dim() != 2:
+        raise ValueError("kv_slot must be [n_seq, max_keys]")
+    n_q, n_heads, _ = q.shape
+    n_seq, max_keys = kv_slot.shape
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty((n_q, n_heads, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((n_q, n_heads), dtype=torch.float32, device=q.device) if want_lse else None
+    ws_bytes = sparse_attn_workspace_size(n_q, n_heads, k)
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lib().idx_sparse_attn(_dev(q, "q", torch.bfloat16), _dev(kv, "kv", torch.bfloat16),
+                               kv.shape[0], _dev(kv_slot, "kv_slot", torch.int32), n_seq, max_keys,
+                               _dev(cu_q, "cu_q", torch.int32, n_seq + 1),
+                               _dev(idx, "idx", torch.int32), n_q, n_heads, k,
+                               float(softmax_scale),
+                               _dev(out, "out", torch.bfloat16, n_q * n_heads * LATENT_DIM),
+                               _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
+                               ws_bytes if workspace is None else workspace.numel(),
+                               _stream(stream))
+    _check(st, "idx_sparse_attn")
+    return out, lse

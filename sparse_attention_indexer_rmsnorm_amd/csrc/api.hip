@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "../../include/dsa_indexer.h"
+#include "attn.h"
 #include "internal.h"
 
 namespace {
@@ -402,6 +403,49 @@ int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const
   if (need > 0 && (!workspace || workspace_bytes < need)) return IDX_EWORKSPACE;
   return hip_status(run_topk(scores, row_stride, row_len, n_rows, k, out_idx, out_val, workspace,
                              static_cast<hipStream_t>(stream)));
+}
+
+size_t idx_sparse_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t k) {
+  if (n_q <= 0 || k < 1 || (n_heads != 32 && n_heads != 64 && n_heads != 128)) return 0;
+  return attn_workspace_bytes(n_q, n_heads, k);
+}
+
+int idx_sparse_attn(const void* q, const void* kv, int64_t n_slots, const int32_t* kv_slot,
+                    int32_t n_seq, int32_t max_keys, const int32_t* cu_q, const int32_t* idx,
+                    int64_t n_q, int32_t n_heads, int32_t k, float softmax_scale, void* out,
+                    float* out_lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_q < 0 || n_seq < 1 || max_keys < 1 || n_slots < 0 || k < 1) return IDX_EINVAL;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return IDX_EINVAL;
+  if (n_heads != 32 && n_heads != 64 && n_heads != 128) return IDX_EUNSUPPORTED;
+  if (n_q == 0) return IDX_OK;
+  if (!q || !kv || !kv_slot || !cu_q || !idx || !out) return IDX_EINVAL;
+  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (misaligned(q) || misaligned(kv) || misaligned(out)) return IDX_EINVAL;
+  AttnArgs a{};
+  attn_plan(n_q, k, &a.n_split, &a.split_keys);
+  if (n_q * a.n_split * 2 > INT32_MAX || n_q * n_heads > INT64_C(4) * INT32_MAX) return IDX_EINVAL;
+  const size_t need = attn_workspace_bytes(n_q, n_heads, k);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return IDX_EWORKSPACE;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.n_slots = n_slots;
+  a.kv_slot = kv_slot;
+  a.n_seq = n_seq;
+  a.max_keys = max_keys;
+  a.cu_q = cu_q;
+  a.idx = idx;
+  a.n_q = n_q;
+  a.n_heads = n_heads;
+  a.k = k;
+  a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = out_lse;
+  if (a.n_split > 1) {
+    const size_t parts = static_cast<size_t>(n_q) * a.n_split * n_heads;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + parts * kLatentDim * 4);
+  }
+  return hip_status(launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

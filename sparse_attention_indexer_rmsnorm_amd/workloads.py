@@ -11,6 +11,8 @@ so each input is independent of the order in which the others are drawn:
     0 x (pre-norm key activations)   1 gamma            2 q        3 w
     4 context lengths                5 page permutation 6 needle positions
     7 needle noise                   8 needle query choice
+    20 attention q                   21 latents         22 latent slot permutation
+    23 listed keys
 
 Distributions (the DeepSeek Sparse Attention indexer as the four blog pages describe it, with the
 shapes of their 4.5K / 10.5K / 22K-token tests and the 128K context length of the serving config):
@@ -35,6 +37,8 @@ FP4 = 2
 EPS = 1e-6
 
 T_X, T_GAMMA, T_Q, T_W, T_LENS, T_PERM, T_NEEDLE_POS, T_NEEDLE_NOISE, T_NEEDLE_Q = range(9)
+T_ATTN_Q, T_ATTN_KV, T_ATTN_SLOT, T_ATTN_SEL = 20, 21, 22, 23
+LATENT_DIM = 512
 
 
 def rng(seed: int, tensor_id: int) -> np.random.Generator:
@@ -247,3 +251,64 @@ def cfg4(seed: int = 104, needles: bool = True) -> Workload:
 
 
 CONFIGS = {0: cfg0, 1: cfg1, 2: cfg2, 3: cfg3, 4: cfg4}
+
+
+# ---- inputs of the sparse attention over the selected keys --------------------------------------
+
+@dataclass
+class AttnInputs:
+    """Host-side inputs of the sparse attention on a workload's sequences and query rows."""
+    q_bits: np.ndarray       # [n_q, n_heads, 512] uint16 bf16 bit patterns
+    kv_bits: np.ndarray      # [n_slots, 512] uint16
+    kv_slot: np.ndarray      # [n_seq, max_keys] int32
+    idx: np.ndarray          # [n_q, k] int32, -1 = none
+    scale: float
+
+    @property
+    def n_heads(self) -> int:
+        return int(self.q_bits.shape[1])
+
+    def torch_inputs(self, device="cuda"):
+        bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)  # noqa: E731
+        return (bf(self.q_bits), bf(self.kv_bits), torch.from_numpy(self.kv_slot).to(device),
+                torch.from_numpy(self.idx).to(device))
+
+
+def visible_counts(wl: Workload) -> np.ndarray:
+    """Visible compressed keys of every query row: floor((t + 1) / 4), capped at max_keys."""
+    t = wl.query_positions()
+    nv = np.minimum((t + 1) // COMPRESS, wl.max_keys)
+    nv[t < 0] = 0
+    return nv.astype(np.int64)
+
+
+def _bf16_normal_rows(g: np.random.Generator, n: int, width: int, chunk: int = 1 << 16):
+    out = np.empty((n, width), np.uint16)
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        out[r0:r1] = bf16_bits_from_normal(g.standard_normal((r1 - r0, width), dtype=np.float32))
+    return out
+
+
+def attn_inputs(wl: Workload, n_heads: int = 64, k: Optional[int] = None,
+                scale: Optional[float] = None) -> AttnInputs:
+    """q and the latents ~ N(0, 1) rounded to bf16; one latent row per (sequence, key), on a
+    random permutation of the rows; per query row a random subset of min(k, visible) of its
+    visible keys in random order, then -1 padding (the shape of a top-k list, whose order is
+    unspecified); softmax scale 1 / sqrt(512) unless given."""
+    k = wl.k if k is None else int(k)
+    n_seq, max_keys = wl.n_seq, wl.max_keys
+    q = _bf16_normal_rows(rng(wl.seed, T_ATTN_Q), wl.n_q * n_heads, LATENT_DIM)
+    n_slots = n_seq * max_keys
+    kv = _bf16_normal_rows(rng(wl.seed, T_ATTN_KV), n_slots, LATENT_DIM)
+    kv_slot = rng(wl.seed, T_ATTN_SLOT).permutation(n_slots).astype(np.int32).reshape(
+        n_seq, max_keys)
+    nv = visible_counts(wl)
+    g = rng(wl.seed, T_ATTN_SEL)
+    idx = np.full((wl.n_q, k), -1, np.int32)
+    for r in range(wl.n_q):
+        m = int(min(k, nv[r]))
+        if m:
+            idx[r, :m] = g.permutation(int(nv[r]))[:m]
+    return AttnInputs(q_bits=q.reshape(wl.n_q, n_heads, LATENT_DIM), kv_bits=kv, kv_slot=kv_slot,
+                      idx=idx, scale=LATENT_DIM ** -0.5 if scale is None else float(scale))

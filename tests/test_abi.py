@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), f"missing export {n}"
     assert sorted(n for n, _, _ in ix.SIGNATURES) == names
@@ -134,6 +134,42 @@ def test_topk_rows_validation(L):
     assert f(None, 0, 100, None, 10, None, None, None, 0, None) == E_OK
     # a two-pass selection without its workspace
     assert f(FAKE, 4, 40000, None, 1024, FAKE, None, None, 0, None) == E_WS
+
+
+def test_sparse_attn_workspace_and_validation(L):
+    # few rows split their lists: 32 rows x 1024 entries -> 8 splits of 128 entries, each
+    # keeping a 512-dim fp32 partial and (max, sum) per head
+    assert L.idx_sparse_attn_workspace_size(32, 64, 1024) == 32 * 8 * 64 * (512 * 4 + 8)
+    assert L.idx_sparse_attn_workspace_size(256, 64, 512) == 0      # enough rows: no split
+    assert L.idx_sparse_attn_workspace_size(8192, 128, 512) == 0
+    assert L.idx_sparse_attn_workspace_size(32, 48, 1024) == 0      # unsupported head count
+    F = ctypes.c_void_p(0x1000)
+    MIS = ctypes.c_void_p(0x1008)                                  # not 16-byte aligned
+    f = ctypes.c_float
+
+    def call(q=F, kv=F, n_slots=10, slot=F, n_seq=1, max_keys=8, cu=F, idx=F, n_q=4, h=64,
+             k=16, scale=0.1, out=F, ws=None, ws_bytes=0):
+        return L.idx_sparse_attn(q, kv, n_slots, slot, n_seq, max_keys, cu, idx, n_q, h, k,
+                                 f(scale), out, None, ws, ws_bytes, None)
+    assert call(n_q=0) == E_OK
+    assert call(h=48) == E_UNSUP
+    assert call(k=0) == E_INVAL
+    assert call(n_q=-1) == E_INVAL
+    assert call(n_seq=0) == E_INVAL
+    assert call(max_keys=0) == E_INVAL
+    assert call(n_slots=-1) == E_INVAL
+    assert call(scale=float("nan")) == E_INVAL
+    assert call(scale=float("inf")) == E_INVAL
+    assert call(scale=0.0) == E_INVAL
+    assert call(scale=-0.5) == E_INVAL
+    assert call(q=None) == E_INVAL
+    assert call(idx=None) == E_INVAL
+    assert call(out=None) == E_INVAL
+    assert call(q=MIS) == E_INVAL
+    assert call(kv=MIS) == E_INVAL
+    assert call(out=MIS) == E_INVAL
+    assert call(n_q=32, k=1024) == E_WS                              # split: needs a workspace
+    assert call(n_q=32, k=1024, ws=F, ws_bytes=100) == E_WS
 
 
 def test_binding_rejects_host_tensors():
