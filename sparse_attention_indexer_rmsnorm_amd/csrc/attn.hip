@@ -7,17 +7,24 @@
 // One workgroup per (query row, split of the list, block of HW = min(H, 64) heads), HW / 16
 // waves.  Wave w owns 32 heads of the block, 32 (w / 2) .., and one half of the 512 output dims,
 // 256 (w % 2) ...  Per 32 listed keys:
-//   1. the keys' latents are gathered into LDS twice: row-major (16-byte chunks XOR-swizzled by
-//      row) and transposed [dim][key] (chunks swizzled by dim), the key order inside each 16-key
-//      step permuted so that the transposed operand matches the accumulator layout below;
-//   2. S^T = K Q^T on bf16 MFMA 32x32x16: each wave of a pair sums over its own 256 dims, and the
-//      pair swaps partial sums through LDS (fp32 addition commutes, so both hold the same S);
+//   1. the keys' latents go from global memory straight into LDS (global_load_lds_dwordx4: one
+//      instruction per 1 KB latent row, each lane's 16 bytes landing at its own slot), up to three
+//      chunks ahead of their use in four buffers, so no registers or VALU work stage them; the
+//      16-byte chunks of row r are XOR-swizzled by sw(r) = 2 (r % 4) + (r / 4) % 2;
+//   2. S^T = K Q^T on bf16 MFMA 32x32x16 with the latents as A operand (ds_read_b128): each wave
+//      of a pair sums over its own 256 dims, and the pair swaps partial sums through LDS (fp32
+//      addition commutes, so both hold the same S);
 //   3. online softmax in base 2: each lane owns one head and 16 of the 32 keys, the maximum is
 //      shared with the lane holding the other 16, a reference maximum moves only when exceeded
 //      by more than 2^8, and the weights are rounded to bf16 (the weight sum adds the rounded
 //      values, so the weights used sum to the divisor);
 //   4. O^T += K^T P^T on the same MFMA: the accumulator of S^T, rounded, is already the B operand
-//      of this product (lane = head, 8 keys), and the transposed latents are its A operand.
+//      of this product (lane = head, 8 keys), and the A operand, latents transposed to (dim,
+//      4 keys) per lane, comes from the same row-major buffer through gfx950's transposing LDS
+//      read ds_read_b64_tr_b16 (in each 16-lane group, lane j's element f is element j % 4 of
+//      lane 4 f + j / 4's 8-byte read).
+// Chunks are software-pipelined: S of chunk c + 1 is issued before the softmax of chunk c, so
+// its MFMAs run while the VALU computes the weights.
 // Batches of few rows split each list over several workgroups; a second kernel merges their
 // partial outputs by their maxima and weight sums.
 
@@ -41,8 +48,8 @@ union AFrag {
 };
 
 constexpr int kRowBytes = kLatentDim * 2;                  // 1024: one latent
-constexpr int kRowMajorBytes = kAttnChunk * kRowBytes;      // 32 KB
-constexpr int kTransBytes = kLatentDim * kAttnChunk * 2;    // 32 KB: [512 dims][32 keys]
+constexpr int kChunkBytes = kAttnChunk * kRowBytes;         // 32 KB
+constexpr int kAttnBufs = 4;                                // chunk buffers in LDS
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -61,10 +68,15 @@ __device__ __forceinline__ int32_t seq_of_row(const int32_t* cu_q, int32_t n_seq
   return lo;
 }
 
-// Row-major copy: 16-byte chunk c of key row r sits at chunk c ^ row_swizzle(r).  Eight
-// consecutive rows (an MFMA operand read) and the rows 4q + e of eight key quads q (one staging
-// write) both land on eight distinct 16-byte bank groups.
-__device__ __forceinline__ int row_swizzle(int r) { return (r ^ (r >> 2)) & 7; }
+// 16-byte chunk c of latent row r (r < 32) sits at chunk c ^ sw(r) of the buffer row.  Eight
+// consecutive rows (one operand read of 8 lanes) get eight distinct values, and the rows 4u..4u+3
+// of one transposing read get four distinct values of bits 1-2, i.e. four distinct 32-byte
+// groups of banks.
+__device__ __forceinline__ int sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
 // global loads, so the next chunk's latents stay in flight across it (a __syncthreads() fence
@@ -77,22 +89,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Position of key kappa (0..31) in a transposed row: inside each 16-key step, bits 2 and 3 of
-// the key swap, so that positions 16 kk + 8 g + e hold keys 16 kk + 8 (e / 4) + 4 g + e % 4.
-__device__ __forceinline__ int trans_pos(int kappa) {
-  return (kappa & ~12) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
-}
-
 template <int HW>
 __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
-  constexpr int NT = HW * 4;                   // HW / 16 waves
-  constexpr int kItems = kAttnChunk / 4 * (kLatentDim / 8) / NT;   // (4 keys x 8 dims) per thread
-  static_assert(kItems >= 1 && kItems * NT == 512, "staging items");
-  __shared__ __attribute__((aligned(16))) uint8_t kr[kRowMajorBytes];   // also the S exchange
-  __shared__ __attribute__((aligned(16))) uint8_t kt[kTransBytes];
+  constexpr int NW = HW / 16;                  // waves
+  constexpr int NT = 64 * NW;
+  constexpr int kRowsPerWave = kAttnChunk / NW;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kAttnBufs][kChunkBytes];   // latents
+  __shared__ __attribute__((aligned(16))) float ex[NW * 16 * 64];         // S^T partial sums
   __shared__ int32_t sl[kMaxAttnList];        // latent row of each list entry, -1 = none
   __shared__ int32_t n_used;
-  static_assert(HW / 16 * 16 * 64 * 4 <= kRowMajorBytes, "exchange fits the row-major buffer");
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -112,22 +117,18 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   {
     const uint16_t* qrow = a.q + (i * H + h) * kLatentDim + 256 * dh + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks].u = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+    for (int ks = 0; ks < 16; ++ks) {
+      qf[ks].u = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+      // kept in accumulation registers: the MFMA reads its B operand from there, and the arch
+      // registers stay free for the outputs and for several operand reads in flight
+      asm volatile("" : "+a"(qf[ks].u));
+    }
   }
 
   floatx16 oacc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) oacc[t] = floatx16{};
   float m_run = -INFINITY, l_run = 0.0f;
-
-  const uint8_t* s_base[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    s_base[c] = kr + m * kRowBytes + 512 * dh + (((2 * c + g) ^ row_swizzle(m)) << 4);
-  const uint8_t* t_base[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    t_base[kk] = kt + (256 * dh + m) * (kAttnChunk * 2) + (((2 * kk + g) ^ ((m >> 1) & 3)) << 4);
 
   // The workgroup's list entries, resolved to latent rows once: slot or -1.
   const int j0 = sp * a.split_keys;
@@ -153,107 +154,137 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   __syncthreads();
   const int n_chunks = (n_used + kAttnChunk - 1) / kAttnChunk;   // up to the last valid entry
 
-  // 1. gather: thread item = 4 keys x 8 dims (4 rows x 16 B).  The next chunk's rows are loaded
-  //    into registers before the current chunk is computed, so their latency overlaps the MFMAs.
-  u32x4 rows[kItems][4];
-  // Item of a thread: key quad q4 = item % 8 (fastest, so that the eight lanes writing one
-  // transposed row are neighbours), dim octet oct = item / 8.
-  auto load_chunk = [&](int c) {
+  // 1. Wave w requests rows w * kRowsPerWave .. of chunk c into buffer c % 4: lane L fetches the
+  //    logical chunk L ^ sw(r) of its row, which then lands at physical chunk L.  An entry with
+  //    no latent reads row 0 (some row is valid when a chunk is requested); its score is masked,
+  //    and its weight 0 times finite latents adds nothing.
+  auto request = [&](int c) {
+    uint8_t* dst = kbuf[c % kAttnBufs];
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-      const int item = threadIdx.x + it * NT;
-      const int q4 = item & 7, oct = item >> 3;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int32_t slot = sl[c * kAttnChunk + 4 * q4 + e];
-        rows[it][e] = slot >= 0 ? *reinterpret_cast<const u32x4*>(
-                                      a.kv + static_cast<int64_t>(slot) * kLatentDim + 8 * oct)
-                                : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+      const int r = wid * kRowsPerWave + rr;
+      const int32_t slot = max(sl[c * kAttnChunk + r], 0);
+      __builtin_amdgcn_global_load_lds(
+          a.kv + static_cast<int64_t>(slot) * kLatentDim + 8 * (lane ^ sw(r)),
+          (lds_void*)(dst + r * kRowBytes), 16, 0, 0);
     }
   };
-  if (n_chunks > 0) load_chunk(0);
+#pragma unroll
+  for (int c = 0; c < kAttnBufs - 1; ++c)
+    if (c < n_chunks) request(c);
 
-  for (int c = 0; c < n_chunks; ++c) {
-    lds_barrier();                             // the previous chunk's LDS readers are done
-    const uint32_t vmask = static_cast<uint32_t>(__ballot(sl[c * kAttnChunk + m] >= 0));
-    // row-major and transposed copies of the chunk
+
+  // Operand addresses inside a buffer (bytes):
+  //  - S^T, A = latents: lane (m, g) reads row m, chunk 32 dh + 2 ks + g; the swizzle reaches
+  //    the low 3 bits only, so four offsets (ks % 4) plus 128 B per 4 steps cover it;
+  //  - O^T, A = transposed latents, k-step kk, half e / 4 = hf, tile t: the lane's 8-byte read
+  //    is row 16 kk + 8 hf + 4 g' + f of group G = lane / 16 (g' = G / 2, f = (lane % 16) / 4),
+  //    dims 256 dh + 32 t + 16 (G % 2) + 4 q (q = lane % 4); the swizzle moves bits 0-2 of the
+  //    chunk, where t contributes bit 2, so t % 2 picks one of two offsets and t / 2 adds 128 B.
+  int s_off[4];
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-      const int item = threadIdx.x + it * NT;
-      const int q4 = item & 7, oct = item >> 3;
-      const u32x4* r = rows[it];
+  for (int c = 0; c < 4; ++c) s_off[c] = m * kRowBytes + 512 * dh + (((2 * c + g) ^ sw(m)) << 4);
+  int t_off[2][2][2];
+  {
+    const int G = lane >> 4, f = (lane >> 2) & 3, q = lane & 3, gg = G >> 1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 4 * q4 + e;
-        *reinterpret_cast<u32x4*>(kr + key * kRowBytes + ((oct ^ row_swizzle(key)) << 4)) = r[e];
-      }
-      // transposed: the 8 quads of a dim fill its 64-byte row (8 distinct (chunk, half) slots);
-      // lanes with odd oct take the dims of the other parity first, so that the 16 lanes of one
-      // write cover both halves of the banks
-      const int pos = trans_pos(4 * q4);
-      const int flip = oct & 1;
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int hh = k2 ^ flip;
-          const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
-          const int d = 8 * oct + 2 * w + hh;
-          u32x2 v;
-          v.x = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);   // keys 0, 1 of the quad at dim d
-          v.y = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);   // keys 2, 3
-          const int phys = (((pos >> 3) ^ ((d >> 1) & 3)) << 4) | (((pos >> 2) & 1) << 3);
-          *reinterpret_cast<u32x2*>(kt + d * (kAttnChunk * 2) + phys) = v;
+        for (int tp = 0; tp < 2; ++tp) {
+          const int r = 16 * kk + 8 * hf + 4 * gg + f;
+          const int ch = (4 * tp + 2 * (G & 1) + (q >> 1)) ^ sw(r);
+          t_off[kk][hf][tp] = r * kRowBytes + 512 * dh + (ch << 4) + 8 * (q & 1);
         }
-      }
-    }
-    if (c + 1 < n_chunks) load_chunk(c + 1);
-    lds_barrier();
+  }
 
-    // 2. S^T partial over this wave's 256 dims: A = latents (key m, 8 dims), B = q
-    //    chunk 32 dh + 2 ks + g of row m sits at chunk ^ row_swizzle(m): the swizzle reaches only
-    //    the low 3 bits, so four bases (ks % 4) and immediate offsets of 128 B per 4 steps cover it
-    floatx16 sacc = floatx16{};
+  // gfx9 s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt
+  // 11:8.  Requests complete in order, so "at most n chunks outstanding" means every older one
+  // has landed.
+  static_assert(3 * kRowsPerWave < 64, "vmcnt range");
+  auto wait_chunks_left = [&](int n) {        // n = 0..2, uniform
+    if (n >= 2)
+      __builtin_amdgcn_s_waitcnt(((2 * kRowsPerWave) & 15) | 0x0070 | (((2 * kRowsPerWave) >> 4) << 14));
+    else if (n == 1)
+      __builtin_amdgcn_s_waitcnt((kRowsPerWave & 15) | 0x0070 | ((kRowsPerWave >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // 2. partial S^T of chunk c over this wave's 256 dims (operands read four steps ahead of their
+  //    MFMA; two accumulators, even and odd steps, so that consecutive MFMAs do not wait for each
+  //    other's result), and the sum with the partner wave's partial through LDS
+  auto s_partial = [&](int c) {
+    const uint8_t* buf = kbuf[c % kAttnBufs];
+    floatx16 sacc2[2] = {floatx16{}, floatx16{}};
+    AFrag ka[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      ka[ks].u = *reinterpret_cast<const u32x4*>(buf + s_off[ks]);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      AFrag ka;
-      ka.u = *reinterpret_cast<const u32x4*>(s_base[ks & 3] + 128 * (ks >> 2));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka.v, qf[ks].v, sacc, 0, 0, 0);
+      sacc2[ks & 1] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 3].v, qf[ks].v, sacc2[ks & 1], 0, 0, 0);
+      if (ks + 4 < 16)
+        ka[ks & 3].u = *reinterpret_cast<const u32x4*>(buf + s_off[ks & 3] + 128 * ((ks + 4) >> 2));
     }
-    lds_barrier();                             // every wave is done with the row-major latents
-    float* ex = reinterpret_cast<float*>(kr);
+    return sacc2[0] + sacc2[1];
+  };
+  auto s_exchange = [&](floatx16 part) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ex[(wid * 16 + r) * 64 + lane] = sacc[r];
+    for (int r = 0; r < 16; ++r) ex[(wid * 16 + r) * 64 + lane] = part[r];
     lds_barrier();
+    float other[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] += ex[((wid ^ 1) * 16 + r) * 64 + lane];
+    for (int r = 0; r < 16; ++r) other[r] = ex[((wid ^ 1) * 16 + r) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] += other[r];
+    return part;
+  };
 
-    // 3. online softmax in base 2: lane (m, g) holds head h and keys 8 (r / 4) + 4 g + r % 4.
-    //    The reference maximum moves only when a chunk's maximum exceeds it by more than 2^8, so
-    //    the outputs are rescaled rarely; weights stay below 2^8, exact in range for bf16 / fp32.
-    if (vmask != 0xFFFFFFFFu) {                // the same for every lane of the wave
+  // S of the chunk being finished, and its validity mask
+  floatx16 s_cur = floatx16{};
+  uint32_t vmask_cur = 0;
+  if (n_chunks > 0) {
+    wait_chunks_left(min(n_chunks - 1, kAttnBufs - 2));
+    s_cur = s_exchange(s_partial(0));
+    vmask_cur = static_cast<uint32_t>(__ballot(sl[m] >= 0));
+  }
+
+  // One step per chunk c: S of chunk c + 1 is computed while the softmax of chunk c runs (its
+  // MFMAs execute in the matrix pipe while the VALU works), then P.V of chunk c.
+  for (int c = 0; c < n_chunks; ++c) {
+    const bool has_next = c + 1 < n_chunks;
+    // chunk c + 1 has landed in every wave's rows; every wave is done with chunk c - 1, whose
+    // buffer chunk c + kAttnBufs - 1 now overwrites
+    wait_chunks_left(min(n_chunks - c - 2, kAttnBufs - 3));
+    if (c + kAttnBufs - 1 < n_chunks) request(c + kAttnBufs - 1);
+    floatx16 s_next = floatx16{};
+    if (has_next) s_next = s_partial(c + 1);
+
+    // 3. online softmax of chunk c in base 2: lane (m, g) holds head h and keys
+    //    8 (r / 4) + 4 g + r % 4.  The reference maximum moves only when a chunk's maximum
+    //    exceeds it by more than 2^8, so the outputs are rescaled rarely; weights stay below 2^8.
+    floatx16 sv = s_cur;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-        sacc[r] = ((vmask >> key) & 1u) ? sacc[r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+      sv[r] = ((vmask_cur >> key) & 1u) ? sv[r] : -INFINITY;
     }
-    float smax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    float smax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
 #pragma unroll
     for (int r = 4; r < 16; r += 4)
-      smax = fmaxf(smax, fmaxf(fmaxf(sacc[r], sacc[r + 1]), fmaxf(sacc[r + 2], sacc[r + 3])));
+      smax = fmaxf(smax, fmaxf(fmaxf(sv[r], sv[r + 1]), fmaxf(sv[r + 2], sv[r + 3])));
     smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
     const float mloc = smax * a.scale_log2;    // the scale is positive
     const bool move = mloc > m_run + 8.0f;     // -inf m_run: the first listed key moves it
     const float m_new = move ? mloc : m_run;
-    if (__ballot(move && m_run != -INFINITY)) {
-      const float alpha = (move && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new)
-                                                       : 1.0f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) oacc[t] *= alpha;
-      l_run *= alpha;
-    }
+    const bool rescale = move && m_run != -INFINITY;
+    const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
     const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;   // nothing listed yet: weights 0
     union {
@@ -263,28 +294,50 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, neg_m));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r + 1], a.scale_log2, neg_m));
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], a.scale_log2, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], a.scale_log2, neg_m));
       const bf16x2 pb = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};   // RNE
       const uint32_t u = __builtin_bit_cast(uint32_t, pb);
       psum += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
       pf[r >> 3].w[(r & 7) >> 1] = u;
     }
-    l_run += psum;
+    l_run = l_run * alpha + psum;
+    if (__ballot(rescale)) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) oacc[t] *= alpha;
+    }
 
-    // 4. O^T += K^T P^T over this wave's dims: A = transposed latents (dim m, 8 keys)
-    //    dim d = 256 dh + 32 t + m, chunk (2 kk + g) ^ ((d / 2) % 4) = (2 kk + g) ^ ((m / 2) % 4):
-    //    two bases and immediate offsets of 2 KB per tile
+    // 4. O^T += K^T P^T of chunk c over this wave's dims: A = latents transposed by the LDS
+    //    read (operands read four MFMAs ahead)
+    const uint8_t* buf = kbuf[c % kAttnBufs];
+    auto tr_frag = [&](int n) {                // n = t + 8 kk: a tile's two steps 8 apart
+      const int t = n & 7, kk = n >> 3;
+      const int add = 128 * (t >> 1);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(buf + t_off[kk][0][t & 1] + add));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(buf + t_off[kk][1][t & 1] + add));
+      AFrag f;
+      f.u = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                  __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+      return f;
+    };
+    AFrag kt[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int n = 0; n < 4; ++n) kt[n] = tr_frag(n);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        AFrag ka;
-        ka.u = *reinterpret_cast<const u32x4*>(t_base[kk] + 32 * (kAttnChunk * 2) * t);
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka.v, pf[kk].v, oacc[t], 0, 0, 0);
-      }
+    for (int n = 0; n < 16; ++n) {
+      oacc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[n & 3].v, pf[n >> 3].v,
+                                                           oacc[n & 7], 0, 0, 0);
+      if (n + 4 < 16) kt[n & 3] = tr_frag(n + 4);
+    }
+
+    if (has_next) {
+      s_cur = s_exchange(s_next);
+      vmask_cur = static_cast<uint32_t>(__ballot(sl[(c + 1) * kAttnChunk + m] >= 0));
     }
   }
+  // no request is left in flight: the last chunk requests nothing
 
   // lanes (m, 0) and (m, 1) summed different keys of head h under the same maximum
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
