@@ -112,17 +112,26 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   const int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
   const int h = HW * hb + 32 * hg + m;
 
+  // Prologue, ordered so that its memory round trips overlap: the list entries and q are loaded
+  // together, then the entries' latent rows (slot or -1) go into LDS, then the first chunks are
+  // requested, and only then is q pinned to the accumulation registers (which waits for it).
+  const int j0 = sp * a.split_keys;
+  const int n_list = max(0, min(a.k, j0 + a.split_keys) - j0);
+  constexpr int kPer = kMaxAttnList / NT;     // list entries per thread
+  if (threadIdx.x == 0) n_used = 0;
+  int32_t ent[kPer];
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + p * NT;
+    ent[p] = (e < n_list && b >= 0) ? a.idx[i * a.k + j0 + e] : -1;
+  }
+
   // q as the B operand of S^T = K Q^T: lane (m, g) holds head h, dims 256 dh + 16 ks + 8 g ..
   AFrag qf[16];
   {
     const uint16_t* qrow = a.q + (i * H + h) * kLatentDim + 256 * dh + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      qf[ks].u = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-      // kept in accumulation registers: the MFMA reads its B operand from there, and the arch
-      // registers stay free for the outputs and for several operand reads in flight
-      asm volatile("" : "+a"(qf[ks].u));
-    }
+    for (int ks = 0; ks < 16; ++ks) qf[ks].u = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
   }
 
   floatx16 oacc[8];
@@ -130,28 +139,26 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   for (int t = 0; t < 8; ++t) oacc[t] = floatx16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // The workgroup's list entries, resolved to latent rows once: slot or -1.
-  const int j0 = sp * a.split_keys;
-  const int n_list = max(0, min(a.k, j0 + a.split_keys) - j0);
-  if (threadIdx.x == 0) n_used = 0;
-  __syncthreads();
   int last = 0;
-  for (int e = threadIdx.x; e < n_list; e += NT) {
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int32_t s = ent[p];
     int32_t slot = -1;
-    if (b >= 0) {
-      const int32_t s = a.idx[i * a.k + j0 + e];
-      if (s >= 0 && s < a.max_keys) {
-        const int32_t v = a.kv_slot[static_cast<int64_t>(b) * a.max_keys + s];
-        if (v >= 0 && v < a.n_slots) slot = v;
-      }
+    if (s >= 0 && s < a.max_keys) {
+      const int32_t v = a.kv_slot[static_cast<int64_t>(b) * a.max_keys + s];
+      slot = (v >= 0 && v < a.n_slots) ? v : -1;
     }
-    sl[e] = slot;
-    if (slot >= 0) last = e + 1;
+    ent[p] = slot;
   }
-  for (int e = n_list + threadIdx.x; e < ((n_list + kAttnChunk - 1) & ~(kAttnChunk - 1)); e += NT)
-    sl[e] = -1;
+  lds_barrier();                               // n_used is cleared
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + p * NT;
+    if (e < ((n_list + kAttnChunk - 1) & ~(kAttnChunk - 1))) sl[e] = e < n_list ? ent[p] : -1;
+    if (e < n_list && ent[p] >= 0) last = e + 1;
+  }
   if (last) atomicMax(&n_used, last);
-  __syncthreads();
+  lds_barrier();
   const int n_chunks = (n_used + kAttnChunk - 1) / kAttnChunk;   // up to the last valid entry
 
   // 1. Wave w requests rows w * kRowsPerWave .. of chunk c into buffer c % 4: lane L fetches the
@@ -172,6 +179,10 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < kAttnBufs - 1; ++c)
     if (c < n_chunks) request(c);
+  // q kept in accumulation registers: the MFMA reads its B operand from there, and the arch
+  // registers stay free for the outputs and for several operand reads in flight
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qf[ks].u));
 
 
   // Operand addresses inside a buffer (bytes):

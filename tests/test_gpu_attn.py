@@ -169,6 +169,17 @@ def test_attn_on_the_oracle_selection(oracle_mod):
     _check(a, wl.cu_q, g_out, g_lse, rows, oracle_mod, "oracle selection")
 
 
+def test_attn_long_lists_are_split(oracle_mod):
+    """Lists longer than one workgroup's slot table (2048 entries) are split even when the batch
+    has enough rows, and merged: 300 rows with k = 3000 over sequences of up to 4000 keys."""
+    wl = W.make_workload("long-lists", 61, [16000, 12000], [150, 150], 3000, permute_pages=True)
+    a = W.attn_inputs(wl, k=3000)
+    assert ix.sparse_attn_workspace_size(wl.n_q, 64, 3000) > 0, "the lists must be split"
+    g_out, g_lse = _run_gpu(a, wl.cu_q)
+    rows = _rows(wl.n_q, 12, 61)
+    _check(a, wl.cu_q, g_out, g_lse, rows, oracle_mod, "long lists")
+
+
 def test_attn_repeatable():
     wl = workload(2)
     a = W.attn_inputs(wl)
