@@ -422,7 +422,7 @@ int idx_sparse_attn(const void* q, const void* kv, int64_t n_slots, const int32_
   const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
   if (misaligned(q) || misaligned(kv) || misaligned(out)) return IDX_EINVAL;
   AttnArgs a{};
-  attn_plan(n_q, k, &a.n_split, &a.split_keys);
+  attn_plan(n_q, n_heads, k, &a.n_split, &a.split_keys);
   if (n_q * a.n_split * 2 > INT32_MAX || n_q * n_heads > INT64_C(4) * INT32_MAX) return IDX_EINVAL;
   const size_t need = attn_workspace_bytes(n_q, n_heads, k);
   if (need > 0 && (!workspace || workspace_bytes < need)) return IDX_EWORKSPACE;

@@ -9,7 +9,10 @@ namespace dsa {
 
 constexpr int kLatentDim = 512;     // main-KV latent: key and value of every head
 constexpr int kAttnChunk = 32;      // listed keys staged per step
-constexpr int kMaxAttnList = 2048;  // list entries one workgroup resolves
+constexpr int kMaxAttnList = 2048;  // list entries one workgroup resolves (1024 with 32 heads)
+
+// List entries one workgroup resolves for n_heads heads: eight per thread.
+constexpr int attn_max_list(int n_heads) { return n_heads == 32 ? kMaxAttnList / 2 : kMaxAttnList; }
 
 struct AttnArgs {
   const uint16_t* q;        // [n_q, H, 512] bf16
@@ -33,7 +36,7 @@ struct AttnArgs {
 };
 
 // Splits per query row and entries per split for a batch; workspace bytes for the partials.
-void attn_plan(int64_t n_q, int32_t k, int32_t* n_split, int32_t* split_keys);
+void attn_plan(int64_t n_q, int32_t n_heads, int32_t k, int32_t* n_split, int32_t* split_keys);
 size_t attn_workspace_bytes(int64_t n_q, int32_t n_heads, int32_t k);
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);

@@ -4,8 +4,10 @@
 // Knowledge: the sparse attention reads the top-K entries, the main KV cache is bf16 with
 // head_dim 512; "The Fused Kernel Decision", Message: that cache is unpaged, one slot per entry).
 //
-// One workgroup per (query row, split of the list, block of HW = min(H, 64) heads), HW / 16
-// waves.  Wave w owns 32 heads of the block, 32 (w / 2) .., and one half of the 512 output dims,
+// Work items are (query row, split of the list, block of HW = min(H, 64) heads); a workgroup of
+// HW / 16 waves, one per CU (its LDS fills the CU), takes items blockIdx.x, blockIdx.x + G, ...
+// (G workgroups), and loads the next item's list entries, latent rows and q while it works on the
+// current one, so only the first item waits for them.  Wave w owns 32 heads of the block, 32 (w / 2) .., and one half of the 512 output dims,
 // 256 (w % 2) ...  Per 32 listed keys:
 //   1. the keys' latents go from global memory straight into LDS (global_load_lds_dwordx4: one
 //      instruction per 1 KB latent row, each lane's 16 bytes landing at its own slot), up to three
@@ -89,6 +91,19 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// One 16-byte global-to-LDS transfer per lane (global_load_lds_dwordx4): lane L's 16 bytes land
+// at LDS byte lds + 16 L, lds being wave-uniform.  Written as inline assembly so that the
+// compiler does not see an LDS write: it cannot tell the four chunk buffers apart and would
+// otherwise wait for every transfer in flight before each LDS read.  The kernel orders the
+// buffers itself, with counter waits and barriers.  (M0 takes the LDS address; one wait state
+// separates its write from the transfer.)
+__device__ __forceinline__ void dma_row16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
 template <int HW>
 __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   constexpr int NW = HW / 16;                  // waves
@@ -97,7 +112,7 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kAttnBufs][kChunkBytes];   // latents
   __shared__ __attribute__((aligned(16))) float ex[NW * 16 * 64];         // S^T partial sums
   __shared__ int32_t sl[kMaxAttnList];        // latent row of each list entry, -1 = none
-  __shared__ int32_t n_used;
+  __shared__ int32_t last_w[NW];              // per wave: one past its last valid entry
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -105,61 +120,73 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   const int m = lane & 31, g = lane >> 5;
   const int H = a.n_heads;
   const int n_hb = H / HW;
-  const int64_t rs = blockIdx.x / n_hb;                 // i * n_split + sp
-  const int hb = blockIdx.x - static_cast<int>(rs * n_hb);
-  const int64_t i = rs / a.n_split;
-  const int sp = static_cast<int>(rs - i * a.n_split);
-  const int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
-  const int h = HW * hb + 32 * hg + m;
+  const int64_t n_items = a.n_q * a.n_split * n_hb;
 
-  // Prologue, ordered so that its memory round trips overlap: the list entries and q are loaded
-  // together, then the entries' latent rows (slot or -1) go into LDS, then the first chunks are
-  // requested, and only then is q pinned to the accumulation registers (which waits for it).
-  const int j0 = sp * a.split_keys;
-  const int n_list = max(0, min(a.k, j0 + a.split_keys) - j0);
-  constexpr int kPer = kMaxAttnList / NT;     // list entries per thread
-  if (threadIdx.x == 0) n_used = 0;
-  int32_t ent[kPer];
+  // Item it = (i * n_split + sp) * n_hb + hb: row i, split sp, head block hb; b is its sequence.
+  struct Item {
+    int64_t i;
+    int32_t b;
+    int sp, hb, n_list;
+  };
+  auto item_of = [&](int64_t it) {
+    Item t;
+    const int64_t rs = it / n_hb;
+    t.hb = static_cast<int>(it - rs * n_hb);
+    t.i = rs / a.n_split;
+    t.sp = static_cast<int>(rs - t.i * a.n_split);
+    t.b = seq_of_row(a.cu_q, a.n_seq, t.i);
+    const int j0 = t.sp * a.split_keys;
+    t.n_list = t.b >= 0 ? max(0, min(a.k, j0 + a.split_keys) - j0) : 0;
+    return t;
+  };
+  constexpr int kPer = attn_max_list(HW) / NT;   // list entries per thread
+  static_assert(kPer == 8, "eight list entries per thread");
+  // list entries of an item (-1 = none), then their latent rows (-1 = none)
+  auto load_entries = [&](const Item& t, int32_t (&ent)[kPer]) {
+    const int32_t* src = a.idx + t.i * a.k + t.sp * a.split_keys;
 #pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int e = threadIdx.x + p * NT;
-    ent[p] = (e < n_list && b >= 0) ? a.idx[i * a.k + j0 + e] : -1;
-  }
-
-  // q as the B operand of S^T = K Q^T: lane (m, g) holds head h, dims 256 dh + 16 ks + 8 g ..
-  AFrag qf[16];
-  {
-    const uint16_t* qrow = a.q + (i * H + h) * kLatentDim + 256 * dh + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks].u = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-  }
-
-  floatx16 oacc[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) oacc[t] = floatx16{};
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  int last = 0;
-#pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int32_t s = ent[p];
-    int32_t slot = -1;
-    if (s >= 0 && s < a.max_keys) {
-      const int32_t v = a.kv_slot[static_cast<int64_t>(b) * a.max_keys + s];
-      slot = (v >= 0 && v < a.n_slots) ? v : -1;
+    for (int p = 0; p < kPer; ++p) {
+      const int e = threadIdx.x + p * NT;
+      ent[p] = e < t.n_list ? src[e] : -1;
     }
-    ent[p] = slot;
-  }
-  lds_barrier();                               // n_used is cleared
+  };
+  // (every load is issued before any result is tested, so they overlap: an entry out of range
+  // reads column 0 of the row, and a row outside the sequences row 0, and the result is dropped)
+  auto resolve_rows = [&](const Item& t, int32_t (&ent)[kPer]) {
+    const int32_t* srow = a.kv_slot + static_cast<int64_t>(max(t.b, 0)) * a.max_keys;
+    int32_t v[kPer];
 #pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int e = threadIdx.x + p * NT;
-    if (e < ((n_list + kAttnChunk - 1) & ~(kAttnChunk - 1))) sl[e] = e < n_list ? ent[p] : -1;
-    if (e < n_list && ent[p] >= 0) last = e + 1;
-  }
-  if (last) atomicMax(&n_used, last);
-  lds_barrier();
-  const int n_chunks = (n_used + kAttnChunk - 1) / kAttnChunk;   // up to the last valid entry
+    for (int p = 0; p < kPer; ++p) v[p] = srow[(ent[p] >= 0 && ent[p] < a.max_keys) ? ent[p] : 0];
+#pragma unroll
+    for (int p = 0; p < kPer; ++p)
+      ent[p] = (ent[p] >= 0 && ent[p] < a.max_keys && v[p] >= 0 && v[p] < a.n_slots) ? v[p] : -1;
+  };
+  // q as the B operand of S^T = K Q^T: lane (m, g) holds head h, dims 256 dh + 16 ks + 8 g ..
+  auto load_q = [&](const Item& t, AFrag (&qd)[16]) {
+    const int h = HW * t.hb + 32 * hg + m;
+    const uint16_t* qrow = a.q + (t.i * H + h) * kLatentDim + 256 * dh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qd[ks].u = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+  };
+  // The item's latent rows into the slot table; returns its number of 32-entry chunks, up to the
+  // last valid entry.  The caller has made sure no wave still reads the table.
+  auto install = [&](const Item& t, const int32_t (&ent)[kPer]) {
+    int last = 0;
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int e = threadIdx.x + p * NT;
+      if (e < ((t.n_list + kAttnChunk - 1) & ~(kAttnChunk - 1))) sl[e] = e < t.n_list ? ent[p] : -1;
+      if (e < t.n_list && ent[p] >= 0) last = e + 1;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    if (lane == 0) last_w[wid] = last;
+    lds_barrier();
+    int n_used = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n_used = max(n_used, last_w[w]);
+    return (n_used + kAttnChunk - 1) / kAttnChunk;
+  };
 
   // 1. Wave w requests rows w * kRowsPerWave .. of chunk c into buffer c % 4: lane L fetches the
   //    logical chunk L ^ sw(r) of its row, which then lands at physical chunk L.  An entry with
@@ -171,19 +198,39 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
     for (int rr = 0; rr < kRowsPerWave; ++rr) {
       const int r = wid * kRowsPerWave + rr;
       const int32_t slot = max(sl[c * kAttnChunk + r], 0);
-      __builtin_amdgcn_global_load_lds(
-          a.kv + static_cast<int64_t>(slot) * kLatentDim + 8 * (lane ^ sw(r)),
-          (lds_void*)(dst + r * kRowBytes), 16, 0, 0);
+      const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) uint8_t*)(dst + r * kRowBytes)));
+      dma_row16(a.kv + static_cast<int64_t>(slot) * kLatentDim + 8 * (lane ^ sw(r)),
+                __builtin_amdgcn_readfirstlane(lds));
     }
   };
+
+  // First item: its entries and q are loaded together, then its latent rows; q reaches the
+  // operand registers through the same copy as every later item's (so no load into them is
+  // outstanding where the products read them).  The next item's entries and q are issued before
+  // the first chunks are requested: all requests then complete in order behind them, so the
+  // chunk waits below stay exact.
+  int64_t it = blockIdx.x;
+  if (it >= n_items) return;
+  Item cur = item_of(it);
+  int32_t ent[kPer];
+  AFrag qf[16], qn[16];
+  load_entries(cur, ent);
+  load_q(cur, qn);
+  resolve_rows(cur, ent);
+  int n_chunks = install(cur, ent);
+  __builtin_amdgcn_s_waitcnt(0x0070);
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qf[ks] = qn[ks];
+  int64_t it_next = it + gridDim.x;
+  Item nxt = item_of(it_next < n_items ? it_next : it);
+  if (it_next < n_items) {
+    load_entries(nxt, ent);
+    load_q(nxt, qn);
+  }
 #pragma unroll
   for (int c = 0; c < kAttnBufs - 1; ++c)
     if (c < n_chunks) request(c);
-  // q kept in accumulation registers: the MFMA reads its B operand from there, and the arch
-  // registers stay free for the outputs and for several operand reads in flight
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qf[ks].u));
-
 
   // Operand addresses inside a buffer (bytes):
   //  - S^T, A = latents: lane (m, g) reads row m, chunk 32 dh + 2 ks + g; the swizzle reaches
@@ -257,6 +304,19 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
     return part;
   };
 
+  for (;;) {
+  const bool has_next_item = it_next < n_items;
+  const int h = HW * cur.hb + 32 * hg + m;
+  const int64_t i = cur.i;
+  // q kept in accumulation registers: the MFMA reads its B operand from there, and the arch
+  // registers stay free for the outputs and for several operand reads in flight
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qf[ks].u));
+  floatx16 oacc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) oacc[t] = floatx16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
   // S of the chunk being finished, and its validity mask
   floatx16 s_cur = floatx16{};
   uint32_t vmask_cur = 0;
@@ -274,6 +334,9 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
     // buffer chunk c + kAttnBufs - 1 now overwrites
     wait_chunks_left(min(n_chunks - c - 2, kAttnBufs - 3));
     if (c + kAttnBufs - 1 < n_chunks) request(c + kAttnBufs - 1);
+    // last chunk: every request has landed, so the next item's latent rows are looked up now,
+    // behind this chunk's softmax and P.V
+    if (c == n_chunks - 1 && has_next_item) resolve_rows(nxt, ent);
     floatx16 s_next = floatx16{};
     if (has_next) s_next = s_partial(c + 1);
 
@@ -349,6 +412,19 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
     }
   }
   // no request is left in flight: the last chunk requests nothing
+  if (n_chunks == 0 && has_next_item) resolve_rows(nxt, ent);
+  // the item after the next one (its sequence lookup waits for loads, so it comes before this
+  // item's stores are issued)
+  const int64_t it_nn = it_next + gridDim.x;
+  const Item nn = item_of(it_nn < n_items ? it_nn : it);
+  // the next item's q into the operand registers (this item's last S is done).  Every load is
+  // waited for here, where only the latent-row lookups are still in flight, so that no load
+  // into those registers is pending when the next item's products read them.
+  if (has_next_item) {
+    __builtin_amdgcn_s_waitcnt(0x0070);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = qn[ks];
+  }
 
   // lanes (m, 0) and (m, 1) summed different keys of head h under the same maximum
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -369,7 +445,7 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
     if (a.lse && dh == 0 && g == 0)
       a.lse[i * H + h] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   } else {
-    const int64_t part = (i * a.n_split + sp) * H + h;
+    const int64_t part = (i * a.n_split + cur.sp) * H + h;
     float* po = a.part_o + part * kLatentDim + 256 * dh + 4 * g;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -383,6 +459,25 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
       a.part_ml[2 * part] = l_tot > 0.0f ? m_run : -INFINITY;
       a.part_ml[2 * part + 1] = l_tot;
     }
+  }
+  if (!has_next_item) break;
+
+  // Next item: once every wave is done with this item's slot table and buffers, its latent rows
+  // go into the table, the item after it has its entries and q issued, and its first chunks are
+  // requested.
+  lds_barrier();
+  n_chunks = install(nxt, ent);
+  cur = nxt;
+  it = it_next;
+  it_next = it_nn;
+  nxt = nn;
+  if (it_next < n_items) {
+    load_entries(nxt, ent);
+    load_q(nxt, qn);
+  }
+#pragma unroll
+  for (int c = 0; c < kAttnBufs - 1; ++c)
+    if (c < n_chunks) request(c);
   }
 }
 
@@ -425,9 +520,23 @@ __global__ __launch_bounds__(256) void sparse_attn_merge_kernel(AttnArgs a) {
     a.lse[row] = l > 0.0f ? (mx + log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
+// Compute units of the current device (one workgroup of the attention kernel fits per CU).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
 template <int HW>
 hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
-  const int64_t blocks = a.n_q * a.n_split * (a.n_heads / HW);
+  const int64_t items = a.n_q * a.n_split * (a.n_heads / HW);
+  const int64_t blocks = items < cu_count() ? items : cu_count();
   hipLaunchKernelGGL(sparse_attn_kernel<HW>, dim3(static_cast<uint32_t>(blocks)), dim3(HW * 4), 0,
                      stream, a);
   if (a.n_split > 1) {
@@ -442,7 +551,7 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
 
 // Rows are split when the batch has too few of them to fill the chip (each split keeping at
 // least two 32-key steps) and when a list is longer than one workgroup's slot table.
-void attn_plan(int64_t n_q, int32_t k, int32_t* n_split, int32_t* split_keys) {
+void attn_plan(int64_t n_q, int32_t n_heads, int32_t k, int32_t* n_split, int32_t* split_keys) {
   const int32_t chunks = (k + kAttnChunk - 1) / kAttnChunk;
   int32_t s = 1;
   if (n_q > 0 && n_q < 256) {
@@ -450,7 +559,8 @@ void attn_plan(int64_t n_q, int32_t k, int32_t* n_split, int32_t* split_keys) {
     s = s < chunks / 2 ? s : chunks / 2;
     if (s < 1) s = 1;
   }
-  const int32_t min_s = (chunks * kAttnChunk + kMaxAttnList - 1) / kMaxAttnList;
+  const int32_t max_list = attn_max_list(n_heads);
+  const int32_t min_s = (chunks * kAttnChunk + max_list - 1) / max_list;
   if (s < min_s) s = min_s;
   const int32_t per = (chunks + s - 1) / s;
   *n_split = (chunks + per - 1) / per;
@@ -459,7 +569,7 @@ void attn_plan(int64_t n_q, int32_t k, int32_t* n_split, int32_t* split_keys) {
 
 size_t attn_workspace_bytes(int64_t n_q, int32_t n_heads, int32_t k) {
   int32_t s = 1, per = 0;
-  attn_plan(n_q, k, &s, &per);
+  attn_plan(n_q, n_heads, k, &s, &per);
   if (s <= 1) return 0;
   const size_t parts = static_cast<size_t>(n_q) * s * n_heads;
   return parts * kLatentDim * 4 + parts * 2 * 4;
