@@ -58,8 +58,12 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Sequence b with cu_q[b] <= i < cu_q[b + 1], or -1.
-__device__ __forceinline__ int32_t seq_of_row(const int32_t* cu_q, int32_t n_seq, int64_t i) {
+// Sequence b with cu_q[b] <= i < cu_q[b + 1], or -1.  i is workgroup-uniform and the table
+// read-only, so it is read through the constant address space: scalar loads, which leave the
+// vector memory counter (and the transfers it tracks) alone.
+__device__ __forceinline__ int32_t seq_of_row(const int32_t* cu_q_ptr, int32_t n_seq, int64_t i) {
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const_i32* cu_q = (const_i32*)cu_q_ptr;
   if (n_seq <= 0 || i < cu_q[0] || i >= cu_q[n_seq]) return -1;
   int32_t lo = 0, hi = n_seq;
   while (hi - lo > 1) {
@@ -141,6 +145,8 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   };
   constexpr int kPer = attn_max_list(HW) / NT;   // list entries per thread
   static_assert(kPer == 8, "eight list entries per thread");
+  int32_t ent[kPer];
+  AFrag qf[16], qn[16];
   // list entries of an item (-1 = none), then their latent rows (-1 = none)
   auto load_entries = [&](const Item& t, int32_t (&ent)[kPer]) {
     const int32_t* src = a.idx + t.i * a.k + t.sp * a.split_keys;
@@ -170,16 +176,25 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   };
   // The item's latent rows into the slot table; returns its number of 32-entry chunks, up to the
   // last valid entry.  The caller has made sure no wave still reads the table.
-  auto install = [&](const Item& t, const int32_t (&ent)[kPer]) {
+  // (the wave's maximum of one past its last valid entry is taken first, on its own, so that the
+  // lookups are waited for where nothing else is in flight)
+  auto wave_last = [&](const Item& t, const int32_t (&ent)[kPer]) {
     int last = 0;
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
       const int e = threadIdx.x + p * NT;
-      if (e < ((t.n_list + kAttnChunk - 1) & ~(kAttnChunk - 1))) sl[e] = e < t.n_list ? ent[p] : -1;
       if (e < t.n_list && ent[p] >= 0) last = e + 1;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    return last;
+  };
+  auto install = [&](const Item& t, const int32_t (&ent)[kPer], int last) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int e = threadIdx.x + p * NT;
+      if (e < ((t.n_list + kAttnChunk - 1) & ~(kAttnChunk - 1))) sl[e] = e < t.n_list ? ent[p] : -1;
+    }
     if (lane == 0) last_w[wid] = last;
     lds_barrier();
     int n_used = 0;
@@ -213,21 +228,16 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   int64_t it = blockIdx.x;
   if (it >= n_items) return;
   Item cur = item_of(it);
-  int32_t ent[kPer];
-  AFrag qf[16], qn[16];
   load_entries(cur, ent);
   load_q(cur, qn);
   resolve_rows(cur, ent);
-  int n_chunks = install(cur, ent);
+  int n_chunks = install(cur, ent, wave_last(cur, ent));
   __builtin_amdgcn_s_waitcnt(0x0070);
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) qf[ks] = qn[ks];
   int64_t it_next = it + gridDim.x;
   Item nxt = item_of(it_next < n_items ? it_next : it);
-  if (it_next < n_items) {
-    load_entries(nxt, ent);
-    load_q(nxt, qn);
-  }
+  if (it_next < n_items) load_entries(nxt, ent);
 #pragma unroll
   for (int c = 0; c < kAttnBufs - 1; ++c)
     if (c < n_chunks) request(c);
@@ -333,6 +343,10 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
     // chunk c + 1 has landed in every wave's rows; every wave is done with chunk c - 1, whose
     // buffer chunk c + kAttnBufs - 1 now overwrites
     wait_chunks_left(min(n_chunks - c - 2, kAttnBufs - 3));
+    // the next item's q, at the second step rather than at the item boundary, where every
+    // workgroup (all run the same steps at about the same time) would load it at once; issued
+    // before this step's request, so the counted waits still find the chunks in order
+    if (has_next_item && c == 1) load_q(nxt, qn);
     if (c + kAttnBufs - 1 < n_chunks) request(c + kAttnBufs - 1);
     // last chunk: every request has landed, so the next item's latent rows are looked up now,
     // behind this chunk's softmax and P.V
@@ -413,18 +427,19 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   }
   // no request is left in flight: the last chunk requests nothing
   if (n_chunks == 0 && has_next_item) resolve_rows(nxt, ent);
-  // the item after the next one (its sequence lookup waits for loads, so it comes before this
-  // item's stores are issued)
+  // the item after the next one
   const int64_t it_nn = it_next + gridDim.x;
   const Item nn = item_of(it_nn < n_items ? it_nn : it);
   // the next item's q into the operand registers (this item's last S is done).  Every load is
   // waited for here, where only the latent-row lookups are still in flight, so that no load
   // into those registers is pending when the next item's products read them.
   if (has_next_item) {
+    if (n_chunks < 2) load_q(nxt, qn);                   // the steps did not reach it
     __builtin_amdgcn_s_waitcnt(0x0070);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qf[ks] = qn[ks];
   }
+  const int nx_last = has_next_item ? wave_last(nxt, ent) : 0;
 
   // lanes (m, 0) and (m, 1) summed different keys of head h under the same maximum
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -466,15 +481,12 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   // go into the table, the item after it has its entries and q issued, and its first chunks are
   // requested.
   lds_barrier();
-  n_chunks = install(nxt, ent);
+  n_chunks = install(nxt, ent, nx_last);
   cur = nxt;
   it = it_next;
   it_next = it_nn;
   nxt = nn;
-  if (it_next < n_items) {
-    load_entries(nxt, ent);
-    load_q(nxt, qn);
-  }
+  if (it_next < n_items) load_entries(nxt, ent);
 #pragma unroll
   for (int c = 0; c < kAttnBufs - 1; ++c)
     if (c < n_chunks) request(c);
