@@ -561,15 +561,24 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Rows are split when the batch has too few of them to fill the chip (each split keeping at
-// least two 32-key steps) and when a list is longer than one workgroup's slot table.
+// Rows are split when the batch has too few of them to fill the chip, and when a list is longer
+// than one workgroup's slot table.  More splits shorten each workgroup's run of 32-key steps
+// (about 1.8 us each) but add partial outputs to write and merge (about n_q * H * 4 KB, some
+// 1 us per 1000 (row, head) pairs, per split), so the count balances the two, near
+// sqrt(1765 * chunks / (n_q * H)) (measured on 32 decode rows x 64 heads x 1024 keys: 4 splits
+// 31 us, 8 splits 33 us, 2 splits 41 us), without exceeding the CUs' worth of items or going
+// below two steps per split.
 void attn_plan(int64_t n_q, int32_t n_heads, int32_t k, int32_t* n_split, int32_t* split_keys) {
   const int32_t chunks = (k + kAttnChunk - 1) / kAttnChunk;
   int32_t s = 1;
   if (n_q > 0 && n_q < 256) {
-    s = static_cast<int32_t>((256 + n_q - 1) / n_q);
-    s = s < chunks / 2 ? s : chunks / 2;
-    if (s < 1) s = 1;
+    const int64_t n_hb = n_heads > 64 ? n_heads / 64 : 1;
+    const int64_t fill = (256 + n_q * n_hb - 1) / (n_q * n_hb);
+    const int64_t cost = static_cast<int64_t>(
+        sqrt(1765.0 * chunks / (static_cast<double>(n_q) * (n_heads > 0 ? n_heads : 64))) + 0.5);
+    int64_t t = fill < cost ? fill : cost;
+    t = t < chunks / 2 ? t : chunks / 2;
+    s = t < 1 ? 1 : static_cast<int32_t>(t);
   }
   const int32_t max_list = attn_max_list(n_heads);
   const int32_t min_s = (chunks * kAttnChunk + max_list - 1) / max_list;
