@@ -284,7 +284,8 @@ int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const
  * out      device bf16 [n_q, n_heads, 512], 16-byte aligned; out_lse device fp32 [n_q, n_heads]
  *          or NULL
  * workspace device, at least idx_sparse_attn_workspace_size(n_q, n_heads, k) bytes (0, and
- *          workspace may be NULL, for batches of 256 rows or more)
+ *          workspace may be NULL, when no list is split: batches of 256 rows or more with
+ *          k <= 2048, or k <= 1024 with 32 heads)
  * n_heads is 32, 64 or 128.
  * Errors: IDX_EINVAL (null pointer, misaligned q / kv / out, n_q < 0, n_seq < 1, max_keys < 1,
  * n_slots < 0, k < 1, softmax_scale not finite and positive), IDX_EUNSUPPORTED (n_heads),
