@@ -563,11 +563,10 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t stream) {
 
 // Rows are split when the batch has too few of them to fill the chip, and when a list is longer
 // than one workgroup's slot table.  More splits shorten each workgroup's run of 32-key steps
-// (about 1.8 us each) but add partial outputs to write and merge (about n_q * H * 4 KB, some
-// 1 us per 1000 (row, head) pairs, per split), so the count balances the two, near
-// sqrt(1765 * chunks / (n_q * H)) (measured on 32 decode rows x 64 heads x 1024 keys: 4 splits
-// 31 us, 8 splits 33 us, 2 splits 41 us), without exceeding the CUs' worth of items or going
-// below two steps per split.
+// (about 1.8 us each), but every split adds an item start and a partial output to write and
+// merge.  Measured on 32 decode rows x 64 heads x 1024 keys: 2 splits 41 us, 4 splits 31 us,
+// 5 splits 30.8 us, 8 splits 33 us.  The count is near sqrt(1765 * chunks / (n_q * H)), a fit
+// of those timings, without exceeding the CUs' worth of items or going below two steps per split.
 void attn_plan(int64_t n_q, int32_t n_heads, int32_t k, int32_t* n_split, int32_t* split_keys) {
   const int32_t chunks = (k + kAttnChunk - 1) / kAttnChunk;
   int32_t s = 1;
