@@ -7,8 +7,8 @@
 // Work items are (query row, split of the list, block of HW = min(H, 64) heads); a workgroup of
 // HW / 16 waves, one per CU (its LDS fills the CU), takes items blockIdx.x, blockIdx.x + G, ...
 // (G workgroups), and loads the next item's list entries, latent rows and q while it works on the
-// current one, so only the first item waits for them.  Wave w owns 32 heads of the block, 32 (w / 2) .., and one half of the 512 output dims,
-// 256 (w % 2) ...  Per 32 listed keys:
+// current one, so only the first item waits for them.  Wave w owns 32 heads of the block,
+// 32 (w / 2) .., and one half of the 512 output dims, 256 (w % 2) ...  Per 32 listed keys:
 //   1. the keys' latents go from global memory straight into LDS (global_load_lds_dwordx4: one
 //      instruction per 1 KB latent row, each lane's 16 bytes landing at its own slot), up to three
 //      chunks ahead of their use in four buffers, so no registers or VALU work stage them; the
@@ -273,7 +273,8 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   static_assert(3 * kRowsPerWave < 64, "vmcnt range");
   auto wait_chunks_left = [&](int n) {        // n = 0..2, uniform
     if (n >= 2)
-      __builtin_amdgcn_s_waitcnt(((2 * kRowsPerWave) & 15) | 0x0070 | (((2 * kRowsPerWave) >> 4) << 14));
+      __builtin_amdgcn_s_waitcnt(((2 * kRowsPerWave) & 15) | 0x0070 |
+                                 (((2 * kRowsPerWave) >> 4) << 14));
     else if (n == 1)
       __builtin_amdgcn_s_waitcnt((kRowsPerWave & 15) | 0x0070 | ((kRowsPerWave >> 4) << 14));
     else
@@ -445,16 +446,52 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (a.n_split == 1) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    uint16_t* orow = a.out + (i * H + h) * kLatentDim + 256 * dh + 4 * g;
+    if constexpr (HW == 64) {
+      // The wave's [32 heads x 256 dims] bf16 output goes through LDS so that every store writes
+      // whole 512-byte row segments: from the accumulators, lane (m, g) holds 8-byte units
+      // u = 8 t + 2 j + g (dims 4 u ..) of head m, and a direct store would touch 32 rows per
+      // instruction.  The tile sits in one half of a chunk buffer the last step no longer uses
+      // (chunks n - 2 and n - 3 are done once the last step's barrier is passed, and nothing is
+      // requested after chunk n - 1), head m's row at 512 m, unit u at 8 (u ^ m), so the 32 heads
+      // of one write land in distinct banks.  Each wave reads back only its own tile.  (Two-wave
+      // workgroups, for 32 heads, store directly: their registers have no room for the staging.)
+      uint8_t* stg = kbuf[(n_chunks + 1 + (wid >> 1)) % kAttnBufs] + (wid & 1) * (kChunkBytes / 2);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 8; ++t) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 v;
-        v.x = bf16_rne_bits(oacc[t][4 * j] * inv) | (bf16_rne_bits(oacc[t][4 * j + 1] * inv) << 16);
-        v.y = bf16_rne_bits(oacc[t][4 * j + 2] * inv) |
-              (bf16_rne_bits(oacc[t][4 * j + 3] * inv) << 16);
-        *reinterpret_cast<u32x2*>(orow + 32 * t + 8 * j) = v;
+        for (int j = 0; j < 4; ++j) {
+          u32x2 v;
+          v.x = bf16_rne_bits(oacc[t][4 * j] * inv) |
+                (bf16_rne_bits(oacc[t][4 * j + 1] * inv) << 16);
+          v.y = bf16_rne_bits(oacc[t][4 * j + 2] * inv) |
+                (bf16_rne_bits(oacc[t][4 * j + 3] * inv) << 16);
+          const int u = 8 * t + 2 * j + g;
+          *reinterpret_cast<u32x2*>(stg + 512 * m + 8 * (u ^ m)) = v;
+        }
+      }
+      // read back: lane L takes head 2 s + L / 32 and its 16-byte piece p = L % 32 (units 2 p and
+      // 2 p + 1, found at chunk p ^ (head / 2), in swapped order when the head is odd)
+      uint16_t* obase = a.out + (i * H + HW * cur.hb + 32 * hg) * kLatentDim + 256 * dh;
+#pragma unroll 4
+      for (int st = 0; st < 16; ++st) {
+        const int hh = 2 * st + g, pc = m;
+        u32x4 v = *reinterpret_cast<const u32x4*>(stg + 512 * hh + 16 * (pc ^ (hh >> 1)));
+        if (hh & 1) v = u32x4{v.z, v.w, v.x, v.y};
+        *reinterpret_cast<u32x4*>(obase + hh * kLatentDim + 8 * pc) = v;
+      }
+    } else {
+      uint16_t* orow = a.out + (i * H + h) * kLatentDim + 256 * dh + 4 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x2 v;
+          v.x = bf16_rne_bits(oacc[t][4 * j] * inv) |
+                (bf16_rne_bits(oacc[t][4 * j + 1] * inv) << 16);
+          v.y = bf16_rne_bits(oacc[t][4 * j + 2] * inv) |
+                (bf16_rne_bits(oacc[t][4 * j + 3] * inv) << 16);
+          *reinterpret_cast<u32x2*>(orow + 32 * t + 8 * j) = v;
+        }
       }
     }
     if (a.lse && dh == 0 && g == 0)
