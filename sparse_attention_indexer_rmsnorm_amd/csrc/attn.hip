@@ -115,7 +115,7 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   constexpr int kRowsPerWave = kAttnChunk / NW;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kAttnBufs][kChunkBytes];   // latents
   __shared__ __attribute__((aligned(16))) float ex[NW * 16 * 64];         // S^T partial sums
-  __shared__ int32_t sl[kMaxAttnList];        // latent row of each list entry, -1 = none
+  __shared__ __attribute__((aligned(16))) int32_t sl[kMaxAttnList];   // latent row per entry, -1 none
   __shared__ int32_t last_w[NW];              // per wave: one past its last valid entry
 
   const int lane = threadIdx.x & 63;
@@ -207,16 +207,25 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
   //    logical chunk L ^ sw(r) of its row, which then lands at physical chunk L.  An entry with
   //    no latent reads row 0 (some row is valid when a chunk is requested); its score is masked,
   //    and its weight 0 times finite latents adds nothing.
+  //    The wave's row entries are read from the slot table together (16-byte reads), so the
+  //    transfers do not each wait for an LDS round trip.
+  const uint32_t kbuf_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)&kbuf[0][0]));
   auto request = [&](int c) {
-    uint8_t* dst = kbuf[c % kAttnBufs];
+    int32_t slot[kRowsPerWave];
+#pragma unroll
+    for (int q4 = 0; q4 < kRowsPerWave / 4; ++q4) {
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(&sl[c * kAttnChunk + wid * kRowsPerWave + 4 * q4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) slot[4 * q4 + e] = static_cast<int32_t>(v[e]);
+    }
+    const uint32_t buf = kbuf_lds + static_cast<uint32_t>(c % kAttnBufs) * kChunkBytes;
 #pragma unroll
     for (int rr = 0; rr < kRowsPerWave; ++rr) {
       const int r = wid * kRowsPerWave + rr;
-      const int32_t slot = max(sl[c * kAttnChunk + r], 0);
-      const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-          (__attribute__((address_space(3))) uint8_t*)(dst + r * kRowBytes)));
-      dma_row16(a.kv + static_cast<int64_t>(slot) * kLatentDim + 8 * (lane ^ sw(r)),
-                __builtin_amdgcn_readfirstlane(lds));
+      dma_row16(a.kv + static_cast<int64_t>(max(slot[rr], 0)) * kLatentDim + 8 * (lane ^ sw(r)),
+                __builtin_amdgcn_readfirstlane(buf + r * kRowBytes));
     }
   };
 
