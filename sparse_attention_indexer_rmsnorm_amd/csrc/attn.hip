@@ -507,13 +507,40 @@ __global__ __launch_bounds__(HW * 4) void sparse_attn_kernel(AttnArgs a) {
       a.lse[i * H + h] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   } else {
     const int64_t part = (i * a.n_split + cur.sp) * H + h;
-    float* po = a.part_o + part * kLatentDim + 256 * dh + 4 * g;
+    if constexpr (HW == 64) {
+      // Staged like the bf16 output, so each store writes a whole 1 KB row: once every wave is
+      // past its last chunk all four buffers are free, and wave w's [32 heads x 256 dims] fp32
+      // tile goes into buffer w, head m's row at 1024 m and its 16-byte unit u (dims 4 u ..) at
+      // 16 (u ^ m) (16 consecutive heads of one write on distinct banks).
+      lds_barrier();
+      uint8_t* stg = kbuf[wid];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 8; ++t) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        floatx4 v = {oacc[t][4 * j], oacc[t][4 * j + 1], oacc[t][4 * j + 2], oacc[t][4 * j + 3]};
-        *reinterpret_cast<floatx4*>(po + 32 * t + 8 * j) = v;
+        for (int j = 0; j < 4; ++j) {
+          const floatx4 v = {oacc[t][4 * j], oacc[t][4 * j + 1], oacc[t][4 * j + 2],
+                             oacc[t][4 * j + 3]};
+          const int u = 8 * t + 2 * j + g;
+          *reinterpret_cast<floatx4*>(stg + 1024 * m + 16 * (u ^ m)) = v;
+        }
+      }
+      float* pbase = a.part_o +
+                     ((i * a.n_split + cur.sp) * H + HW * cur.hb + 32 * hg) * kLatentDim + 256 * dh;
+#pragma unroll 4
+      for (int hh = 0; hh < 32; ++hh) {
+        const floatx4 v = *reinterpret_cast<const floatx4*>(stg + 1024 * hh + 16 * (lane ^ hh));
+        *reinterpret_cast<floatx4*>(pbase + hh * kLatentDim + 4 * lane) = v;
+      }
+    } else {
+      float* po = a.part_o + part * kLatentDim + 256 * dh + 4 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const floatx4 v = {oacc[t][4 * j], oacc[t][4 * j + 1], oacc[t][4 * j + 2],
+                             oacc[t][4 * j + 3]};
+          *reinterpret_cast<floatx4*>(po + 32 * t + 8 * j) = v;
+        }
       }
     }
     if (dh == 0 && g == 0) {
