@@ -574,25 +574,32 @@ __global__ __launch_bounds__(256) void sparse_attn_merge_kernel(AttnArgs a) {
   if (row >= a.n_q * H) return;
   const int64_t i = row / H;
   const int h = static_cast<int>(row - i * H);
+  // one pass with a running maximum (rescaling when it moves), so the loads of several splits
+  // are in flight together
   float mx = -INFINITY;
-  for (int sp = 0; sp < a.n_split; ++sp)
-    mx = fmaxf(mx, a.part_ml[2 * ((i * a.n_split + sp) * H + h)]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float l = 0.0f;
-  if (mx != -INFINITY) {
-    for (int sp = 0; sp < a.n_split; ++sp) {
-      const int64_t part = (i * a.n_split + sp) * H + h;
-      const float ms = a.part_ml[2 * part];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - mx);
-      l += wgt * a.part_ml[2 * part + 1];
-      const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + part * kLatentDim + 8 * lane);
-      const floatx4 v0 = po[0], v1 = po[1];
+#pragma unroll 4
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const int64_t part = (i * a.n_split + sp) * H + h;
+    const float ms = a.part_ml[2 * part];
+    const float ls = a.part_ml[2 * part + 1];
+    const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + part * kLatentDim + 8 * lane);
+    const floatx4 v0 = po[0], v1 = po[1];
+    if (ms == -INFINITY) continue;
+    if (ms > mx) {
+      const float r = exp2f(mx - ms);     // 0 for the first split with keys
+      l *= r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += wgt * v0[e];
-        acc[4 + e] += wgt * v1[e];
-      }
+      for (int e = 0; e < 8; ++e) acc[e] *= r;
+      mx = ms;
+    }
+    const float wgt = exp2f(ms - mx);
+    l += wgt * ls;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += wgt * v0[e];
+      acc[4 + e] += wgt * v1[e];
     }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
