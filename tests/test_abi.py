@@ -137,10 +137,15 @@ def test_topk_rows_validation(L):
 
 
 def test_sparse_attn_workspace_and_validation(L):
-    # few rows split their lists: 32 rows x 1024 entries -> 8 splits of 128 entries, each
-    # keeping a 512-dim fp32 partial and (max, sum) per head
-    assert L.idx_sparse_attn_workspace_size(32, 64, 1024) == 32 * 8 * 64 * (512 * 4 + 8)
+    # few rows split their lists: 32 rows x 1024 entries x 64 heads -> 5 splits (224 entries
+    # each, the last 128), each keeping a 512-dim fp32 partial and (max, sum) per head
+    part = 64 * (512 * 4 + 8)
+    assert L.idx_sparse_attn_workspace_size(32, 64, 1024) == 32 * 5 * part
     assert L.idx_sparse_attn_workspace_size(256, 64, 512) == 0      # enough rows: no split
+    # lists longer than one workgroup's slot table (2048 entries, 1024 with 32 heads) are split
+    assert L.idx_sparse_attn_workspace_size(300, 64, 3000) == 300 * 2 * part
+    assert L.idx_sparse_attn_workspace_size(300, 64, 1500) == 0
+    assert L.idx_sparse_attn_workspace_size(300, 32, 1500) == 300 * 2 * 32 * (512 * 4 + 8)
     assert L.idx_sparse_attn_workspace_size(8192, 128, 512) == 0
     assert L.idx_sparse_attn_workspace_size(32, 48, 1024) == 0      # unsupported head count
     F = ctypes.c_void_p(0x1000)
