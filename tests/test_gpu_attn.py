@@ -186,3 +186,22 @@ def test_attn_repeatable():
     g1, l1 = _run_gpu(a, wl.cu_q)
     g2, l2 = _run_gpu(a, wl.cu_q)
     assert np.array_equal(g1, g2) and np.array_equal(l1, l2)
+
+
+def test_attn_split_lists_with_empty_splits(oracle_mod):
+    """Few rows, so every list is split and merged: the first half of each list is padding, so the
+    first splits hold no key (the merge starts from the later ones), some rows hold nothing at all,
+    and one row's only valid entries sit in its last split."""
+    wl = workload(4)                                   # 32 decode rows, 1024 listed keys
+    a = W.attn_inputs(wl)
+    assert ix.sparse_attn_workspace_size(wl.n_q, 64, a.idx.shape[1]) > 0, "lists must be split"
+    idx = a.idx.copy()
+    k = idx.shape[1]
+    idx[:, : k // 2] = -1
+    idx[3, :] = -1                                     # nothing listed
+    idx[7, :] = -1
+    idx[7, -3:] = a.idx[7, -3:]                        # three keys, all in the last split
+    a = W.AttnInputs(a.q_bits, a.kv_bits, a.kv_slot, idx, a.scale)
+    g_out, g_lse = _run_gpu(a, wl.cu_q)
+    assert np.isneginf(g_lse[3]).all() and np.all(g_out[3] == 0)
+    _check(a, wl.cu_q, g_out, g_lse, np.arange(wl.n_q, dtype=np.int64), oracle_mod, "empty splits")
