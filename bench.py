@@ -84,7 +84,11 @@ def committed_traffic(kernel: str, workload: str):
 
 
 def _pairs(wl) -> int:
-    t = wl.query_positions()
+    """(query, visible key) pairs of a batch: the queries of sequence b are its last q_len_b
+    tokens, and the query at token t sees floor((t + 1) / 4) compressed keys."""
+    t = np.concatenate([int(L) - int(ql) + np.arange(int(ql), dtype=np.int64)
+                        for L, ql in zip(wl.seq_lens, wl.q_lens)]) if wl.n_q else \
+        np.zeros(0, np.int64)
     nv = np.minimum((t + 1) // 4, wl.max_keys)
     nv[t < 0] = 0
     return int(nv.sum()), nv
@@ -323,7 +327,7 @@ def main() -> int:
 
     import torch  # noqa: PLC0415
     import sparse_attention_indexer_rmsnorm_amd as ix  # noqa: PLC0415
-    from sparse_attention_indexer_rmsnorm_amd import workloads as W  # noqa: PLC0415
+    import workloads as W  # noqa: PLC0415
 
     if args.ceilings:
         return ceilings(args, torch)

@@ -68,18 +68,19 @@ WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k) {
   return L;
 }
 
-// A bound on workspace_layout(rows).total that never decreases with `rows` (fewer rows may be
-// selected in more segments, so the exact size is not monotone): every row reserves the
-// candidate space of a single-row chunk.
+// A bound on workspace_layout(n).total for every n <= rows that never decreases with `rows`:
+// the exact size is not monotone (a batch of few rows is selected by one workgroup per row with
+// no candidates, more rows in segments with candidate buffers), so every row reserves the widest
+// candidate row any batch shape can need, and the alignment slack of each region is counted.
 size_t workspace_upper(int64_t rows, int32_t max_pages, int32_t k) {
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
-  const size_t cand_row = topk_workspace_bytes(1, static_cast<int64_t>(cols), k);
-  return static_cast<size_t>(rows) * (cols * sizeof(float) + sizeof(int32_t) + cand_row) +
-         3 * kAlign;
+  const size_t cand = static_cast<size_t>(topk_cand_bound(static_cast<int64_t>(cols), k));
+  return static_cast<size_t>(rows) * (sizeof(int32_t) + cols * sizeof(float) + 2 * cand * 8) +
+         4 * kAlign;
 }
 
 // Query rows per chunk for a workspace of `bytes`: all of them if they fit, else the largest
-// count whose upper bound fits.
+// count whose upper bound fits, so that every chunk (the last one has fewer rows) fits too.
 int64_t rows_fitting(size_t bytes, int32_t max_pages, int32_t k, int64_t n_q) {
   if (workspace_layout(n_q, max_pages, k).total <= bytes) return n_q;
   int64_t lo = 0, hi = n_q;
@@ -279,6 +280,28 @@ size_t idx_logits_topk_workspace_size(int64_t n_q, int32_t n_seq, int32_t max_pa
 size_t idx_logits_topk_min_workspace(int32_t n_seq, int32_t max_pages, int32_t k) {
   (void)n_seq;
   return workspace_upper(1, max_pages < 0 ? 0 : max_pages, k < 1 ? 1 : k);
+}
+
+int idx_logits_topk_plan(int64_t n_q, int32_t max_pages, int32_t k, size_t workspace_bytes,
+                         int64_t* rows_per_chunk, size_t* max_chunk_bytes) {
+  if (n_q < 1 || max_pages < 0 || k < 1 || k > IDX_MAX_TOPK || !rows_per_chunk ||
+      !max_chunk_bytes)
+    return IDX_EINVAL;
+  if (n_q > INT32_MAX || static_cast<int64_t>(max_pages) * IDX_PAGE_KEYS > INT32_MAX / 2)
+    return IDX_EINVAL;
+  const int64_t rows = rows_fitting(workspace_bytes, max_pages, k, n_q);
+  *rows_per_chunk = rows;
+  *max_chunk_bytes = 0;
+  if (rows < 1) return IDX_EWORKSPACE;
+  // every chunk has `rows` rows except the last, which has the remainder
+  size_t most = workspace_layout(rows, max_pages, k).total;
+  const int64_t tail = n_q % rows;
+  if (tail > 0) {
+    const size_t t = workspace_layout(tail, max_pages, k).total;
+    most = t > most ? t : most;
+  }
+  *max_chunk_bytes = most;
+  return IDX_OK;
 }
 
 int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype,

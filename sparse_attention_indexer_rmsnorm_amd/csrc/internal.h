@@ -104,6 +104,9 @@ struct TopkPlan {
 TopkPlan topk_plan(int64_t n_rows, int64_t cols, int32_t k);
 // Workspace the selection of n_rows rows of `cols` scores needs (0 for one pass).
 size_t topk_workspace_bytes(int64_t n_rows, int64_t cols, int32_t k);
+// Widest candidate row any batch of rows of `cols` scores can need, whatever its row count:
+// topk_workspace_bytes(n, cols, k) <= 2 * (n * topk_cand_bound(cols, k) * 8 + 256) for every n.
+int64_t topk_cand_bound(int64_t cols, int32_t k);
 // Top-k of every row (ties to the lower index, output sorted by index, -1 / -inf padding).
 hipError_t run_topk(const float* scores, int64_t row_stride, const int32_t* row_len,
                     int64_t n_rows, int32_t k, int32_t* out_idx, float* out_val, void* ws,

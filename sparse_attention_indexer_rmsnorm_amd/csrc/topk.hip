@@ -1036,6 +1036,19 @@ TopkPlan topk_plan(int64_t n_rows, int64_t cols, int32_t k) {
   return p;
 }
 
+int64_t topk_cand_bound(int64_t cols, int32_t k) {
+  // The first pass cuts a row into at most max(need, min(fit, usable)) segments (the wave
+  // spread only lowers the count as rows grow); each later pass's candidate row is no wider,
+  // because ceil(ns * k / kMaxSegment) <= ns for k <= kMaxSegment.
+  const int64_t need = (cols + kMaxSegment - 1) / kMaxSegment;
+  int64_t want = kMaxSegment / k;
+  const int64_t usable = cols / (2 * static_cast<int64_t>(k));
+  if (want > usable) want = usable;
+  int64_t ns = need > want ? need : want;
+  if (ns <= 1) return 0;
+  return ns * k;
+}
+
 size_t topk_workspace_bytes(int64_t n_rows, int64_t cols, int32_t k) {
   const TopkPlan p = topk_plan(n_rows, cols, k);
   if (p.passes <= 1) return 0;

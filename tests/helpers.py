@@ -8,7 +8,7 @@ import os
 import numpy as np
 import torch
 
-from sparse_attention_indexer_rmsnorm_amd import workloads as W
+import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
@@ -22,6 +22,17 @@ def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", text)))
+
+
+def query_positions(wl) -> np.ndarray:
+    """Token position t of every query row: the queries of sequence b are its last q_len_b
+    tokens, t = L_b - q_len_b + i."""
+    t = np.empty(wl.n_q, dtype=np.int64)
+    cu = wl.cu_q
+    for b in range(wl.n_seq):
+        ql = int(wl.q_lens[b])
+        t[cu[b]:cu[b + 1]] = int(wl.seq_lens[b]) - ql + np.arange(ql)
+    return t
 
 
 @functools.lru_cache(maxsize=None)

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), f"missing export {n}"
     assert sorted(n for n, _, _ in ix.SIGNATURES) == names
@@ -63,6 +63,31 @@ def test_workspace_sizes(L):
     assert L.idx_topk_rows_workspace_size(8192, 5632, 512) == 0
     assert L.idx_topk_rows_workspace_size(32, 32768, 1024) == 0     # one workgroup per row
     assert L.idx_topk_rows_workspace_size(32, 40000, 1024) > 0      # longer than a workgroup
+
+
+def test_chunk_plan_fits_workspace(L):
+    """Every query chunk of idx_logits_topk fits the workspace it is given: the planner's row
+    bound must cover the segmented selection's candidate buffers, which a batch of more than 128
+    long rows needs even where a single row is selected with none."""
+    for max_pages in (97, 128, 192, 256, 384, 512, 640):      # 6208 .. 40960 key columns
+        for k in (512, 1024, 2048):
+            mins = ix.min_workspace(1, max_pages, k)
+            for n_q in (1, 2, 128, 129, 200, 517, 1000, 4096, 8192):
+                rec = ix.workspace_size(n_q, 1, max_pages, k)
+                budgets = {rec, mins, mins + 12345, 4 << 20, 8 << 20, 11 << 20, 64 << 20,
+                           rec // 3, rec - 1}
+                for b in sorted(budgets):
+                    if b < mins:
+                        continue
+                    rows, most = ix.topk_plan(n_q, max_pages, k, b)
+                    assert 1 <= rows <= n_q, (max_pages, k, n_q, b, rows)
+                    assert most <= b, (max_pages, k, n_q, b, rows, most)
+                rows, _ = ix.topk_plan(n_q, max_pages, k, rec)
+                assert rows == n_q or rec <= 256 << 20 + 4096, (max_pages, k, n_q, rec)
+    # too small for a single row
+    with pytest.raises(ix.IndexerError):
+        ix.topk_plan(10, 88, 512, 100)
+    assert L.idx_logits_topk_plan(0, 88, 512, 1 << 20, FAKE, FAKE) == E_INVAL
 
 
 def _store(L, **kw):

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import sparse_attention_indexer_rmsnorm_amd as ix
-from sparse_attention_indexer_rmsnorm_amd import workloads as W
+import workloads as W
 from tests.helpers import (check_logits, check_topk_sets, dev_inputs, gpu_store, oracle_rows,
                            workload)
 

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import sparse_attention_indexer_rmsnorm_amd as ix
-from sparse_attention_indexer_rmsnorm_amd import workloads as W
+import workloads as W
 from tests.helpers import by_index, check_logits, check_topk_sets, dev_inputs, gpu_store, workload
 
 pytestmark = pytest.mark.gpu

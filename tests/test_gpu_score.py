@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import sparse_attention_indexer_rmsnorm_amd as ix
-from sparse_attention_indexer_rmsnorm_amd import workloads as W
+import workloads as W
 from tests.helpers import check_logits, dev_inputs, oracle_rows, workload
 
 pytestmark = pytest.mark.gpu

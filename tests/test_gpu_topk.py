@@ -14,8 +14,9 @@ import pytest
 import torch
 
 import sparse_attention_indexer_rmsnorm_amd as ix
-from sparse_attention_indexer_rmsnorm_amd import workloads as W
-from tests.helpers import by_index, check_topk_sets, dev_inputs, gpu_store, oracle_rows, workload
+import workloads as W
+from tests.helpers import (by_index, check_topk_sets, dev_inputs, gpu_store, oracle_rows,
+                           query_positions, workload)
 
 pytestmark = pytest.mark.gpu
 FP8, BF16 = W.FP8, W.BF16
@@ -175,10 +176,39 @@ def test_decode_selection_matches_dense_then_select(dtype, k):
     gi, gv = _gpu_topk(wl, d, pool, dtype, want_values=True)
     dense = ix.logits_dense(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
                             d["cu_q"], wl.max_keys)
-    t = wl.query_positions()
+    t = query_positions(wl)
     nv = torch.from_numpy(np.minimum((t + 1) // 4, wl.max_keys).astype(np.int32)).cuda()
     si, sv = ix.topk_rows(dense, wl.k, nv)
     gi, gv = by_index(gi, gv)
     si, sv = by_index(si, sv)
     assert torch.equal(gi, si)
     assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
+
+
+@pytest.mark.parametrize("budget", ["min", 4 << 20, 11 << 20, "recommended"])
+def test_workspace_guard_bytes(budget):
+    """More than 128 rows of more than 6144 keys go through the segmented selection, whose
+    candidate buffers a one-row chunk does not need: however the workspace budget cuts the
+    batch into chunks, nothing is written outside it, and the selection equals the one made
+    with a workspace for the whole batch in one pass."""
+    wl = W.make_workload("guard", 909, [4 * 7100], [300], 512, permute_pages=True)
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, BF16, d)
+    full, _ = _gpu_topk(wl, d, pool, BF16)
+    if budget == "min":
+        nbytes = ix.min_workspace(wl.n_seq, wl.max_pages, wl.k)
+    elif budget == "recommended":
+        nbytes = ix.workspace_size(wl.n_q, wl.n_seq, wl.max_pages, wl.k)
+    else:
+        nbytes = budget
+    rows, most = ix.topk_plan(wl.n_q, wl.max_pages, wl.k, nbytes)
+    print(f"guard budget={nbytes} rows/chunk={rows} most={most}", flush=True)
+    assert most <= nbytes
+    guard = 1 << 16
+    buf = torch.full((nbytes + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = buf[guard:guard + nbytes]
+    part, _ = _gpu_topk(wl, d, pool, BF16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:guard] == 0x5A), "bytes written before the workspace"
+    assert torch.all(buf[guard + nbytes:] == 0x5A), "bytes written after the workspace"
+    assert torch.equal(by_index(full), by_index(part))

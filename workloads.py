@@ -1,6 +1,7 @@
 """Seeded synthetic inputs for the DSA indexer hot path (store -> score -> top-k).
 
-This module draws random numbers and builds integer structure only: sequence lengths, query
+Harness code, outside the library: the tests, the benchmark and the smoke check draw their inputs
+here.  It draws random numbers and builds integer structure only: sequence lengths, query
 counts, page tables and needle positions.  None of the indexer's arithmetic (normalisation, rotary
 embedding, quantisation, scoring, selection) lives here, so the kernels and the CPU oracle can both
 consume these arrays without sharing any of the method's code.
@@ -102,15 +103,6 @@ class Workload:
     def cu_q(self) -> np.ndarray:
         return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
 
-    def query_positions(self) -> np.ndarray:
-        """Token position t of every query row (integer bookkeeping only)."""
-        t = np.empty(self.n_q, dtype=np.int64)
-        cu = self.cu_q
-        for b in range(self.n_seq):
-            ql = int(self.q_lens[b])
-            t[cu[b]:cu[b + 1]] = int(self.seq_lens[b]) - ql + np.arange(ql)
-        return t
-
     def q_torch(self) -> torch.Tensor:
         return torch.from_numpy(self.q_bits.view(np.int16)).view(torch.bfloat16)
 
@@ -168,11 +160,12 @@ def make_workload(name: str, seed: int, seq_lens, q_lens, k: int, *, permute_pag
 
 
 def draw_needles(wl: Workload, per_seq: int, s_hi: Optional[int] = None) -> dict:
-    """Choose needle positions: for each needle, a query row of its sequence and a key s that the
-    query sees, without replacement within the sequence.  Returns integer arrays plus the N(0, 0.1)
-    noise each needle adds; the needle vectors themselves are built by the test harness."""
+    """Choose needle positions: for each needle, a query row of its sequence and a key index s
+    below s_hi (default: every stored key of the sequence, which a decode query at the last token
+    sees), without replacement within the sequence.  The caller picks s_hi so that every query of
+    the sequence sees the needle.  Returns integer arrays plus the N(0, 0.1) noise each needle
+    adds; the needle vectors themselves are built by the test harness."""
     g_pos, g_noise, g_q = rng(wl.seed, T_NEEDLE_POS), rng(wl.seed, T_NEEDLE_NOISE), rng(wl.seed, T_NEEDLE_Q)
-    t_all = wl.query_positions()
     cu = wl.cu_q
     seq, qrow, s_arr, krow = [], [], [], []
     key_base = np.concatenate([[0], np.cumsum(np.bincount(wl.key_seq, minlength=wl.n_seq))])
@@ -181,9 +174,8 @@ def draw_needles(wl: Workload, per_seq: int, s_hi: Optional[int] = None) -> dict
         if ql == 0:
             continue
         rows = cu[b] + g_q.integers(0, ql, size=per_seq)
-        n_vis_min = min(int((t_all[r] + 1) // COMPRESS) for r in rows)
-        hi = n_vis_min if s_hi is None else min(s_hi, n_vis_min)
-        hi = min(hi, int(key_base[b + 1] - key_base[b]))
+        hi = int(key_base[b + 1] - key_base[b])
+        hi = hi if s_hi is None else min(s_hi, hi)
         ss = g_pos.choice(hi, size=per_seq, replace=False)
         for r, s in zip(rows, ss):
             seq.append(b)
@@ -274,14 +266,6 @@ class AttnInputs:
                 torch.from_numpy(self.idx).to(device))
 
 
-def visible_counts(wl: Workload) -> np.ndarray:
-    """Visible compressed keys of every query row: floor((t + 1) / 4), capped at max_keys."""
-    t = wl.query_positions()
-    nv = np.minimum((t + 1) // COMPRESS, wl.max_keys)
-    nv[t < 0] = 0
-    return nv.astype(np.int64)
-
-
 def _bf16_normal_rows(g: np.random.Generator, n: int, width: int, chunk: int = 1 << 16):
     out = np.empty((n, width), np.uint16)
     for r0 in range(0, n, chunk):
@@ -293,9 +277,10 @@ def _bf16_normal_rows(g: np.random.Generator, n: int, width: int, chunk: int = 1
 def attn_inputs(wl: Workload, n_heads: int = 64, k: Optional[int] = None,
                 scale: Optional[float] = None) -> AttnInputs:
     """q and the latents ~ N(0, 1) rounded to bf16; one latent row per (sequence, key), on a
-    random permutation of the rows; per query row a random subset of min(k, visible) of its
-    visible keys in random order, then -1 padding (the shape of a top-k list, whose order is
-    unspecified); softmax scale 1 / sqrt(512) unless given."""
+    random permutation of the rows; per query row a random subset of min(k, n) of the n keys
+    stored for its sequence, in random order, then -1 padding (the shape of a top-k list, whose
+    order is unspecified; the attention reads whatever keys a list names); softmax scale
+    1 / sqrt(512) unless given."""
     k = wl.k if k is None else int(k)
     n_seq, max_keys = wl.n_seq, wl.max_keys
     q = _bf16_normal_rows(rng(wl.seed, T_ATTN_Q), wl.n_q * n_heads, LATENT_DIM)
@@ -303,12 +288,14 @@ def attn_inputs(wl: Workload, n_heads: int = 64, k: Optional[int] = None,
     kv = _bf16_normal_rows(rng(wl.seed, T_ATTN_KV), n_slots, LATENT_DIM)
     kv_slot = rng(wl.seed, T_ATTN_SLOT).permutation(n_slots).astype(np.int32).reshape(
         n_seq, max_keys)
-    nv = visible_counts(wl)
+    n_stored = np.bincount(wl.key_seq, minlength=n_seq)
+    row_seq = np.repeat(np.arange(n_seq), wl.q_lens)
     g = rng(wl.seed, T_ATTN_SEL)
     idx = np.full((wl.n_q, k), -1, np.int32)
     for r in range(wl.n_q):
-        m = int(min(k, nv[r]))
+        n = int(n_stored[row_seq[r]])
+        m = min(k, n)
         if m:
-            idx[r, :m] = g.permutation(int(nv[r]))[:m]
+            idx[r, :m] = g.permutation(n)[:m]
     return AttnInputs(q_bits=q.reshape(wl.n_q, n_heads, LATENT_DIM), kv_bits=kv, kv_slot=kv_slot,
                       idx=idx, scale=LATENT_DIM ** -0.5 if scale is None else float(scale))
