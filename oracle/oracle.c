@@ -231,7 +231,8 @@ static void canonical_key(const float* x, const float* gamma, float eps, int32_t
     double ss = 0.0;
     int n_norm = (g_mutation == 3) ? 64 : OR_D;  /* planted: mean over half the dims */
     for (int i = 0; i < n_norm; i++) ss += (double)x[i] * (double)x[i];
-    double r = 1.0 / sqrt(ss / (double)n_norm + (double)eps);
+    double r = (g_mutation == 27) ? 1.0 / (sqrt(ss / (double)n_norm) + (double)eps)  /* planted */
+                                  : 1.0 / sqrt(ss / (double)n_norm + (double)eps);
     for (int i = 0; i < OR_D; i++) {
         double g = (g_mutation == 4) ? 1.0 : (double)gamma[i];   /* planted: gamma dropped */
         y[i] = (double)x[i] * r * g;
@@ -310,7 +311,9 @@ int64_t oracle_store_keys(const float* x, const float* gamma, float eps, const i
             float scale = (float)(amax / fmax_code);
             for (int i = 0; i < OR_D; i++) {
                 uint8_t c = 0;
-                if (scale > 0.0f) c = oracle_e4m3_encode((float)((double)k32[i] / (double)scale));
+                if (scale > 0.0f)
+                    c = oracle_e4m3_encode((g_mutation == 26) ? k32[i] * (1.0f / scale)  /* planted */
+                                                              : (float)((double)k32[i] / (double)scale));
                 pg[slot * OR_D + i] = c;
             }
             memcpy(pg + OR_PAGE * OR_D + slot * 4, &scale, 4);

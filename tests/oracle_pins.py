@@ -252,6 +252,95 @@ def pin_fp8_store_scale_and_bound():
         assert np.array_equal(np.signbit(deq) | (deq == 0), np.signbit(k32[i]) | (deq == 0))
 
 
+# eps = 2^80 swamps the mean square of any row with |x| < 2^12 (half an fp64 ulp of 2^80 is
+# 2^27), so 1 / sqrt(ms + eps) = 2^-40 exactly; gamma = 2^40 undoes it and position 0 rotates by
+# nothing: the canonical key is x itself, bit for bit.  With eps outside the root the factor would
+# be 2^-80 instead.
+_EPS_HUGE, _GAMMA_HUGE = 2.0 ** 80, np.full(D, 2.0 ** 40, np.float32)
+
+
+def _store_rows_pos0(x, dtype):
+    """Store each row of x at key index 0 of its own sequence (position 0, no rotation) with the
+    eps / gamma pair above; returns (pool, k32, page_table)."""
+    n = x.shape[0]
+    pt = np.arange(n, dtype=np.int32)[:, None]
+    pool = oracle.new_pool(n, dtype)
+    skipped, k32 = oracle.store_keys(x, _GAMMA_HUGE, _EPS_HUGE, np.zeros(n, np.int32),
+                                     np.arange(n, dtype=np.int32), pt, dtype, pool, want_k32=True)
+    assert skipped == 0
+    return pool, k32, pt
+
+
+def pin_rmsnorm_eps_placement():
+    """eps sits inside the square root, 1 / sqrt(mean(x^2) + eps), in two closed forms."""
+    r = _rng(60)
+    # (1) eps comparable to the mean square: x = c * ones with c = 2^-3 has mean square c^2, and
+    # eps = 3 c^2 makes the factor 1 / sqrt(4 c^2) = 1 / (2c) = 4, so the key is gamma / 2.
+    g = (1 + 0.1 * r.standard_normal(D)).astype(np.float32)
+    x = np.full((3, D), 0.125, np.float32)
+    x[1] *= -1.0
+    x[2, ::2] *= -1.0                      # signs do not change the mean square
+    _, k32, _ = _store_rows(x, np.zeros(3, np.int32), gamma=g, eps=3.0 / 64.0)
+    assert np.array_equal(k32, np.sign(x) * (g / 2)), "eps must enter under the square root"
+    # (2) eps = 2^80 with gamma = 2^40 returns x unchanged
+    x = (r.standard_normal((5, D)) * 2.0 ** r.integers(-20, 10, (5, 1))).astype(np.float32)
+    _, k32, _ = _store_rows_pos0(x, BF16)
+    assert np.array_equal(k32, x)
+
+
+def _e4m3_positive_midpoints():
+    """Midpoints between adjacent non-negative e4m3 values (by torch's decoding), and the values."""
+    vals = np.unique(_torch_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8)))
+    return (vals[:-1] + vals[1:]) / 2.0, vals
+
+
+def pin_fp8_store_bytes():
+    """fp8 store bytes rebuilt in numpy and torch from the canonical keys: the scale is numpy's
+    correctly rounded fp32 division absmax / 448, the codes torch's e4m3fn cast of numpy's fp32
+    quotients k / scale.  Keys equal x exactly (eps = 2^80, gamma = 2^40, position 0), so the
+    rows are built to put quotients on and next to every e4m3 midpoint, over scales of many
+    magnitudes, where any other rounding of the quotient (a product with the fp32 reciprocal of
+    the scale, say) picks the other code."""
+    r = _rng(61)
+    mids, _ = _e4m3_positive_midpoints()
+    rows = []
+    for n in range(96):
+        amax = np.float32(r.uniform(1.0, 2.0) * 2.0 ** r.integers(-24, 11))
+        scale = amax / np.float32(448.0)
+        m = r.choice(mids, D - 1)
+        t = (m * np.float64(scale)).astype(np.float32)
+        step = r.integers(-3, 4, D - 1)
+        v = t.copy()
+        for _ in range(3):                 # walk a few fp32 ulps from the rounded target
+            v = np.where(step > 0, np.nextafter(v, np.float32(np.inf)), v)
+            v = np.where(step < 0, np.nextafter(v, np.float32(-np.inf)), v)
+            step = step - np.sign(step)
+        v = np.minimum(v, amax)            # the absmax stays the key's largest magnitude
+        sign = np.where(r.random(D - 1) < 0.5, -1.0, 1.0).astype(np.float32)
+        row = np.concatenate([[amax if n % 2 else -amax], sign * v]).astype(np.float32)
+        rows.append(row[r.permutation(D)])
+    # plain Gaussian keys with a heavy channel, and a key with a zero
+    g = r.standard_normal((32, D)) * 2.0 ** r.integers(-20, 10, (32, 1))
+    g[:, 5] *= 40.0
+    g[3, 7] = 0.0
+    x = np.concatenate([np.stack(rows), g]).astype(np.float32)
+    pool, k32, pt = _store_rows_pos0(x, FP8)
+    assert np.array_equal(k32, x)
+    pb = oracle.page_bytes(FP8)
+    amax = np.abs(x).max(axis=1).astype(np.float32)
+    scale = amax / np.float32(448.0)                                   # fp32 division
+    q = (x / scale[:, None]).astype(np.float32)                        # fp32 division
+    want = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    recip = (x * (np.float32(1.0) / scale)[:, None]).astype(np.float32)
+    other = torch.from_numpy(recip).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.sum(other != want) > 20, "the rows must tell the two quotient roundings apart"
+    for n in range(x.shape[0]):
+        base = int(pt[n, 0]) * pb
+        assert np.array_equal(pool[base: base + D], want[n]), n
+        got_s = pool[base + PAGE * D: base + PAGE * D + 4].view(np.float32)[0]
+        assert got_s == scale[n], n
+
+
 def pin_paging_invariance():
     r = _rng(9)
     n = 150
@@ -406,6 +495,51 @@ def pin_needle_planting():
     for i in range(5):
         c = k32[i].astype(np.float64) @ kstar[i] / (np.linalg.norm(k32[i]) * np.linalg.norm(kstar[i]))
         assert c > 1 - 1e-6, c
+
+
+def pin_needle_must_rank_bf16():
+    """A needle planted along the query's weighted head sum must be selected under bf16 storage,
+    on the oracle alone (store, logits, top-k), on inputs small enough for brute force.
+
+    Bound (the must-rank reading of the pages' recall test): bf16 rounding moves each key element
+    by at most 2^-9 of itself and ReLU is 1-Lipschitz, so a logit moves by at most
+    B(s) = 2^-9 sum_i u_i |k32_i|, u = sum_h |w_h| |q_h|.  A needle whose unquantised logit minus
+    2B beats all but fewer than k other keys' unquantised logits plus 2B must be in the top-k.
+    The bf16 logits are also recomputed by brute force from the stored bytes."""
+    import workloads as W
+    wl = W.make_workload("needle-pin", 4242, [1024, 1024, 1536, 2048], [1, 1, 1, 1], 16,
+                         permute_pages=True, extra_pages=1)
+    wl.needles = W.draw_needles(wl, 4)
+    x = oracle.plant_needles(wl, "weighted")
+    pool = oracle.new_pool(wl.n_pages_pool, BF16)
+    _, k32 = oracle.store_keys(x, wl.gamma, wl.eps, wl.key_idx, wl.key_seq, wl.page_table, BF16,
+                               pool, want_k32=True)
+    ref = np.zeros((wl.n_seq, wl.max_keys, D), np.float32)
+    ref[wl.key_seq, wl.key_idx] = k32
+    o16, nv = oracle.logits(wl.q_bits, wl.w, pool, BF16, wl.page_table, wl.seq_lens, wl.cu_q)
+    o32, _ = oracle.logits(wl.q_bits, wl.w, None, BF16, wl.page_table, wl.seq_lens, wl.cu_q,
+                           keys_ref=ref, ref_stride=wl.max_keys)
+    top, _ = oracle.topk(o16, wl.k, row_len=nv)
+    nd = wl.needles
+    checked = 0
+    for r in range(wl.n_q):
+        n = int(nv[r])
+        assert n == wl.seq_lens[r] // 4     # one query at the last token sees every key
+        q = _bf16_to_f64(wl.q_bits[r])                          # [64, 128]
+        w = wl.w[r].astype(np.float64)
+        keys = _pool_keys(pool, wl.page_table, BF16, r, n)      # decoded from the bytes
+        brute = np.maximum(keys @ q.T, 0.0) @ w
+        assert np.allclose(brute, o16[r, :n], rtol=1e-12, atol=1e-12)
+        u = np.abs(w) @ np.abs(q)
+        bound = 2.0 * 2.0 ** -9 * (np.abs(ref[r, :n]).astype(np.float64) @ u)
+        lo, hi = o32[r, :n] - bound, o32[r, :n] + bound
+        sel = set(int(v) for v in top[r] if v >= 0)
+        for sn in nd["s"][nd["qrow"] == r]:
+            sn = int(sn)
+            if np.sum(np.delete(hi, sn) >= lo[sn]) < wl.k:
+                assert sn in sel, f"needle ({r}, {sn}) must be in the bf16 top-{wl.k}"
+                checked += 1
+    assert checked >= 12, checked
 
 
 # ---- rotated store: the normalised Walsh-Hadamard transform -------------------------------------

@@ -8,13 +8,14 @@ dropped on dequantisation, a Hadamard butterfly stage skipped, the butterfly dif
 the Hadamard scale 1/128 instead of 2^-3.5, q quantised without dividing by its scale, the q
 scale dropped from the fp8 x fp8 logit, e2m1 ties away from zero, fp4 nibbles swapped, the
 attention's softmax scale dropped, a -1 list entry read as key 0, the kv slot of the next key
-taken, the log-sum-exp without its maximum, q read as [512][heads].
+taken, the log-sum-exp without its maximum, q read as [512][heads], the fp8 quotient taken as a
+product with the fp32 reciprocal of the scale, eps added outside the square root.
 """
 import pytest
 
 from tests.oracle_pins import ALL_PINS
 
-MUTATIONS = list(range(1, 26))
+MUTATIONS = list(range(1, 28))
 
 
 @pytest.mark.parametrize("m", MUTATIONS)
