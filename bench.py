@@ -123,10 +123,29 @@ def cpu_baseline(wl, dtype, x_step_mask, n_sample_rows: int, rotate: bool = Fals
     t_read = time.perf_counter() - t0
     secs = t_store * frac + t_read
     return {"value": float(nv.sum() / secs), "unit": "keys/s", "cores": oracle.num_threads(),
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{rows.size} of {wl.n_q} query rows (every {stride}th) scored and "
                       f"selected, plus the step's store scaled by {frac:.4f}; "
                       f"{secs:.2f} s of wall time"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def ev_stats(pairs) -> dict:
+    """Median, min and mean in ms of a list of (start, end) timing events."""
+    t = np.array([a.elapsed_time(b) for a, b in pairs], dtype=np.float64)
+    return {"median": round(float(np.median(t)), 5), "min": round(float(t.min()), 5),
+            "mean": round(float(t.mean()), 5)}
 
 
 def ceilings(args, torch) -> int:
@@ -278,7 +297,8 @@ def attn_bench(args, cfg, ix, torch, W) -> int:
         secs = time.perf_counter() - c0
         n_s = int((a.idx[rows] >= 0).sum())
         line["cpu_baseline"] = {"value": n_s / secs, "unit": "keys/s", "cores": oracle.num_threads(),
-                                "kind": "oracle",
+                                "affinity_cores": len(os.sched_getaffinity(0)),
+                                "cpu_model": cpu_model(), "kind": "oracle",
                                 "sample": f"{rows.size} of {wl.n_q} rows (every {stride}th), "
                                           f"{n_s} listed keys, {secs:.2f} s of wall time"}
     print(json.dumps(line), flush=True)
@@ -288,7 +308,7 @@ def attn_bench(args, cfg, ix, torch, W) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -378,11 +398,13 @@ def main() -> int:
                      device=dev)
     out_idx = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def ev_pairs():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.steps)]
-    for a, b in evs + step_evs:     # materialise the underlying hipEvent_t handles
+
+    evs, call_evs, step_evs = ev_pairs(), ev_pairs(), ev_pairs()
+    for a, b in evs:     # materialise the underlying hipEvent_t handles the library records
         a.record(stream)
         b.record(stream)
     flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
@@ -390,17 +412,24 @@ def main() -> int:
 
     q_rot = torch.empty_like(d["q"]) if args.rotate else None
 
-    def step(events=None):
+    def step(i=None):
         ix.store_keys(sx, d["gamma"], sidx, d["page_table"], pool, dtype, eps=wl.eps,
                       key_seq=sseq, rotate=args.rotate)
+        events = None if i is None else evs[i]
         if args.fp8q:
             codes, scales = ix.quantize_q(d["q"])
+            if i is not None:
+                call_evs[i][0].record(stream)
             ix.logits_topk_fp8q(codes, scales, d["w"], pool, d["page_table"], d["seq_lens"],
                                 d["cu_q"], wl.k, out_idx=out_idx, workspace=ws, events=events)
-            return
-        q = ix.rotate_q(d["q"], out=q_rot) if args.rotate else d["q"]
-        ix.logits_topk(q, d["w"], pool, dtype, d["page_table"], d["seq_lens"], d["cu_q"],
-                       wl.k, out_idx=out_idx, workspace=ws, events=events)
+        else:
+            q = ix.rotate_q(d["q"], out=q_rot) if args.rotate else d["q"]
+            if i is not None:
+                call_evs[i][0].record(stream)
+            ix.logits_topk(q, d["w"], pool, dtype, d["page_table"], d["seq_lens"], d["cu_q"],
+                           wl.k, out_idx=out_idx, workspace=ws, events=events)
+        if i is not None:
+            call_evs[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -411,32 +440,42 @@ def main() -> int:
             # read, not write, the 512 MiB: written lines would be dirty in the MALL and every
             # read of the step would then also pay for writing them back
             flush_sink.copy_(flush.max())
-        if flush is not None:
-            step_evs[i][0].record(stream)
-        step(evs[i])
-        if flush is not None:
-            step_evs[i][1].record(stream)
+        step_evs[i][0].record(stream)
+        step(i)
+        step_evs[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    if flush is None:
-        ms = (t1 - t0) * 1e3 / args.steps
-    else:
-        ms = float(np.mean([a.elapsed_time(b) for a, b in step_evs]))
+    # the host clock times the loop (with --cold it also covers the flushes, so the step events
+    # time the steps); the events give the median and min of single steps and calls
+    step_t = ev_stats(step_evs)
+    call_t = ev_stats(call_evs)
+    score_t = ev_stats(evs)
+    ms = (t1 - t0) * 1e3 / args.steps if flush is None else step_t["mean"]
     pairs, nv = _pairs(wl)
-    score_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     key_bytes = KEY_BYTES[dtype]
-    if cfg in (2, 4):   # decode: one pass over the visible keys of every sequence
+    decode = cfg in (2, 4)
+    if decode:
+        # one pass over the visible keys of every sequence, plus q and w; the roofline covers the
+        # whole idx_logits_topk call (scoring and selection), the score kernel alone beside it
         algo_bytes = float(nv.sum()) * key_bytes + wl.n_q * (64 * 128 * 2 + 64 * 4)
-        achieved = algo_bytes / (score_ms * 1e-3) / 1e9
+        achieved = algo_bytes / (call_t["median"] * 1e-3) / 1e9
+        score_ach = algo_bytes / (score_t["median"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "region": "idx_logits_topk call (score + select), median of HIP events",
+                "call_ms": call_t,
+                "score_only": {"achieved": round(score_ach, 1),
+                               "frac": round(score_ach / PEAK_HBM_GBS, 4), "kernel_ms": score_t}}
     else:
         flops = 2.0 * 64 * 128 * pairs
+        score_ms = score_t["mean"]
         achieved = flops / (score_ms * 1e-3) / 1e12
         peak = PEAK_FP8_TFLOPS if args.fp8q else PEAK_BF16_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "region": "scoring kernel, mean of HIP events around it on its stream",
+                "kernel_ms": score_t, "call_ms": call_t}
     # prefill-shaped batches (>= 1024 queries, >= 4 per sequence) run a rows kernel (the bf16 one
     # stages pages straight into LDS), the others the split kernel
     prefill_shaped = wl.n_q >= 1024 and wl.n_q >= 4 * wl.n_seq
@@ -447,7 +486,6 @@ def main() -> int:
     name = args.workload + ("-rotated" if args.rotate else "") + ("-fp8q" if args.fp8q else "")
     roof["traffic"] = committed_traffic(kernel, name)
     roof["kernel"] = kernel
-    roof["kernel_ms"] = round(score_ms, 4)
 
     line = {
         "metric": "indexer keys scored/s (top-k queries/s alongside)",
@@ -467,6 +505,7 @@ def main() -> int:
                    "keys_stored_in_step": int(stp.size), "heads": 64, "head_dim": 128,
                    "workspace_bytes": int(ws.numel())},
         "topk_queries_per_s": wl.n_q / (ms * 1e-3),
+        "step_ms": step_t,
         "roofline": roof,
         "cpu_baseline": None,
     }
