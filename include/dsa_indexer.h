@@ -141,16 +141,20 @@ size_t idx_logits_topk_workspace_size(int64_t n_q, int32_t n_seq, int32_t max_pa
 size_t idx_logits_topk_min_workspace(int32_t n_seq, int32_t max_pages, int32_t k);
 
 /*
- * Host only (no HIP call): the query chunking idx_logits_topk uses for a workspace of
- * workspace_bytes, so that a caller can see how a budget is spent before launching.
- * rows_per_chunk   out: query rows scored and selected per chunk (the last chunk may be smaller)
+ * Host only (no HIP call): the query chunking idx_logits_topk (and idx_logits_topk_fp8q) uses
+ * for a workspace of workspace_bytes, so that a caller can see how a budget is spent before
+ * launching.  n_seq as for the call (it decides which selection a batch shape gets).
+ * rows_per_chunk   out: query rows scored and selected per chunk (the last chunk may be smaller;
+ *                  the smaller of the two calls' chunkings)
  * max_chunk_bytes  out: the most workspace bytes any chunk of the call touches; never more than
  *                  workspace_bytes when the status is IDX_OK
- * Errors: IDX_EINVAL (null output, n_q < 1, max_pages < 0, k outside [1, IDX_MAX_TOPK]),
+ * Errors: IDX_EINVAL (null output, n_q < 1, n_seq < 0, max_pages < 0, k outside
+ * [1, IDX_MAX_TOPK]),
  * IDX_EWORKSPACE (not even one query row fits; rows_per_chunk is then 0).
  */
-int idx_logits_topk_plan(int64_t n_q, int32_t max_pages, int32_t k, size_t workspace_bytes,
-                         int64_t* rows_per_chunk, size_t* max_chunk_bytes);
+int idx_logits_topk_plan(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t k,
+                         size_t workspace_bytes, int64_t* rows_per_chunk,
+                         size_t* max_chunk_bytes);
 
 /*
  * S2 + S3 -- score every query against every causally visible key and select the top-k

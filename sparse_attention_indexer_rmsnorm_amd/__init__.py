@@ -41,7 +41,7 @@ SIGNATURES = [
     ("idx_rotate_q", ctypes.c_int, [_p, _p, _i64, _p]),
     ("idx_logits_topk_workspace_size", _sz, [_i64, _i32, _i32, _i32]),
     ("idx_logits_topk_min_workspace", _sz, [_i32, _i32, _i32]),
-    ("idx_logits_topk_plan", ctypes.c_int, [_i64, _i32, _i32, _sz, _p, _p]),
+    ("idx_logits_topk_plan", ctypes.c_int, [_i64, _i32, _i32, _i32, _sz, _p, _p]),
     ("idx_logits_topk", ctypes.c_int,
      [_p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _i32, _p, _p, _p, _sz,
       _p]),
@@ -129,13 +129,15 @@ def min_workspace(n_seq: int, max_pages: int, k: int) -> int:
     return int(lib().idx_logits_topk_min_workspace(n_seq, max_pages, k))
 
 
-def topk_plan(n_q: int, max_pages: int, k: int, workspace_bytes: int) -> Tuple[int, int]:
+def topk_plan(n_q: int, n_seq: int, max_pages: int, k: int,
+              workspace_bytes: int) -> Tuple[int, int]:
     """(query rows per chunk, most workspace bytes any chunk touches) for a workspace budget.
     Host only; raises IndexerError when not even one row fits."""
     rows = ctypes.c_int64(0)
     most = ctypes.c_size_t(0)
-    _check(lib().idx_logits_topk_plan(n_q, max_pages, k, workspace_bytes, ctypes.byref(rows),
-                                      ctypes.byref(most)), "idx_logits_topk_plan")
+    _check(lib().idx_logits_topk_plan(n_q, n_seq, max_pages, k, workspace_bytes,
+                                      ctypes.byref(rows), ctypes.byref(most)),
+           "idx_logits_topk_plan")
     return int(rows.value), int(most.value)
 
 

@@ -52,37 +52,88 @@ bool dtype_ok(int dtype) {
   return dtype == IDX_KV_FP8_E4M3 || dtype == IDX_KV_BF16 || dtype == IDX_KV_FP4_E2M1;
 }
 
-// Workspace layout for a chunk of `rows` query rows:
-//   [row_nvis int32 x rows | pad][scores fp32 rows x cols | pad][selection candidates]
-struct WsLayout {
-  size_t nvis, scores, topk, total;
+// Decode-shaped chunks (the split scoring kernel) are selected from per-workgroup histograms
+// (launch_topk_hist): the scoring kernel's workgroups cover 4 chunks of 256 or 512 keys of one
+// row, and a selection workgroup covers seg_len scores.  Rows of more than this many histogram
+// workgroups are selected in segments and passes instead (run_topk).
+constexpr int32_t kMaxHistWgPerRow = 64;
+
+struct HistPlan {
+  int32_t chunk_keys, n_chunks, wg_per_row, seg_len, n_seg;
 };
 
-WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k) {
+void plan_chunks(int64_t n_rows, int32_t n_cols, int32_t* chunk_keys, int32_t* n_chunks);
+
+HistPlan hist_plan(int64_t rows, int32_t cols) {
+  HistPlan h{};
+  int32_t ck, nc;
+  plan_chunks(rows, cols, &ck, &nc);
+  h.chunk_keys = ck >= 512 ? 512 : 256;
+  h.n_chunks = (cols + h.chunk_keys - 1) / h.chunk_keys;
+  h.wg_per_row = (h.n_chunks + kHistChunks - 1) / kHistChunks;
+  const int64_t segs4k = (static_cast<int64_t>(cols) + 4095) / 4096;
+  h.seg_len = rows * segs4k >= 256 ? 4096 : 2048;
+  h.n_seg = (cols + h.seg_len - 1) / h.seg_len;
+  return h;
+}
+
+// The selection a chunk of `rows` query rows gets: from histograms for decode-shaped chunks
+// scored by the split kernel (not for fp8 x fp8 scoring, whose rows kernel serves every shape).
+bool use_hist(int64_t rows, int32_t n_seq, int32_t cols, bool q8) {
+  if (q8 || cols <= 0 || prefill_shaped(rows, n_seq)) return false;
+  return hist_plan(rows, cols).wg_per_row <= kMaxHistWgPerRow;
+}
+
+// Workspace layout for a chunk of `rows` query rows:
+//   [row_nvis int32 x rows | pad][scores fp32 rows x cols | pad] then either
+//   [selection candidates] (segments and passes), or
+//   [histograms u16 rows x wg_per_row x kHistBins | pad][row counters int32 x rows | pad]
+//   [candidates u64 rows x cols] (selection from histograms)
+struct WsLayout {
+  size_t nvis, scores, topk, hist, ctr, cand, total;
+  bool hist_path;
+};
+
+WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k, int32_t n_seq, bool q8) {
   WsLayout L{};
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
   L.nvis = 0;
   L.scores = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
   L.topk = align_up(L.scores + static_cast<size_t>(rows) * cols * sizeof(float));
-  L.total = L.topk + topk_workspace_bytes(rows, static_cast<int64_t>(cols), k);
+  L.hist_path = use_hist(rows, n_seq, static_cast<int32_t>(cols), q8);
+  if (!L.hist_path) {
+    L.total = L.topk + topk_workspace_bytes(rows, static_cast<int64_t>(cols), k);
+    return L;
+  }
+  const HistPlan h = hist_plan(rows, static_cast<int32_t>(cols));
+  L.hist = L.topk;
+  L.ctr = align_up(L.hist + static_cast<size_t>(rows) * h.wg_per_row * kHistBins * 2);
+  L.cand = align_up(L.ctr + static_cast<size_t>(rows) * sizeof(int32_t));
+  L.total = L.cand + static_cast<size_t>(rows) * cols * 8;
   return L;
 }
 
-// A bound on workspace_layout(n).total for every n <= rows that never decreases with `rows`:
-// the exact size is not monotone (a batch of few rows is selected by one workgroup per row with
-// no candidates, more rows in segments with candidate buffers), so every row reserves the widest
-// candidate row any batch shape can need, and the alignment slack of each region is counted.
+// A bound on workspace_layout(n).total for every n <= rows, every n_seq and both selections,
+// that never decreases with `rows`: the exact size is not monotone (a batch of few rows is
+// selected by one workgroup per row with no candidates, more rows in segments with candidate
+// buffers, decode-shaped chunks from histograms), so every row reserves the most any of them
+// needs per row, and the alignment slack of each region is counted.
 size_t workspace_upper(int64_t rows, int32_t max_pages, int32_t k) {
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
   const size_t cand = static_cast<size_t>(topk_cand_bound(static_cast<int64_t>(cols), k));
-  return static_cast<size_t>(rows) * (sizeof(int32_t) + cols * sizeof(float) + 2 * cand * 8) +
-         4 * kAlign;
+  const size_t passes_row = 2 * cand * 8;
+  const size_t wg_max = (cols + 4 * 256 - 1) / (4 * 256);   // histogram workgroups of 4 x 256 keys
+  const size_t hist_row = wg_max * kHistBins * 2 + sizeof(int32_t) + cols * 8;
+  const size_t sel_row = passes_row > hist_row ? passes_row : hist_row;
+  return static_cast<size_t>(rows) * (sizeof(int32_t) + cols * sizeof(float) + sel_row) +
+         6 * kAlign;
 }
 
 // Query rows per chunk for a workspace of `bytes`: all of them if they fit, else the largest
 // count whose upper bound fits, so that every chunk (the last one has fewer rows) fits too.
-int64_t rows_fitting(size_t bytes, int32_t max_pages, int32_t k, int64_t n_q) {
-  if (workspace_layout(n_q, max_pages, k).total <= bytes) return n_q;
+int64_t rows_fitting(size_t bytes, int32_t max_pages, int32_t k, int64_t n_q, int32_t n_seq,
+                     bool q8) {
+  if (workspace_layout(n_q, max_pages, k, n_seq, q8).total <= bytes) return n_q;
   int64_t lo = 0, hi = n_q;
   while (lo < hi) {
     const int64_t mid = lo + (hi - lo + 1) / 2;
@@ -146,7 +197,8 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
   if (n_q > 0 && !out_idx) return IDX_EINVAL;
   if (n_q == 0) return IDX_OK;
   if (!workspace) return IDX_EWORKSPACE;
-  const int64_t rows_per_chunk = rows_fitting(workspace_bytes, max_pages, k, n_q);
+  const bool q8 = q_scale != nullptr;
+  const int64_t rows_per_chunk = rows_fitting(workspace_bytes, max_pages, k, n_q, n_seq, q8);
   if (rows_per_chunk < 1) return IDX_EWORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -165,18 +217,31 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
 
   for (int64_t q0 = 0; q0 < n_q; q0 += rows_per_chunk) {
     const int64_t rows = (n_q - q0 < rows_per_chunk) ? n_q - q0 : rows_per_chunk;
-    const WsLayout L = workspace_layout(rows, max_pages, k);
+    const WsLayout L = workspace_layout(rows, max_pages, k, n_seq, q8);
     int32_t* nvis = reinterpret_cast<int32_t*>(ws + L.nvis);
     float* scores = reinterpret_cast<float*>(ws + L.scores);
     sa.q_begin = q0;
     sa.n_rows = rows;
     sa.out = scores;
     sa.row_nvis = nvis;
-    if (cols > 0) {
-      plan_chunks(rows, cols, &sa.chunk_keys, &sa.n_chunks);
+    HistPlan hp{};
+    if (L.hist_path) {
+      hp = hist_plan(rows, cols);
+      sa.chunk_keys = hp.chunk_keys;
+      sa.n_chunks = hp.n_chunks;
+      sa.wg_per_row = hp.wg_per_row;
+      sa.wg_hist = reinterpret_cast<uint16_t*>(ws + L.hist);
+      sa.row_ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
     } else {
-      sa.chunk_keys = 32;
-      sa.n_chunks = 1;
+      sa.wg_hist = nullptr;
+      sa.row_ctr = nullptr;
+      sa.wg_per_row = 0;
+      if (cols > 0) {
+        plan_chunks(rows, cols, &sa.chunk_keys, &sa.n_chunks);
+      } else {
+        sa.chunk_keys = 32;
+        sa.n_chunks = 1;
+      }
     }
     if (ev_begin && q0 == 0 && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
       return IDX_EHIP;
@@ -184,9 +249,27 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
     if (ev_end && q0 + rows >= n_q &&
         hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
       return IDX_EHIP;
-    if (run_topk(scores, cols > 0 ? cols : 1, nvis, rows, k, out_idx + q0 * k,
-                 out_val ? out_val + q0 * k : nullptr, ws + L.topk, s) != hipSuccess)
+    if (L.hist_path) {
+      HistSelArgs h{};
+      h.scores = scores;
+      h.cols = cols;
+      h.row_nvis = nvis;
+      h.n_rows = rows;
+      h.k = k;
+      h.wg_hist = sa.wg_hist;
+      h.wg_per_row = hp.wg_per_row;
+      h.wg_keys = kHistChunks * hp.chunk_keys;
+      h.row_ctr = sa.row_ctr;
+      h.n_seg = hp.n_seg;
+      h.seg_len = hp.seg_len;
+      h.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
+      h.out_idx = out_idx + q0 * k;
+      h.out_val = out_val ? out_val + q0 * k : nullptr;
+      if (launch_topk_hist(h, s) != hipSuccess) return IDX_EHIP;
+    } else if (run_topk(scores, cols > 0 ? cols : 1, nvis, rows, k, out_idx + q0 * k,
+                        out_val ? out_val + q0 * k : nullptr, ws + L.topk, s) != hipSuccess) {
       return IDX_EHIP;
+    }
   }
   return IDX_OK;
 }
@@ -267,13 +350,15 @@ int idx_rotate_q(const void* q, void* out, int64_t n_vec, void* stream) {
 }
 
 size_t idx_logits_topk_workspace_size(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t k) {
-  (void)n_seq;
   if (k < 1) k = 1;
   if (max_pages < 0) max_pages = 0;
   if (n_q <= 0) return align_up(sizeof(int32_t));
-  const size_t all = workspace_layout(n_q, max_pages, k).total;
+  // enough for the selection either scoring path (bf16-q or fp8-q) takes for the whole batch
+  const size_t a = workspace_layout(n_q, max_pages, k, n_seq, false).total;
+  const size_t b = workspace_layout(n_q, max_pages, k, n_seq, true).total;
+  const size_t all = a > b ? a : b;
   if (all <= kWorkspaceCap) return all;
-  const int64_t cap_rows = rows_fitting(kWorkspaceCap, max_pages, k, n_q);
+  const int64_t cap_rows = rows_fitting(kWorkspaceCap, max_pages, k, n_q, n_seq, false);
   return workspace_upper(cap_rows < 1 ? 1 : cap_rows, max_pages, k);
 }
 
@@ -282,24 +367,34 @@ size_t idx_logits_topk_min_workspace(int32_t n_seq, int32_t max_pages, int32_t k
   return workspace_upper(1, max_pages < 0 ? 0 : max_pages, k < 1 ? 1 : k);
 }
 
-int idx_logits_topk_plan(int64_t n_q, int32_t max_pages, int32_t k, size_t workspace_bytes,
-                         int64_t* rows_per_chunk, size_t* max_chunk_bytes) {
-  if (n_q < 1 || max_pages < 0 || k < 1 || k > IDX_MAX_TOPK || !rows_per_chunk ||
+int idx_logits_topk_plan(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t k,
+                         size_t workspace_bytes, int64_t* rows_per_chunk,
+                         size_t* max_chunk_bytes) {
+  if (n_q < 1 || n_seq < 0 || max_pages < 0 || k < 1 || k > IDX_MAX_TOPK || !rows_per_chunk ||
       !max_chunk_bytes)
     return IDX_EINVAL;
   if (n_q > INT32_MAX || static_cast<int64_t>(max_pages) * IDX_PAGE_KEYS > INT32_MAX / 2)
     return IDX_EINVAL;
-  const int64_t rows = rows_fitting(workspace_bytes, max_pages, k, n_q);
-  *rows_per_chunk = rows;
+  *rows_per_chunk = 0;
   *max_chunk_bytes = 0;
-  if (rows < 1) return IDX_EWORKSPACE;
-  // every chunk has `rows` rows except the last, which has the remainder
-  size_t most = workspace_layout(rows, max_pages, k).total;
-  const int64_t tail = n_q % rows;
-  if (tail > 0) {
-    const size_t t = workspace_layout(tail, max_pages, k).total;
-    most = t > most ? t : most;
+  // the plan of the bf16 / fp8 / fp4-q call, and of the fp8 x fp8 one: report the larger
+  size_t most = 0;
+  int64_t rows_min = n_q;
+  for (int v = 0; v < 2; ++v) {
+    const bool q8 = v == 1;
+    const int64_t rows = rows_fitting(workspace_bytes, max_pages, k, n_q, n_seq, q8);
+    if (rows < 1) return IDX_EWORKSPACE;
+    rows_min = rows < rows_min ? rows : rows_min;
+    // every chunk has `rows` rows except the last, which has the remainder
+    size_t m = workspace_layout(rows, max_pages, k, n_seq, q8).total;
+    const int64_t tail = n_q % rows;
+    if (tail > 0) {
+      const size_t t = workspace_layout(tail, max_pages, k, n_seq, q8).total;
+      m = t > m ? t : m;
+    }
+    most = m > most ? m : most;
   }
+  *rows_per_chunk = rows_min;
   *max_chunk_bytes = most;
   return IDX_OK;
 }

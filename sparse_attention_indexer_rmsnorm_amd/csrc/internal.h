@@ -66,7 +66,30 @@ struct ScoreArgs {
   int32_t* row_nvis;         // [n_rows] visible-key count per row, or null
   const uint8_t* q8;         // fp8 x fp8 scoring: q e4m3 codes [n_q, 64, 128], or null
   const float* q_scale;      // [n_q, 64] scales of q8
+  // Histogram mode of the split kernel (set by the decode-shaped selection): workgroup
+  // (row r, j) scores chunks 4j .. 4j + 3 of row r and writes a kHistBins-bin histogram of its
+  // scores to wg_hist[(r * wg_per_row + j) * kHistBins ..] (16-bit counts); workgroup (r, 0)
+  // also zeroes row_ctr[r] for the selection.  Null wg_hist: plain mode (any four work items per
+  // workgroup).
+  uint16_t* wg_hist;
+  int32_t* row_ctr;
+  int32_t wg_per_row;
 };
+
+// Selection histogram: bins are the top kHistBits bits of a score's order-preserving key, so a
+// bin is the same set of values in every workgroup of a row.
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 32 - kHistBits;
+// Chunks of one row per histogram workgroup (one per wave).
+constexpr int kHistChunks = 4;
+
+// Order-preserving uint32 key of a score that is not a NaN: adding +0 turns -0 into +0 (fp32
+// denormals are kept), then the sign selects the mask.
+__device__ __forceinline__ uint32_t score_order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+}
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 // Prefill-shaped variant: 4 query rows per workgroup share LDS-staged key pages; covers all
@@ -100,6 +123,31 @@ struct TopkPlan {
   int passes;                // selection passes (1: each row in one wave)
   int64_t cand_elems;        // widest candidate row between passes
 };
+
+// Selection over a score matrix written by the split kernel in histogram mode (few long rows:
+// decode batches).  Row r is cut into n_seg segments of seg_len scores, one workgroup each; the
+// workgroup sums the row's histograms, finds the bin holding the k-th largest score, and writes
+// the keys of higher bins straight to their output positions (the histograms of the earlier
+// segments give the offset) and the threshold bin's keys to the row's candidate list; the last
+// workgroup of the row to finish refines the candidates to the exact threshold.
+struct HistSelArgs {
+  const float* scores;       // [n_rows, cols]
+  int64_t cols;
+  const int32_t* row_nvis;   // [n_rows] visible keys per row
+  int64_t n_rows;
+  int32_t k;
+  const uint16_t* wg_hist;   // [n_rows, wg_per_row, kHistBins]
+  int32_t wg_per_row;
+  int32_t wg_keys;           // scores per histogram workgroup; divides seg_len
+  int32_t* row_ctr;          // [n_rows], zero on entry
+  int32_t n_seg;
+  int32_t seg_len;           // 2048 or 4096
+  uint64_t* cand;            // [n_rows, cols] (order key << 32 | index), index order
+  int32_t* out_idx;          // [n_rows, k]
+  float* out_val;            // [n_rows, k] or null
+};
+
+hipError_t launch_topk_hist(const HistSelArgs& a, hipStream_t stream);
 
 TopkPlan topk_plan(int64_t n_rows, int64_t cols, int32_t k);
 // Workspace the selection of n_rows rows of `cols` scores needs (0 for one pass).

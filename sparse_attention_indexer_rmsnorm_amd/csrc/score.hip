@@ -193,41 +193,13 @@ struct KeyBlock<kFp4> {
   }
 };
 
-template <int DT>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+// Scores of keys [c_begin, s_end) of query row i (sequence b): lane (m, g) holds key s0 + m of
+// each 32-key block; in histogram mode the lanes of group 0 also count their keys' scores.
+template <int DT, bool HIST>
+__device__ __forceinline__ void score_chunk(const ScoreArgs& a, int64_t i, int32_t b,
+                                            int32_t c_begin, int32_t s_end, float* out_row,
+                                            uint32_t* hist) {
   const int lane = threadIdx.x & 63;
-  // the wave index is uniform within a wave; say so, so that everything derived from it
-  // (row, sequence, page-table row) lives in scalar registers
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 +
-                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t r = wave / a.n_chunks;
-  const int32_t chunk = static_cast<int32_t>(wave % a.n_chunks);
-  if (r >= a.n_rows) return;
-  const int64_t i = a.q_begin + r;
-
-  // Query position and visible-key count.
-  const int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
-  int64_t n_vis = 0;
-  if (b >= 0) {
-    const int64_t q_len = a.cu_q[b + 1] - a.cu_q[b];
-    const int64_t t = static_cast<int64_t>(a.seq_lens[b]) - q_len + (i - a.cu_q[b]);
-    if (t >= 0) {
-      n_vis = (t + 1) / kRatio;
-      const int64_t cap = static_cast<int64_t>(a.max_pages) * kPageKeys;
-      n_vis = n_vis < cap ? n_vis : cap;
-    }
-  }
-  if (a.row_nvis && chunk == 0 && lane == 0) a.row_nvis[r] = static_cast<int32_t>(n_vis);
-
-  const int32_t c_begin = chunk * a.chunk_keys;
-  const int32_t c_end = min(c_begin + a.chunk_keys, a.n_cols);
-  const int32_t s_end = static_cast<int32_t>(min<int64_t>(c_end, n_vis));
-  float* out_row = a.out + r * a.out_stride;
-  if (a.fill_invisible) {
-    for (int32_t s = max(c_begin, s_end) + lane; s < c_end; s += 64) out_row[s] = -INFINITY;
-  }
-  if (c_begin >= s_end) return;
-
   const int m = lane & 31;      // MFMA row (A) / column (B, D) index
   const int g = lane >> 5;      // lane group: which 64 dims of head_dim this lane feeds
 
@@ -274,10 +246,77 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     float tot = head_sum(acc0, acc1, wv);
     if constexpr (DT != kBf16) tot *= b0.scale;
     const int32_t s = s0 + m;
-    if (g == 0 && s < s_end) out_row[s] = ok0 ? tot : -INFINITY;
+    const float v = ok0 ? tot : -INFINITY;
+    if (g == 0 && s < s_end) {
+      out_row[s] = v;
+      if constexpr (HIST) atomicAdd(&hist[score_order_key(v) >> kHistShift], 1u);
+    }
     b0 = b1; ok0 = ok1;
     b1 = b2; ok1 = ok2;
     p2 = p3;
+  }
+}
+
+// One wave owns one (query row, chunk of chunk_keys keys) work item.  In histogram mode the four
+// waves of a workgroup own consecutive chunks of one row and count their scores into a shared
+// LDS histogram, which the workgroup writes out for the selection.
+template <int DT, bool HIST>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[HIST ? kHistBins : 1];
+  const int lane = threadIdx.x & 63;
+  // the wave index is uniform within a wave; say so, so that everything derived from it
+  // (row, sequence, page-table row) lives in scalar registers
+  const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  int64_t r;
+  int32_t chunk;
+  if constexpr (HIST) {
+    r = blockIdx.x / a.wg_per_row;
+    chunk = static_cast<int32_t>(blockIdx.x % a.wg_per_row) * kHistChunks + wid;
+#pragma unroll
+    for (int c = 0; c < kHistBins / 1024; ++c)
+      reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * c] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  } else {
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+    r = wave / a.n_chunks;
+    chunk = static_cast<int32_t>(wave % a.n_chunks);
+    if (r >= a.n_rows) return;
+  }
+  const int64_t i = a.q_begin + r;
+
+  // Query position and visible-key count.
+  const int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
+  int64_t n_vis = 0;
+  if (b >= 0) {
+    const int64_t q_len = a.cu_q[b + 1] - a.cu_q[b];
+    const int64_t t = static_cast<int64_t>(a.seq_lens[b]) - q_len + (i - a.cu_q[b]);
+    if (t >= 0) {
+      n_vis = (t + 1) / kRatio;
+      const int64_t cap = static_cast<int64_t>(a.max_pages) * kPageKeys;
+      n_vis = n_vis < cap ? n_vis : cap;
+    }
+  }
+  if (a.row_nvis && chunk == 0 && lane == 0) a.row_nvis[r] = static_cast<int32_t>(n_vis);
+
+  const int32_t c_begin = chunk * a.chunk_keys;
+  const int32_t c_end = min(c_begin + a.chunk_keys, a.n_cols);
+  const int32_t s_end = static_cast<int32_t>(min<int64_t>(c_end, n_vis));
+  float* out_row = a.out + r * a.out_stride;
+  if (a.fill_invisible) {
+    for (int32_t s = max(c_begin, s_end) + lane; s < c_end; s += 64) out_row[s] = -INFINITY;
+  }
+  if (c_begin < s_end) score_chunk<DT, HIST>(a, i, b, c_begin, s_end, out_row, hist);
+
+  if constexpr (HIST) {
+    __syncthreads();
+    // bins 8 t .. 8 t + 7 of thread t as 16-bit counts (at most 4 x 512 scores per workgroup)
+    const u32x4 lo = reinterpret_cast<const u32x4*>(hist)[2 * threadIdx.x];
+    const u32x4 hi = reinterpret_cast<const u32x4*>(hist)[2 * threadIdx.x + 1];
+    const u32x4 packed = {lo.x | (lo.y << 16), lo.z | (lo.w << 16), hi.x | (hi.y << 16),
+                          hi.z | (hi.w << 16)};
+    reinterpret_cast<u32x4*>(a.wg_hist + static_cast<int64_t>(blockIdx.x) * kHistBins)
+        [threadIdx.x] = packed;
+    if (threadIdx.x == 0 && blockIdx.x % a.wg_per_row == 0) a.row_ctr[r] = 0;
   }
 }
 
@@ -1058,18 +1097,30 @@ hipError_t launch_score_fp8q(const ScoreArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
-  const int64_t waves = a.n_rows * a.n_chunks;
-  if (waves <= 0) return hipSuccess;
-  const int64_t blocks = (waves + 3) / 4;
-  if (dtype == kBf16)
-    hipLaunchKernelGGL(score_kernel<kBf16>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
-  else if (dtype == kFp4)
-    hipLaunchKernelGGL(score_kernel<kFp4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(score_kernel<kFp8>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, a);
+  int64_t blocks;
+  if (a.wg_hist) {
+    blocks = a.n_rows * a.wg_per_row;
+  } else {
+    const int64_t waves = a.n_rows * a.n_chunks;
+    blocks = (waves + 3) / 4;
+  }
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
+  if (a.wg_hist) {
+    if (dtype == kBf16)
+      hipLaunchKernelGGL((score_kernel<kBf16, true>), grid, block, 0, stream, a);
+    else if (dtype == kFp4)
+      hipLaunchKernelGGL((score_kernel<kFp4, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((score_kernel<kFp8, true>), grid, block, 0, stream, a);
+  } else {
+    if (dtype == kBf16)
+      hipLaunchKernelGGL((score_kernel<kBf16, false>), grid, block, 0, stream, a);
+    else if (dtype == kFp4)
+      hipLaunchKernelGGL((score_kernel<kFp4, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((score_kernel<kFp8, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -42,10 +42,13 @@ def test_page_bytes(L):
 
 
 def test_workspace_sizes(L):
-    # decode batch of 32 queries over 512 pages: a row of 32768 fp32 scores each plus visible
-    # counts; few rows are selected one workgroup per row in a single pass (no candidates)
+    # decode batch of 32 queries over 512 pages: visible counts, a row of 32768 fp32 scores each,
+    # then the histogram selection's 16 workgroup histograms of 2048 16-bit bins per row, one
+    # counter per row and a candidate list of 32768 (key, index) pairs per row
     scores = 256 + 32 * 32768 * 4
-    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == scores
+    hist = 32 * 16 * 2048 * 2
+    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == scores + hist + 256 + \
+        32 * 32768 * 8
     # 256 such rows go through the segmented two-pass selection: two candidate buffers of
     # 6 segments x k (index, value) pairs per row
     cand = 2 * (256 * 6 * 1024 * 8 + 256)
@@ -68,26 +71,31 @@ def test_workspace_sizes(L):
 def test_chunk_plan_fits_workspace(L):
     """Every query chunk of idx_logits_topk fits the workspace it is given: the planner's row
     bound must cover the segmented selection's candidate buffers, which a batch of more than 128
-    long rows needs even where a single row is selected with none."""
-    for max_pages in (97, 128, 192, 256, 384, 512, 640):      # 6208 .. 40960 key columns
+    long rows needs even where a single row is selected with none, and the histogram selection's
+    histograms and candidate lists (decode-shaped batches)."""
+    for max_pages in (1, 16, 97, 128, 192, 256, 384, 512, 640, 2048):  # 64 .. 131072 key columns
         for k in (512, 1024, 2048):
             mins = ix.min_workspace(1, max_pages, k)
             for n_q in (1, 2, 128, 129, 200, 517, 1000, 4096, 8192):
-                rec = ix.workspace_size(n_q, 1, max_pages, k)
-                budgets = {rec, mins, mins + 12345, 4 << 20, 8 << 20, 11 << 20, 64 << 20,
-                           rec // 3, rec - 1}
-                for b in sorted(budgets):
-                    if b < mins:
-                        continue
-                    rows, most = ix.topk_plan(n_q, max_pages, k, b)
-                    assert 1 <= rows <= n_q, (max_pages, k, n_q, b, rows)
-                    assert most <= b, (max_pages, k, n_q, b, rows, most)
-                rows, _ = ix.topk_plan(n_q, max_pages, k, rec)
-                assert rows == n_q or rec <= 256 << 20 + 4096, (max_pages, k, n_q, rec)
+                for n_seq in sorted({1, max(1, n_q // 2), n_q}):
+                    rec = ix.workspace_size(n_q, n_seq, max_pages, k)
+                    budgets = {rec, mins, mins + 12345, 4 << 20, 8 << 20, 11 << 20, 64 << 20,
+                               rec // 3, rec - 1}
+                    for b in sorted(budgets):
+                        if b < mins:
+                            continue
+                        rows, most = ix.topk_plan(n_q, n_seq, max_pages, k, b)
+                        assert 1 <= rows <= n_q, (max_pages, k, n_q, n_seq, b, rows)
+                        assert most <= b, (max_pages, k, n_q, n_seq, b, rows, most)
+                    rows, _ = ix.topk_plan(n_q, n_seq, max_pages, k, rec)
+                    assert rows == n_q or rec <= (256 << 20) + 4096, (max_pages, k, n_q, rec)
+    # the long prefill chunk still runs in one pass within the 256 MiB cap
+    rec = ix.workspace_size(8192, 1, 88, 512)
+    assert ix.topk_plan(8192, 1, 88, 512, rec)[0] == 8192 and rec <= 256 << 20
     # too small for a single row
     with pytest.raises(ix.IndexerError):
-        ix.topk_plan(10, 88, 512, 100)
-    assert L.idx_logits_topk_plan(0, 88, 512, 1 << 20, FAKE, FAKE) == E_INVAL
+        ix.topk_plan(10, 1, 88, 512, 100)
+    assert L.idx_logits_topk_plan(0, 1, 88, 512, 1 << 20, FAKE, FAKE) == E_INVAL
 
 
 def _store(L, **kw):

@@ -201,7 +201,7 @@ def test_workspace_guard_bytes(budget):
         nbytes = ix.workspace_size(wl.n_q, wl.n_seq, wl.max_pages, wl.k)
     else:
         nbytes = budget
-    rows, most = ix.topk_plan(wl.n_q, wl.max_pages, wl.k, nbytes)
+    rows, most = ix.topk_plan(wl.n_q, wl.n_seq, wl.max_pages, wl.k, nbytes)
     print(f"guard budget={nbytes} rows/chunk={rows} most={most}", flush=True)
     assert most <= nbytes
     guard = 1 << 16
@@ -212,3 +212,33 @@ def test_workspace_guard_bytes(budget):
     assert torch.all(buf[:guard] == 0x5A), "bytes written before the workspace"
     assert torch.all(buf[guard + nbytes:] == 0x5A), "bytes written after the workspace"
     assert torch.equal(by_index(full), by_index(part))
+
+
+@pytest.mark.parametrize("dtype,k", [(BF16, 1024), (FP8, 512), (BF16, 2048)])
+def test_decode_selection_ties_match_dense_then_select(dtype, k):
+    """Decode rows whose scores tie massively: a sequence of all-zero keys (every score 0, so
+    the threshold bin holds the whole row, more than a workgroup lists in LDS), a sequence whose
+    keys take three values (dims 64..127 zero, so the rotation leaves identical rows identical),
+    a row shorter than k and long plain rows.  Ties go to the lower index; the selection must
+    equal the one made over the dense logits, bit for bit."""
+    lens = np.array([4 * 9000, 4 * 5000, 4 * 700, 4 * 20000, 4 * 4100, 4 * 33000], np.int32)
+    wl = W.make_workload("decode-ties", 515 + k, lens, np.ones(lens.size, np.int32), k,
+                         permute_pages=True)
+    x = wl.x.copy()
+    x[wl.key_seq == 0] = 0.0
+    rows1 = np.nonzero(wl.key_seq == 1)[0]
+    x[rows1] = x[rows1[np.arange(rows1.size) % 3]]
+    x[rows1, 64:] = 0.0
+    d = dev_inputs(wl, x)
+    pool = gpu_store(ix, wl, dtype, d)
+    gi, gv = _gpu_topk(wl, d, pool, dtype, want_values=True)
+    dense = ix.logits_dense(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
+                            d["cu_q"], wl.max_keys)
+    t = query_positions(wl)
+    nv = torch.from_numpy(np.minimum((t + 1) // 4, wl.max_keys).astype(np.int32)).cuda()
+    si, sv = ix.topk_rows(dense, wl.k, nv)
+    gi, gv = by_index(gi, gv)
+    si, sv = by_index(si, sv)
+    assert torch.equal(gi, si)
+    assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
+    assert torch.equal(gi[0, :k].cpu(), torch.arange(k, dtype=torch.int32))   # all ties: 0..k-1
