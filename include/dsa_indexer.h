@@ -190,6 +190,26 @@ int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * idx_logits_topk for callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It calls no
+ * hipMalloc, hipFree or other allocating routine.  Its workspace is the library's own static
+ * device scratch of idx_logits_topk_noalloc_scratch_bytes() bytes (64 MiB), one per GPU, held
+ * from the library's load until the process ends; its device address is looked up on the first
+ * call on each device (with that device current).  Arguments, results and errors are those of
+ * idx_logits_topk; a batch whose full workspace exceeds the scratch is processed in query chunks
+ * that fit, and one that cannot fit even one query row returns IDX_EWORKSPACE.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or host threads) race and must be ordered by the caller.  The scratch needs no
+ * clearing between calls: every region is written before it is read within a call.
+ */
+int idx_logits_topk_noalloc(const void* q, const float* w, const void* kcache, int dtype,
+                            int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                            int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q,
+                            int64_t n_q, int32_t n_heads, int32_t k, int32_t* out_idx,
+                            float* out_val, void* stream);
+size_t idx_logits_topk_noalloc_scratch_bytes(void);
+
+/*
  * idx_logits_topk with instrumentation: `ev_score_begin` / `ev_score_end` (hipEvent_t, either may
  * be NULL) are recorded on `stream` right before the first and right after the last launch of the
  * scoring kernel, so a caller can time that kernel alone.  Results are identical.

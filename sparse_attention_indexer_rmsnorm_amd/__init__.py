@@ -45,6 +45,9 @@ SIGNATURES = [
     ("idx_logits_topk", ctypes.c_int,
      [_p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _i32, _p, _p, _p, _sz,
       _p]),
+    ("idx_logits_topk_noalloc", ctypes.c_int,
+     [_p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _i32, _p, _p, _p]),
+    ("idx_logits_topk_noalloc_scratch_bytes", _sz, []),
     ("idx_logits_topk_timed", ctypes.c_int,
      [_p, _p, _p, ctypes.c_int, _i64, _p, _i32, _i32, _p, _p, _i64, _i32, _i32, _p, _p, _p, _sz,
       _p, _p, _p]),

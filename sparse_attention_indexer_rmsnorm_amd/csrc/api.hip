@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dsa_indexer.h"
 #include "attn.h"
@@ -274,6 +275,30 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
   return IDX_OK;
 }
 
+// Workspace of idx_logits_topk_noalloc: device memory that belongs to the loaded library (each
+// GPU holds its own copy until the process ends), so that the call allocates nothing.  In host
+// code `scratch` only names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current and kept below.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch, or null when it cannot be had.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -408,6 +433,28 @@ int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype
                           max_pages, seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, workspace,
                           workspace_bytes, nullptr, nullptr, stream);
 }
+
+int idx_logits_topk_noalloc(const void* q, const float* w, const void* kcache, int dtype,
+                            int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
+                            int32_t max_pages, const int32_t* seq_lens, const int32_t* cu_q,
+                            int64_t n_q, int32_t n_heads, int32_t k, int32_t* out_idx,
+                            float* out_val, void* stream) {
+  // the checks the workspace entry point makes, before the scratch is looked up
+  int st = validate_logits_common(q, w, kcache, dtype, n_pages_pool, page_table, n_seq, max_pages,
+                                  seq_lens, cu_q, n_q, n_heads);
+  if (st != IDX_OK) return st;
+  if (k < 1 || k > IDX_MAX_TOPK) return IDX_EINVAL;
+  if (n_q > 0 && !out_idx) return IDX_EINVAL;
+  if (n_q == 0) return IDX_OK;
+  if (rows_fitting(kScratchBytes, max_pages, k, n_q, n_seq, false) < 1) return IDX_EWORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return IDX_EHIP;
+  return logits_topk_impl(q, nullptr, w, kcache, dtype, n_pages_pool, page_table, n_seq,
+                          max_pages, seq_lens, cu_q, n_q, n_heads, k, out_idx, out_val, ws,
+                          kScratchBytes, nullptr, nullptr, stream);
+}
+
+size_t idx_logits_topk_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int idx_logits_topk_timed(const void* q, const float* w, const void* kcache, int dtype,
                           int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
