@@ -123,30 +123,16 @@ __device__ __forceinline__ void hadamard128(double& v0, double& v1, double& v2, 
   v3 *= kHadamardScale;
 }
 
+// Keys per half-wave: all of them are requested (indices, activations, then page ids) before any
+// is computed, so a wave has several rows of activations in flight.
+constexpr int kStoreKeysPerHalfWave = 4;
+
+// One key (row n, sequence b, index s, activations xa/xb, destination page), computed and stored
+// by the 32 lanes of a half-wave; lane j owns dims 2j, 2j+1 and the rotated pair 64+2j, 65+2j.
 template <int DT, bool HAD>
-__global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
+__device__ __forceinline__ void store_one(const StoreArgs& a, int j, bool ok, int32_t page,
+                                          int32_t s, float2 xa, float2 xb, float2 ga, float2 gb) {
 #pragma clang fp contract(off)
-  const int64_t n_raw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
-  const int j = threadIdx.x & 31;
-  const bool in_range = n_raw < a.n_keys;
-  const int64_t n = in_range ? n_raw : a.n_keys - 1;   // idle half-waves recompute the last key
-
-  const int32_t b = a.key_seq ? a.key_seq[n] : 0;
-  const int32_t s = a.key_idx[n];
-  bool ok = in_range && b >= 0 && b < a.n_seq && s >= 0 &&
-            static_cast<int64_t>(s) < static_cast<int64_t>(a.max_pages) * kPageKeys;
-  int32_t page = -1;
-  if (ok) {
-    page = a.page_table[static_cast<int64_t>(b) * a.max_pages + s / kPageKeys];
-    ok = page >= 0 && page < a.n_pages_pool;
-  }
-
-  const float* xr = a.x + n * kHeadDim;
-  const float2 xa = *reinterpret_cast<const float2*>(xr + 2 * j);
-  const float2 xb = *reinterpret_cast<const float2*>(xr + 64 + 2 * j);
-  const float2 ga = *reinterpret_cast<const float2*>(a.gamma + 2 * j);
-  const float2 gb = *reinterpret_cast<const float2*>(a.gamma + 64 + 2 * j);
-
   // RMSNorm in fp64.
   const double x0 = xa.x, x1 = xa.y, x2 = xb.x, x3 = xb.y;
   double ss = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
@@ -180,7 +166,7 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
     amax = half_wave_max(amax);
     if (!ok) return;
     // as for fp8 below, with the largest e2m1 value 6 for 448
-    const float scale = static_cast<float>(static_cast<double>(amax) / 6.0);
+    const float scale = amax / 6.0f;
     uint32_t c01 = 0, c23 = 0;
     if (scale > 0.0f) {
       const double inv = 1.0 / static_cast<double>(scale);
@@ -198,8 +184,10 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
     float amax = fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3)));
     amax = half_wave_max(amax);
     if (!ok) return;
-    // fp64 quotient of fp32 operands rounded once = the correctly rounded fp32 quotient.
-    const float scale = static_cast<float>(static_cast<double>(amax) / 448.0);
+    // The correctly rounded fp32 quotient (HIP's fp32 division is correctly rounded unless
+    // fast-math is asked for), which is also the fp64 quotient rounded once to fp32: 53 >= 2 x 24
+    // + 2 bits make that double rounding harmless.
+    const float scale = amax / 448.0f;
     uint32_t c01 = 0, c23 = 0;
     if (scale > 0.0f) {
       // RN32(k * RN64(1/scale)) equals RN32(k / scale): the fp64 product is within 2^-52
@@ -218,6 +206,44 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
     *reinterpret_cast<uint16_t*>(dst + 2 * j) = static_cast<uint16_t>(c01);
     *reinterpret_cast<uint16_t*>(dst + 64 + 2 * j) = static_cast<uint16_t>(c23);
     if (j == 0) *reinterpret_cast<float*>(pg + kFp8ScaleOffset + (s % kPageKeys) * 4) = scale;
+  }
+}
+
+// Half-wave h of the grid stores keys h U .. h U + U - 1 (U = kStoreKeysPerHalfWave).  Half-waves
+// past the end recompute the last key without storing it, so every lane takes part in the
+// half-wave reductions.
+template <int DT, bool HAD>
+__global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
+  constexpr int U = kStoreKeysPerHalfWave;
+  const int64_t hw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
+  const int j = threadIdx.x & 31;
+  int32_t bq[U], sq[U], page[U];
+  bool ok[U];
+  float2 xa[U], xb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t n_raw = hw * U + u;
+    ok[u] = n_raw < a.n_keys;
+    const int64_t n = ok[u] ? n_raw : a.n_keys - 1;
+    bq[u] = a.key_seq ? a.key_seq[n] : 0;
+    sq[u] = a.key_idx[n];
+    const float* xr = a.x + n * kHeadDim;
+    xa[u] = *reinterpret_cast<const float2*>(xr + 2 * j);
+    xb[u] = *reinterpret_cast<const float2*>(xr + 64 + 2 * j);
+  }
+  const float2 ga = *reinterpret_cast<const float2*>(a.gamma + 2 * j);
+  const float2 gb = *reinterpret_cast<const float2*>(a.gamma + 64 + 2 * j);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t b = bq[u], s = sq[u];
+    ok[u] = ok[u] && b >= 0 && b < a.n_seq && s >= 0 &&
+            static_cast<int64_t>(s) < static_cast<int64_t>(a.max_pages) * kPageKeys;
+    page[u] = ok[u] ? a.page_table[static_cast<int64_t>(b) * a.max_pages + s / kPageKeys] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool okp = ok[u] && page[u] >= 0 && page[u] < a.n_pages_pool;
+    store_one<DT, HAD>(a, j, okp, page[u], sq[u], xa[u], xb[u], ga, gb);
   }
 }
 
@@ -367,7 +393,7 @@ hipError_t launch_quantize_q(const uint16_t* q, uint8_t* codes, float* scales, i
 
 hipError_t launch_store(const StoreArgs& a, int dtype, bool hadamard, hipStream_t stream) {
   if (a.n_keys <= 0) return hipSuccess;
-  const int64_t keys_per_block = 256 / 32;
+  const int64_t keys_per_block = 256 / 32 * kStoreKeysPerHalfWave;
   const dim3 grid(static_cast<uint32_t>((a.n_keys + keys_per_block - 1) / keys_per_block));
   if (dtype == kBf16 && hadamard)
     hipLaunchKernelGGL((store_keys_kernel<kBf16, true>), grid, dim3(256), 0, stream, a);
