@@ -85,6 +85,16 @@ def check_logits(gpu_rows: np.ndarray, ora_rows: np.ndarray, what: str):
     return float(err.max()) if err.size else 0.0
 
 
+def tolerance_ratio(gpu_rows: np.ndarray, ora_rows: np.ndarray) -> float:
+    """Largest |gpu - oracle| / (ATOL + RTOL |oracle|) over the finite entries: how much of the
+    logit tolerance the worst entry uses (check_logits requires it to stay within 1)."""
+    fin = np.isfinite(ora_rows)
+    if not fin.any():
+        return 0.0
+    o = ora_rows[fin]
+    return float(np.max(np.abs(gpu_rows[fin].astype(np.float64) - o) / (ATOL + RTOL * np.abs(o))))
+
+
 def check_topk_sets(gpu_idx: np.ndarray, ora_logits: np.ndarray, n_vis: np.ndarray, k: int,
                     what: str, min_overlap: float = 0.999):
     """Top-k sets against fp64 oracle logits.

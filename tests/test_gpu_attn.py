@@ -72,7 +72,8 @@ def _rows(n_q, n, seed):
 
 
 @pytest.mark.parametrize("cfg,n_heads,n_rows", [(0, 64, 48), (2, 64, None), (4, 64, None),
-                                                (3, 64, 24), (0, 128, 24), (2, 32, None)])
+                                                (3, 64, 24), (0, 128, 24), (2, 32, None),
+                                                (4, 128, None), (2, 128, None)])
 def test_attn_vs_oracle(oracle_mod, cfg, n_heads, n_rows):
     """The measured shapes: prefill rows (one workgroup per row and head block) and decode rows
     (lists split over several workgroups, then merged), 32, 64 and 128 heads."""
@@ -188,13 +189,16 @@ def test_attn_repeatable():
     assert np.array_equal(g1, g2) and np.array_equal(l1, l2)
 
 
-def test_attn_split_lists_with_empty_splits(oracle_mod):
-    """Few rows, so every list is split and merged: the first half of each list is padding, so the
-    first splits hold no key (the merge starts from the later ones), some rows hold nothing at all,
-    and one row's only valid entries sit in its last split."""
+@pytest.mark.parametrize("n_heads", [64, 128])
+def test_attn_split_lists_with_empty_splits(oracle_mod, n_heads):
+    """Few rows, so every list is split and merged (with 128 heads, in two head blocks per row):
+    the first half of each list is padding, so the first splits hold no key (the merge starts
+    from the later ones), some rows hold nothing at all, and one row's only valid entries sit in
+    its last split."""
     wl = workload(4)                                   # 32 decode rows, 1024 listed keys
-    a = W.attn_inputs(wl)
-    assert ix.sparse_attn_workspace_size(wl.n_q, 64, a.idx.shape[1]) > 0, "lists must be split"
+    a = W.attn_inputs(wl, n_heads=n_heads)
+    assert ix.sparse_attn_workspace_size(wl.n_q, n_heads, a.idx.shape[1]) > 0, \
+        "lists must be split"
     idx = a.idx.copy()
     k = idx.shape[1]
     idx[:, : k // 2] = -1

@@ -6,13 +6,17 @@
    (the 8192-query prefill batch on sampled rows), ragged batches and out-of-pool pages.
 3. Top-k against the oracle under R19, and equal to the selection over the dense logits.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import sparse_attention_indexer_rmsnorm_amd as ix
 import workloads as W
-from tests.helpers import by_index, check_logits, check_topk_sets, dev_inputs, gpu_store, workload
+from tests.helpers import (by_index, check_logits, check_topk_sets, dev_inputs, gpu_store,
+                           tolerance_ratio, workload)
 
 pytestmark = pytest.mark.gpu
 FP8 = W.FP8
@@ -42,7 +46,7 @@ def test_quantize_q_bit_exact(oracle_mod):
     assert np.array_equal(scales.cpu().numpy(), os_)
 
 
-@pytest.mark.parametrize("cfg,n_rows", [(0, None), (2, None), (3, 40), (4, None)])
+@pytest.mark.parametrize("cfg,n_rows", [(0, None), (2, None), (3, 1024), (4, None)])
 def test_dense_fp8q_vs_oracle(oracle_mod, cfg, n_rows):
     wl = workload(cfg)
     print(f"fp8q dense cfg{cfg}", flush=True)
@@ -58,7 +62,24 @@ def test_dense_fp8q_vs_oracle(oracle_mod, cfg, n_rows):
     o, _ = oracle_mod.logits_fp8q(oc, os_, wl.w, pool_o, wl.page_table, wl.seq_lens, wl.cu_q,
                                   rows=rows, row_len=wl.max_keys)
     err = check_logits(dense[rows], o, f"fp8q cfg{cfg}")
-    print(f"  max abs err {err:.3g}", flush=True)
+    ratio = tolerance_ratio(dense[rows], o)
+    # the fp8 matrix cores add a product error the bf16 path does not have (about 8e-4 absolute
+    # on logits up to 45); report how much of the tolerance it uses
+    print(f"  max abs err {err:.3g}, max err / tolerance {ratio:.3f}", flush=True)
+    _report(f"cfg{cfg}", {"rows": int(rows.size), "max_abs_err": err, "max_err_over_tol": ratio})
+    assert ratio < 1.0
+
+
+def _report(key, value):
+    """Append to fp8q_error.json under INDEXER_REPORT_DIR (when set)."""
+    path = os.environ.get("INDEXER_REPORT_DIR")
+    if not path:
+        return
+    os.makedirs(path, exist_ok=True)
+    f = os.path.join(path, "fp8q_error.json")
+    data = json.load(open(f)) if os.path.exists(f) else {}
+    data[key] = value
+    json.dump(data, open(f, "w"), indent=1)
 
 
 def test_dense_fp8q_ragged_and_bad_pages(oracle_mod):

@@ -38,16 +38,15 @@ def test_dense_logits_all_rows(oracle_mod, cfg, dtype):
     check_logits(g, o, f"cfg{cfg}")
 
 
-@pytest.mark.parametrize("cfg,dtype,n_rows", [(3, BF16, 40), (4, FP8, 8), (4, BF16, 8)])
-def test_dense_logits_sampled_rows(oracle_mod, cfg, dtype, n_rows):
-    """Full-size batch on the GPU; the oracle recomputes a sample of rows (first, last, spread)."""
+@pytest.mark.parametrize("cfg,dtype,stride", [(3, BF16, 8), (4, FP8, 1), (4, BF16, 1)])
+def test_dense_logits_sampled_rows(oracle_mod, cfg, dtype, stride):
+    """Full-size batch on the GPU; the oracle recomputes every stride-th row and the last one
+    (1,025 of the long prefill chunk's 8,192 rows; every row of the 32-row decode batch)."""
     wl = workload(cfg)
-    print(f"dense cfg{cfg} dtype={dtype} sampled {n_rows} of {wl.n_q}", flush=True)
+    rows = np.unique(np.concatenate([np.arange(0, wl.n_q, stride), [wl.n_q - 1]]))
+    print(f"dense cfg{cfg} dtype={dtype} rows {rows.size} of {wl.n_q}", flush=True)
     pool = _oracle_pool(oracle_mod, wl, dtype)
     g = _dense(wl, dev_inputs(wl), pool, dtype)
-    rows = np.unique(np.concatenate([[0, wl.n_q - 1],
-                                     np.random.default_rng(cfg).choice(wl.n_q, n_rows - 2,
-                                                                       replace=False)]))
     o, _ = oracle_rows(oracle_mod, wl, pool, dtype, rows)
     check_logits(g[torch.from_numpy(rows).cuda()].cpu().numpy(), o, f"cfg{cfg}")
 
