@@ -71,6 +71,58 @@ __device__ __forceinline__ int32_t seq_of_row(const int32_t* cu_q, int32_t n_seq
   return i < cu_q[lo + 1] ? lo : -1;
 }
 
+// Sequence b of flattened query row i and its context length, for the split kernel: with at most
+// 256 sequences every lane loads its share of cu_q and seq_lens at once and a ballot counts the
+// sequences starting at or before i (one memory round trip instead of a dependent binary
+// search); longer batches take the binary search.  b = -1 when i lies in no sequence.
+__device__ __forceinline__ void row_sequence(const int32_t* cu_q, const int32_t* seq_lens,
+                                             int32_t n_seq, int64_t i, int32_t* b_out,
+                                             int64_t* q_len_out, int64_t* row_in_seq,
+                                             int32_t* len_out) {
+  if (n_seq > 256) {
+    const int32_t b = seq_of_row(cu_q, n_seq, i);
+    *b_out = b;
+    if (b >= 0) {
+      *q_len_out = cu_q[b + 1] - cu_q[b];
+      *row_in_seq = i - cu_q[b];
+      *len_out = seq_lens[b];
+    }
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  int32_t c[4], nxt[4], len[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane + 64 * u;
+    c[u] = e < n_seq ? cu_q[e] : INT32_MAX;
+    nxt[u] = e < n_seq ? cu_q[e + 1] : 0;
+    len[u] = e < n_seq ? seq_lens[e] : 0;
+  }
+  int32_t count = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) count += __popcll(__ballot(static_cast<int64_t>(c[u]) <= i));
+  const int32_t b = count - 1;           // cu_q is non-decreasing: the last b with cu_q[b] <= i
+  if (b < 0) {
+    *b_out = -1;
+    return;
+  }
+  const int src = b & 63, u_b = b >> 6;
+  int32_t cb = 0, cn = 0, lb = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int32_t vc = __builtin_amdgcn_readlane(c[u], src);
+    const int32_t vn = __builtin_amdgcn_readlane(nxt[u], src);
+    const int32_t vl = __builtin_amdgcn_readlane(len[u], src);
+    cb = u == u_b ? vc : cb;
+    cn = u == u_b ? vn : cn;
+    lb = u == u_b ? vl : lb;
+  }
+  *b_out = i < cn ? b : -1;
+  *q_len_out = cn - cb;
+  *row_in_seq = i - cb;
+  *len_out = lb;
+}
+
 // ReLU of a finite float as one integer max: a set sign bit makes the pattern a negative int32,
 // which max(., 0) maps to +0; non-negative floats are unchanged.  (A float max would first have
 // to quieten NaNs in IEEE mode, costing a second instruction.)
@@ -113,6 +165,15 @@ template <>
 struct KeyBlock<kBf16> {
   u32x4 raw[8];
   float scale;
+  // Unconditional load (the caller passes an in-range page and slot for keys it will not use, so
+  // that no branch separates the loads of successive blocks).
+  __device__ __forceinline__ void load_any(const uint8_t* kcache, int32_t page, int slot, int g) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        kcache + page * kBf16PageBytes + slot * (kHeadDim * 2) + 128 * g);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) raw[jj] = src[jj];
+    scale = 1.0f;
+  }
   __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int slot, int g, bool ok) {
     if (ok) {
       const u32x4* src = reinterpret_cast<const u32x4*>(
@@ -135,6 +196,13 @@ template <>
 struct KeyBlock<kFp8> {
   u32x4 raw[4];
   float scale;
+  __device__ __forceinline__ void load_any(const uint8_t* kcache, int32_t page, int slot, int g) {
+    const uint8_t* pg = kcache + page * kFp8PageBytes;
+    const u32x4* src = reinterpret_cast<const u32x4*>(pg + slot * kHeadDim + 64 * g);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = src[c];
+    scale = *reinterpret_cast<const float*>(pg + kFp8ScaleOffset + slot * 4);
+  }
   __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int slot, int g, bool ok) {
     if (ok) {
       const uint8_t* pg = kcache + page * kFp8PageBytes;
@@ -166,6 +234,13 @@ template <>
 struct KeyBlock<kFp4> {
   u32x4 raw[2];
   float scale;
+  __device__ __forceinline__ void load_any(const uint8_t* kcache, int32_t page, int slot, int g) {
+    const uint8_t* pg = kcache + page * kFp4PageBytes;
+    const u32x4* src = reinterpret_cast<const u32x4*>(pg + slot * (kHeadDim / 2) + 32 * g);
+    raw[0] = src[0];
+    raw[1] = src[1];
+    scale = *reinterpret_cast<const float*>(pg + kFp4ScaleOffset + slot * 4);
+  }
   __device__ __forceinline__ void load(const uint8_t* kcache, int32_t page, int slot, int g, bool ok) {
     if (ok) {
       const uint8_t* pg = kcache + page * kFp4PageBytes;
@@ -224,19 +299,31 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int64_t i, int32
   auto page_ok = [&](int32_t page) { return page >= 0 && page < a.n_pages_pool; };
   // Key block s0 .. s0+31 (32-aligned, so inside one page): lane (m, g) holds key s0 + m.  Two
   // blocks are in flight while one is multiplied (decode batches are bound by the key bytes in
-  // flight); page ids (wave-uniform scalar loads) run one block further ahead.
-  KeyBlock<DT> b0, b1, b2;
-  auto pg_of = [&](int32_t s0) { return s0 < s_end ? load_uniform(pt_row + s0 / kPageKeys) : -1; };
-  int32_t p0 = pg_of(c_begin), p1 = pg_of(c_begin + 32), p2 = pg_of(c_begin + 64);
-  bool ok0 = page_ok(p0), ok1 = page_ok(p1), ok2;
-  b0.load(a.kcache, p0, (c_begin + m) % kPageKeys, g, ok0 && c_begin + m < s_end);
-  b1.load(a.kcache, p1, (c_begin + 32 + m) % kPageKeys, g, ok1 && c_begin + 32 + m < s_end);
-  for (int32_t s0 = c_begin; s0 < s_end; s0 += 32) {
-    ok2 = page_ok(p2);
-    if (s0 + 64 < s_end) b2.load(a.kcache, p2, (s0 + 64 + m) % kPageKeys, g, ok2 && s0 + 64 + m < s_end);
-    const int32_t p3 = pg_of(s0 + 96);
+  // flight); page ids (wave-uniform scalar loads) run one block further ahead.  The three block
+  // buffers and page ids rotate by unrolling the loop three times: copying a register whose load
+  // is still in flight would make the wave wait for every load it has outstanding.
+  // Every load is issued unconditionally: page ids at a clamped in-range table index, key rows
+  // that are not used (past the chunk, or on a page outside the pool) from page 0, slot 0.  A
+  // branch around some loads would make the compiler's wait for one block conservative enough to
+  // wait for the blocks behind it.  The scores of unused keys are never stored, and a block on an
+  // invalid page scores -inf whatever its data.
+  KeyBlock<DT> kb0, kb1, kb2;
+  bool ok[3];
+  int32_t pid[3];
+  auto pg_of = [&](int32_t s0) { return load_uniform(pt_row + min(s0, s_end - 1) / kPageKeys); };
+  auto load_block = [&](KeyBlock<DT>& blk, int32_t s0, int32_t page, bool& okb) {
+    okb = page_ok(page);
+    const bool use = okb && s0 + m < s_end;
+    blk.load_any(a.kcache, use ? page : 0, use ? (s0 + m) % kPageKeys : 0, g);
+  };
+  // One block: score block s0 from `cur`, request block s0 + 64 into `nxt` (its page id was read
+  // a block ago into pid[in]) and read the page id of block s0 + 96 into pid[out].
+  auto step = [&](int32_t s0, const KeyBlock<DT>& cur, bool ok_cur, KeyBlock<DT>& nxt,
+                  bool& ok_nxt, int in, int out) {
+    load_block(nxt, s0 + 64, pid[in], ok_nxt);
+    pid[out] = pg_of(s0 + 96);
     Frag kb[8];
-    b0.frags(kb);
+    cur.frags(kb);
     floatx16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -244,16 +331,25 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int64_t i, int32
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][jj].v, kb[jj].v, acc1, 0, 0, 0);
     }
     float tot = head_sum(acc0, acc1, wv);
-    if constexpr (DT != kBf16) tot *= b0.scale;
+    if constexpr (DT != kBf16) tot *= cur.scale;
     const int32_t s = s0 + m;
-    const float v = ok0 ? tot : -INFINITY;
+    const float v = ok_cur ? tot : -INFINITY;
     if (g == 0 && s < s_end) {
       out_row[s] = v;
       if constexpr (HIST) atomicAdd(&hist[score_order_key(v) >> kHistShift], 1u);
     }
-    b0 = b1; ok0 = ok1;
-    b1 = b2; ok1 = ok2;
-    p2 = p3;
+  };
+  pid[0] = pg_of(c_begin);
+  pid[1] = pg_of(c_begin + 32);
+  load_block(kb0, c_begin, pid[0], ok[0]);
+  load_block(kb1, c_begin + 32, pid[1], ok[1]);
+  pid[2] = pg_of(c_begin + 64);
+  for (int32_t s0 = c_begin; s0 < s_end; s0 += 96) {
+    step(s0, kb0, ok[0], kb2, ok[2], 2, 0);
+    if (s0 + 32 >= s_end) break;
+    step(s0 + 32, kb1, ok[1], kb0, ok[0], 0, 1);
+    if (s0 + 64 >= s_end) break;
+    step(s0 + 64, kb2, ok[2], kb1, ok[1], 1, 2);
   }
 }
 
@@ -285,11 +381,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int64_t i = a.q_begin + r;
 
   // Query position and visible-key count.
-  const int32_t b = seq_of_row(a.cu_q, a.n_seq, i);
+  int32_t b, len = 0;
+  int64_t q_len = 0, row_in_seq = 0;
+  row_sequence(a.cu_q, a.seq_lens, a.n_seq, i, &b, &q_len, &row_in_seq, &len);
+  b = __builtin_amdgcn_readfirstlane(b);
   int64_t n_vis = 0;
   if (b >= 0) {
-    const int64_t q_len = a.cu_q[b + 1] - a.cu_q[b];
-    const int64_t t = static_cast<int64_t>(a.seq_lens[b]) - q_len + (i - a.cu_q[b]);
+    const int64_t t = static_cast<int64_t>(len) - q_len + row_in_seq;
     if (t >= 0) {
       n_vis = (t + 1) / kRatio;
       const int64_t cap = static_cast<int64_t>(a.max_pages) * kPageKeys;
@@ -305,7 +403,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   if (a.fill_invisible) {
     for (int32_t s = max(c_begin, s_end) + lane; s < c_end; s += 64) out_row[s] = -INFINITY;
   }
-  if (c_begin < s_end) score_chunk<DT, HIST>(a, i, b, c_begin, s_end, out_row, hist);
+  if (c_begin < s_end) {
+    if (a.n_pages_pool > 0) {
+      score_chunk<DT, HIST>(a, i, b, c_begin, s_end, out_row, hist);
+    } else {   // no page in the pool: every visible key scores -inf
+      for (int32_t s = c_begin + lane; s < s_end; s += 64) {
+        out_row[s] = -INFINITY;
+        if constexpr (HIST) atomicAdd(&hist[score_order_key(-INFINITY) >> kHistShift], 1u);
+      }
+    }
+  }
 
   if constexpr (HIST) {
     __syncthreads();
