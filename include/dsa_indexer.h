@@ -90,8 +90,8 @@ size_t idx_page_bytes(int dtype);
  *         an all-zero key stores scale 0 and codes 0
  * and writes the key to slot s % 64 of page page_table[b * max_pages + s / 64] of `kcache`.
  *
- * x          device fp32 [n_keys, 128], row-major
- * gamma      device fp32 [128]
+ * x          device fp32 [n_keys, 128], row-major, 16-byte aligned
+ * gamma      device fp32 [128], 16-byte aligned
  * eps        RMSNorm epsilon (added to the mean square)
  * key_idx    device int32 [n_keys]
  * key_seq    device int32 [n_keys], or NULL: every key belongs to sequence 0
@@ -100,8 +100,8 @@ size_t idx_page_bytes(int dtype);
  *            fp8, their scale words) are written
  * Rows whose sequence, key index (>= max_pages * 64) or page id (outside [0, n_pages_pool)) is out
  * of range are skipped.  Two rows that address the same slot race.  n_keys == 0 is a no-op.
- * Errors: IDX_EINVAL (null pointer with n_keys > 0, n_keys/n_seq/max_pages/n_pages_pool < 0 or
- * eps < 0), IDX_EUNSUPPORTED (unknown dtype), IDX_EHIP.
+ * Errors: IDX_EINVAL (null pointer or misaligned x / gamma / kcache with n_keys > 0,
+ * n_keys/n_seq/max_pages/n_pages_pool < 0 or eps < 0), IDX_EUNSUPPORTED (unknown dtype), IDX_EHIP.
  */
 int idx_store_keys(const float* x, const float* gamma, float eps, const int32_t* key_idx,
                    const int32_t* key_seq, int64_t n_keys, const int32_t* page_table,

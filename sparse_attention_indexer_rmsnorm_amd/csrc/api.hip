@@ -332,6 +332,8 @@ static int store_keys(const float* x, const float* gamma, float eps, const int32
   if (!dtype_ok(dtype)) return IDX_EUNSUPPORTED;
   if (n_keys == 0) return IDX_OK;
   if (!x || !gamma || !key_idx || !page_table || !kcache) return IDX_EINVAL;
+  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (misaligned(x) || misaligned(gamma) || misaligned(kcache)) return IDX_EINVAL;
   if (n_keys > (static_cast<int64_t>(INT32_MAX) - 255) / 8 * 8) return IDX_EINVAL;
   StoreArgs a{};
   a.x = x;

@@ -12,11 +12,14 @@
 // normalised 128-point Walsh-Hadamard matrix after RoPE, before the rounding; q goes through the
 // same map (rotate_q_kernel), so q.k is kept.
 //
-// Work mapping: one half-wave (32 lanes) per key.  Lane j owns the unrotated dims 2j, 2j+1 and the
-// rotated pair (64+2j, 65+2j), so every lane evaluates exactly one sincos.  The arithmetic before
-// the format rounding is fp64 so that the stored bytes are a function of the inputs alone, not of
-// the reduction order: a result only depends on the order when it sits within ~2^-50 of a
-// rounding boundary.  The work is HBM-bound (512 B read and 132/256 B written per key).
+// Work mapping: four lanes (a quad) per key.  The key's 128 dims are 8 chunks of 16; lane l owns
+// dims 16 i + 4 l .. 16 i + 4 l + 3 of every chunk i, so each load and store instruction covers a
+// contiguous 64-byte (activations) or 16-, 32- or 8-byte (codes) span per key, and the per-key
+// work (the norm's square root and division, the fp8 scale and its reciprocal) is repeated by 4
+// lanes instead of 32.  Chunks 4..7 are the rotated half: lane l holds the RoPE pairs 8 (i - 4) +
+// 2 l and 8 (i - 4) + 2 l + 1.  The arithmetic before the format rounding is fp64 so that the
+// stored bytes are a function of the inputs alone, not of the reduction order: a result only
+// depends on the order when it sits within ~2^-50 of a rounding boundary.
 #include "internal.h"
 
 namespace dsa {
@@ -28,224 +31,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Round a finite fp32 to OCP e4m3fn (bias 7, max 448, no inf), nearest-even, saturating to 448.
-// Normal range [2^-6, 448): keep 3 mantissa bits of the fp32 significand with round-half-even;
-// a carry out of the mantissa moves to the next binade by plain addition of the code.
-// Subnormal range [0, 2^-6): the code is the integer round-half-even of |v| * 2^9 (8 = 2^-6).
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  } else {
-    const uint32_t ua = __float_as_uint(a);
-    const uint32_t e = (ua >> 23) - 120u;
-    const uint32_t m = ua & 0x7FFFFFu;
-    const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
-    code = (e << 3) + r;
-    code = code > 0x7Eu ? 0x7Eu : code;
-  }
-  return code | sign;
-}
-
-// Round a finite fp32 to OCP e2m1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; largest
-// 6), nearest-even, saturating to 6.  |v| >= 1: keep 1 mantissa bit with round-half-even, a carry
-// moving to the next binade by plain addition of the code; |v| < 1: the code is the integer
-// round-half-even of |v| * 2 (0, 0.5 or 1.0).  Without branches.
-__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
-  const float a = fabsf(v);
-  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(a * 2.0f));
-  const uint32_t ua = __float_as_uint(a);
-  const uint32_t m = ua & 0x7FFFFFu;
-  const uint32_t r = (m + 0x1FFFFFu + ((m >> 22) & 1u)) >> 22;
-  const uint32_t nrm = min((((ua >> 23) - 126u) << 1) + r, 7u);
-  return (a < 1.0f ? sub : nrm) | sign;
-}
-
-template <typename T>
-__device__ __forceinline__ T half_wave_sum(T v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-__device__ __forceinline__ float half_wave_max(float v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
 // The nearest double to 2^-3.5 (sqrt(2) / 16): the normalisation of the 128-point transform.
 constexpr double kHadamardScale = 0x1.6a09e667f3bcdp-4;
-
-// Normalised 128-point Walsh-Hadamard transform (Sylvester order) of the vector a half-wave holds,
-// lane j (0..31) owning dims 2j, 2j+1 (v0, v1) and 64+2j, 65+2j (v2, v3).  Butterfly stages of
-// span h = 1, 2, ..., 64 map (x_i, x_{i+h}) to (x_i + x_{i+h}, x_i - x_{i+h}) for the i whose bit
-// h is clear; spans 1 and 64 pair values inside a lane, spans 2..32 pair lane j with lane
-// j ^ (h/2), the lower lane taking the sum and the upper one the difference.  The operations are
-// those of the definition, in a fixed order, so the fp64 result does not depend on the lane
-// mapping.  Then one multiplication by 2^-3.5.
-__device__ __forceinline__ void hadamard128(double& v0, double& v1, double& v2, double& v3,
-                                            int j) {
-#pragma clang fp contract(off)
-  double a = v0, b = v1;
-  v0 = a + b;
-  v1 = a - b;
-  a = v2;
-  b = v3;
-  v2 = a + b;
-  v3 = a - b;
-#pragma unroll
-  for (int m = 1; m <= 16; m <<= 1) {
-    const bool upper = (j & m) != 0;
-    const double p0 = __shfl_xor(v0, m, 64), p1 = __shfl_xor(v1, m, 64);
-    const double p2 = __shfl_xor(v2, m, 64), p3 = __shfl_xor(v3, m, 64);
-    v0 = upper ? p0 - v0 : v0 + p0;
-    v1 = upper ? p1 - v1 : v1 + p1;
-    v2 = upper ? p2 - v2 : v2 + p2;
-    v3 = upper ? p3 - v3 : v3 + p3;
-  }
-  a = v0;
-  b = v2;
-  v0 = a + b;
-  v2 = a - b;
-  a = v1;
-  b = v3;
-  v1 = a + b;
-  v3 = a - b;
-  v0 *= kHadamardScale;
-  v1 *= kHadamardScale;
-  v2 *= kHadamardScale;
-  v3 *= kHadamardScale;
-}
-
-// Keys per half-wave: all of them are requested (indices, activations, then page ids) before any
-// is computed, so a wave has several rows of activations in flight.
-constexpr int kStoreKeysPerHalfWave = 4;
-
-// One key (row n, sequence b, index s, activations xa/xb, destination page), computed and stored
-// by the 32 lanes of a half-wave; lane j owns dims 2j, 2j+1 and the rotated pair 64+2j, 65+2j.
-template <int DT, bool HAD>
-__device__ __forceinline__ void store_one(const StoreArgs& a, int j, bool ok, int32_t page,
-                                          int32_t s, float2 xa, float2 xb, float2 ga, float2 gb) {
-#pragma clang fp contract(off)
-  // RMSNorm in fp64.
-  const double x0 = xa.x, x1 = xa.y, x2 = xb.x, x3 = xb.y;
-  double ss = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
-  ss = half_wave_sum(ss);
-  const double r = 1.0 / sqrt(ss / 128.0 + static_cast<double>(a.eps));
-  double y0 = x0 * r * static_cast<double>(ga.x);
-  double y1 = x1 * r * static_cast<double>(ga.y);
-  double y2 = x2 * r * static_cast<double>(gb.x);
-  double y3 = x3 * r * static_cast<double>(gb.y);
-
-  // RoPE on the pair (64+2j, 65+2j) at position 4s.
-  const double phi = static_cast<double>(kRatio) * static_cast<double>(s < 0 ? 0 : s) *
-                     static_cast<double>(a.rope.f[j]);
-  double sn, cs;
-  sincos(phi, &sn, &cs);
-  double r2 = y2 * cs - y3 * sn;
-  double r3 = y2 * sn + y3 * cs;
-  // the rotated store: the Hadamard transform of the whole key, still in fp64
-  if constexpr (HAD) hadamard128(y0, y1, r2, r3, j);
-
-  const float k0 = static_cast<float>(y0), k1 = static_cast<float>(y1);
-  const float k2 = static_cast<float>(r2), k3 = static_cast<float>(r3);
-
-  if constexpr (DT == kBf16) {
-    if (!ok) return;
-    uint8_t* dst = a.kcache + page * kBf16PageBytes + (s % kPageKeys) * (kHeadDim * 2);
-    *reinterpret_cast<uint32_t*>(dst + 4 * j) = bf16_rne(k0) | (bf16_rne(k1) << 16);
-    *reinterpret_cast<uint32_t*>(dst + 128 + 4 * j) = bf16_rne(k2) | (bf16_rne(k3) << 16);
-  } else if constexpr (DT == kFp4) {
-    float amax = fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3)));
-    amax = half_wave_max(amax);
-    if (!ok) return;
-    // as for fp8 below, with the largest e2m1 value 6 for 448
-    const float scale = amax / 6.0f;
-    uint32_t c01 = 0, c23 = 0;
-    if (scale > 0.0f) {
-      const double inv = 1.0 / static_cast<double>(scale);
-      c01 = e2m1_rne_sat(static_cast<float>(static_cast<double>(k0) * inv)) |
-            (e2m1_rne_sat(static_cast<float>(static_cast<double>(k1) * inv)) << 4);
-      c23 = e2m1_rne_sat(static_cast<float>(static_cast<double>(k2) * inv)) |
-            (e2m1_rne_sat(static_cast<float>(static_cast<double>(k3) * inv)) << 4);
-    }
-    uint8_t* pg = a.kcache + page * kFp4PageBytes;
-    uint8_t* dst = pg + (s % kPageKeys) * (kHeadDim / 2);
-    dst[j] = static_cast<uint8_t>(c01);         // dims 2j, 2j+1: low, high nibble of byte j
-    dst[32 + j] = static_cast<uint8_t>(c23);    // dims 64+2j, 65+2j
-    if (j == 0) *reinterpret_cast<float*>(pg + kFp4ScaleOffset + (s % kPageKeys) * 4) = scale;
-  } else {
-    float amax = fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3)));
-    amax = half_wave_max(amax);
-    if (!ok) return;
-    // The correctly rounded fp32 quotient (HIP's fp32 division is correctly rounded unless
-    // fast-math is asked for), which is also the fp64 quotient rounded once to fp32: 53 >= 2 x 24
-    // + 2 bits make that double rounding harmless.
-    const float scale = amax / 448.0f;
-    uint32_t c01 = 0, c23 = 0;
-    if (scale > 0.0f) {
-      // RN32(k * RN64(1/scale)) equals RN32(k / scale): the fp64 product is within 2^-52
-      // (relative) of the exact quotient, while a quotient of two fp32 numbers is never closer
-      // than ~2^-49 (relative) to an fp32 rounding midpoint.
-      const double inv = 1.0 / static_cast<double>(scale);
-      const float v0 = static_cast<float>(static_cast<double>(k0) * inv);
-      const float v1 = static_cast<float>(static_cast<double>(k1) * inv);
-      const float v2 = static_cast<float>(static_cast<double>(k2) * inv);
-      const float v3 = static_cast<float>(static_cast<double>(k3) * inv);
-      c01 = e4m3_rne_sat(v0) | (e4m3_rne_sat(v1) << 8);
-      c23 = e4m3_rne_sat(v2) | (e4m3_rne_sat(v3) << 8);
-    }
-    uint8_t* pg = a.kcache + page * kFp8PageBytes;
-    uint8_t* dst = pg + (s % kPageKeys) * kHeadDim;
-    *reinterpret_cast<uint16_t*>(dst + 2 * j) = static_cast<uint16_t>(c01);
-    *reinterpret_cast<uint16_t*>(dst + 64 + 2 * j) = static_cast<uint16_t>(c23);
-    if (j == 0) *reinterpret_cast<float*>(pg + kFp8ScaleOffset + (s % kPageKeys) * 4) = scale;
-  }
-}
-
-// Half-wave h of the grid stores keys h U .. h U + U - 1 (U = kStoreKeysPerHalfWave).  Half-waves
-// past the end recompute the last key without storing it, so every lane takes part in the
-// half-wave reductions.
-template <int DT, bool HAD>
-__global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
-  constexpr int U = kStoreKeysPerHalfWave;
-  const int64_t hw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
-  const int j = threadIdx.x & 31;
-  int32_t bq[U], sq[U], page[U];
-  bool ok[U];
-  float2 xa[U], xb[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t n_raw = hw * U + u;
-    ok[u] = n_raw < a.n_keys;
-    const int64_t n = ok[u] ? n_raw : a.n_keys - 1;
-    bq[u] = a.key_seq ? a.key_seq[n] : 0;
-    sq[u] = a.key_idx[n];
-    const float* xr = a.x + n * kHeadDim;
-    xa[u] = *reinterpret_cast<const float2*>(xr + 2 * j);
-    xb[u] = *reinterpret_cast<const float2*>(xr + 64 + 2 * j);
-  }
-  const float2 ga = *reinterpret_cast<const float2*>(a.gamma + 2 * j);
-  const float2 gb = *reinterpret_cast<const float2*>(a.gamma + 64 + 2 * j);
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int32_t b = bq[u], s = sq[u];
-    ok[u] = ok[u] && b >= 0 && b < a.n_seq && s >= 0 &&
-            static_cast<int64_t>(s) < static_cast<int64_t>(a.max_pages) * kPageKeys;
-    page[u] = ok[u] ? a.page_table[static_cast<int64_t>(b) * a.max_pages + s / kPageKeys] : -1;
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool okp = ok[u] && page[u] >= 0 && page[u] < a.n_pages_pool;
-    store_one<DT, HAD>(a, j, okp, page[u], sq[u], xa[u], xb[u], ga, gb);
-  }
-}
 
 // Value of lane (lane ^ M) of the same quad, M = 1 or 2 (DPP quad permutation; no LDS).
 template <int M>
@@ -318,9 +105,15 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(const uint16_t* in, uint1
   }
 }
 
-// e4m3_rne_sat without branches (the same code for every finite input of magnitude <= 2^15):
-// the normal-range and subnormal-range codes are both formed and one is selected, so lanes of
-// different magnitudes do not split the wave.
+typedef float float2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round a finite fp32 of magnitude <= 2^15 to OCP e4m3fn (bias 7, max 448, no inf), nearest-even,
+// saturating to 448.  Normal range [2^-6, 448): keep 3 mantissa bits of the fp32 significand with
+// round-half-even, a carry out of the mantissa moving to the next binade by plain addition of the
+// code.  Subnormal range [0, 2^-6): the code is the integer round-half-even of |v| * 2^9 (8 =
+// 2^-6).  Both codes are formed and one is selected, so lanes of different magnitudes do not split
+// the wave.
 __device__ __forceinline__ uint32_t e4m3_rne_sat_nb(float v) {
   const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
   const float a = fabsf(v);
@@ -381,6 +174,233 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* q, uint
   if (l == 0) scales[v] = scale;
 }
 
+// Value of quad lane (lane ^ M), fp32 bits.
+template <int M>
+__device__ __forceinline__ uint32_t quad_xor_u32(uint32_t v) {
+  constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+
+// One butterfly stage of span 4 (M = 1) or 8 (M = 2) across the quad: lane l pairs with l ^ M,
+// the lower lane taking x_i + x_{i+h} and the upper one x_i - x_{i+h}.
+template <int M>
+__device__ __forceinline__ void quad_butterfly(double (&v)[8][4], int l) {
+#pragma clang fp contract(off)
+  const bool upper = (l & M) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const double p = quad_xor<M>(v[i][c]);
+      v[i][c] = upper ? p - v[i][c] : v[i][c] + p;
+    }
+}
+
+// Normalised 128-point Walsh-Hadamard transform (Sylvester order) of the key a quad holds, lane l
+// holding dim 16 i + 4 l + c in v[i][c].  Stages of span h = 1, 2, ..., 64 map (x_d, x_{d+h}) to
+// (x_d + x_{d+h}, x_d - x_{d+h}) for the d whose bit h is clear: spans 1 and 2 are bits of c,
+// spans 4 and 8 bits of l, spans 16, 32 and 64 bits of i.  Every output is the same single
+// addition or subtraction of the same two values as in the definition, in stage order, so the
+// fp64 result does not depend on the lane mapping.  Then one multiplication by 2^-3.5.
+__device__ __forceinline__ void hadamard128_quad(double (&v)[8][4], int l) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    double a = v[i][0], b = v[i][1];
+    v[i][0] = a + b;
+    v[i][1] = a - b;
+    a = v[i][2];
+    b = v[i][3];
+    v[i][2] = a + b;
+    v[i][3] = a - b;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    double a = v[i][0], b = v[i][2];
+    v[i][0] = a + b;
+    v[i][2] = a - b;
+    a = v[i][1];
+    b = v[i][3];
+    v[i][1] = a + b;
+    v[i][3] = a - b;
+  }
+  quad_butterfly<1>(v, l);
+  quad_butterfly<2>(v, l);
+#pragma unroll
+  for (int h = 1; h <= 4; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double a = v[i][c], b = v[i + h][c];
+        v[i][c] = a + b;
+        v[i + h][c] = a - b;
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[i][c] *= kHadamardScale;
+}
+
+// Quad q of the grid stores key q.  Quads past the end leave (whole quads together, so the quad
+// exchanges stay inside live quads); keys with a bad sequence, index or page are computed and not
+// stored.  (Two keys per quad, each wave overlapping its loads of the second key with the
+// arithmetic of the first, measured no faster and needed 230-256 registers.)
+template <int DT, bool HAD>
+__global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
+#pragma clang fp contract(off)
+  const int64_t n = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 2;
+  const int l = threadIdx.x & 3;
+  if (n >= a.n_keys) return;
+  const int32_t b = a.key_seq ? a.key_seq[n] : 0;
+  const int32_t s = a.key_idx[n];
+  float4 xv[8];
+  const float* xr = a.x + n * kHeadDim + 4 * l;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i] = *reinterpret_cast<const float4*>(xr + 16 * i);
+  bool ok = b >= 0 && b < a.n_seq && s >= 0 &&
+            static_cast<int64_t>(s) < static_cast<int64_t>(a.max_pages) * kPageKeys;
+  const int32_t page = ok ? a.page_table[static_cast<int64_t>(b) * a.max_pages + s / kPageKeys]
+                          : -1;
+  ok = ok && page >= 0 && page < a.n_pages_pool;
+  float4 gv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gv[i] = *reinterpret_cast<const float4*>(a.gamma + 16 * i + 4 * l);
+  // The frequencies of the lane's pairs p = 8 (t / 2) + 2 l + t % 2, all read here, ahead of the
+  // arithmetic: read inside the RoPE, each would be a load that its sincos waits for.
+  float fr[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int p0 = 8 * (t / 2) + (t % 2);   // the pair of lane 0
+    fr[t] = l < 2 ? (l == 0 ? a.rope.f[p0] : a.rope.f[p0 + 2])
+                  : (l == 2 ? a.rope.f[p0 + 4] : a.rope.f[p0 + 6]);
+  }
+
+  // RMSNorm in fp64: the squares of fp32 values are exact, summed in the lane, then the quad.
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double x0 = xv[i].x, x1 = xv[i].y, x2 = xv[i].z, x3 = xv[i].w;
+    ss = ss + x0 * x0;
+    ss = ss + x1 * x1;
+    ss = ss + x2 * x2;
+    ss = ss + x3 * x3;
+  }
+  ss = ss + quad_xor<1>(ss);
+  ss = ss + quad_xor<2>(ss);
+  const double r = 1.0 / sqrt(ss / 128.0 + static_cast<double>(a.eps));
+
+  // RoPE on the pairs (64 + 2p, 65 + 2p) at position 4s, p = 8 (i - 4) + 2 l + c / 2.
+  const double pos = static_cast<double>(kRatio) * static_cast<double>(s < 0 ? 0 : s);
+  auto chunk = [&](int i, double (&y)[4]) {
+    y[0] = static_cast<double>(xv[i].x) * r * static_cast<double>(gv[i].x);
+    y[1] = static_cast<double>(xv[i].y) * r * static_cast<double>(gv[i].y);
+    y[2] = static_cast<double>(xv[i].z) * r * static_cast<double>(gv[i].z);
+    y[3] = static_cast<double>(xv[i].w) * r * static_cast<double>(gv[i].w);
+    if (i < 4) return;
+#pragma unroll
+    for (int c = 0; c < 4; c += 2) {
+      double sn, cs;
+      sincos(pos * static_cast<double>(fr[2 * (i - 4) + c / 2]), &sn, &cs);
+      const double ye = y[c], yo = y[c + 1];
+      y[c] = ye * cs - yo * sn;
+      y[c + 1] = ye * sn + yo * cs;
+    }
+  };
+  float k[8][4];
+  if constexpr (HAD) {
+    // the rotated store: the Hadamard transform of the whole key, still in fp64
+    double v[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) chunk(i, v[i]);
+    hadamard128_quad(v, l);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) k[i][c] = static_cast<float>(v[i][c]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      double y[4];
+      chunk(i, y);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) k[i][c] = static_cast<float>(y[c]);
+    }
+  }
+
+  const int slot = s % kPageKeys;
+  // The format conversions are the hardware's (v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32,
+  // v_cvt_scalef32_pk_fp4_f32 with scale 1): each rounds to nearest even, gives subnormal codes
+  // and keeps the sign of zero, and agrees with the integer round-half-even encoders (bf16_rne
+  // and e4m3_rne_sat_nb above, and the same construction with one mantissa bit for e2m1) on every
+  // fp32 input of the ranges used here (checked exhaustively on gfx950).  Quotients stay within 448 (1 + 2^-23) (fp8) or
+  // 6 (1 + 2^-23) (fp4), which round to the largest finite code, so no saturation is needed.
+  if constexpr (DT == kBf16) {
+    if (!ok) return;
+    uint8_t* dst = a.kcache + page * kBf16PageBytes + slot * (kHeadDim * 2) + 8 * l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x2 lo = __builtin_convertvector(float2_v{k[i][0], k[i][1]}, bf16x2);
+      const bf16x2 hi = __builtin_convertvector(float2_v{k[i][2], k[i][3]}, bf16x2);
+      *reinterpret_cast<uint2*>(dst + 32 * i) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
+  } else {
+    // |k| as bit patterns: the max of non-negative floats is the max of their patterns
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) am = max(am, __float_as_uint(k[i][c]) & 0x7FFFFFFFu);
+    am = max(am, quad_xor_u32<1>(am));
+    am = max(am, quad_xor_u32<2>(am));
+    if (!ok) return;
+    const float amax = __uint_as_float(am);
+    if constexpr (DT == kFp4) {
+      // as for fp8 below, with the largest e2m1 value 6 for 448
+      const float scale = amax / 6.0f;
+      const double inv = scale > 0.0f ? 1.0 / static_cast<double>(scale) : 0.0;
+      uint8_t* pg = a.kcache + page * kFp4PageBytes;
+      uint8_t* dst = pg + slot * (kHeadDim / 2) + 2 * l;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = static_cast<float>(static_cast<double>(k[i][c]) * inv);
+        // dims 2m, 2m + 1 are the low and high nibbles of byte m
+        uint32_t c4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+        c4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c4, v[2], v[3], 1.0f, 1);
+        *reinterpret_cast<uint16_t*>(dst + 8 * i) = static_cast<uint16_t>(scale > 0.0f ? c4 : 0u);
+      }
+      if (l == 0) *reinterpret_cast<float*>(pg + kFp4ScaleOffset + slot * 4) = scale;
+    } else {
+      // The correctly rounded fp32 quotient (HIP's fp32 division is correctly rounded unless
+      // fast-math is asked for), which is also the fp64 quotient rounded once to fp32: 53 >= 2 x
+      // 24 + 2 bits make that double rounding harmless.
+      const float scale = amax / 448.0f;
+      // RN32(k * RN64(1/scale)) equals RN32(k / scale): the fp64 product is within 2^-52
+      // (relative) of the exact quotient, while a quotient of two fp32 numbers is never closer
+      // than ~2^-49 (relative) to an fp32 rounding midpoint.
+      const double inv = scale > 0.0f ? 1.0 / static_cast<double>(scale) : 0.0;
+      uint8_t* pg = a.kcache + page * kFp8PageBytes;
+      uint8_t* dst = pg + slot * kHeadDim + 4 * l;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = static_cast<float>(static_cast<double>(k[i][c]) * inv);
+        int c4 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        c4 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], c4, true);
+        *reinterpret_cast<uint32_t*>(dst + 16 * i) = scale > 0.0f ? static_cast<uint32_t>(c4) : 0u;
+      }
+      if (l == 0) *reinterpret_cast<float*>(pg + kFp8ScaleOffset + slot * 4) = scale;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_q(const uint16_t* q, uint8_t* codes, float* scales, int64_t n_vec,
@@ -393,7 +413,7 @@ hipError_t launch_quantize_q(const uint16_t* q, uint8_t* codes, float* scales, i
 
 hipError_t launch_store(const StoreArgs& a, int dtype, bool hadamard, hipStream_t stream) {
   if (a.n_keys <= 0) return hipSuccess;
-  const int64_t keys_per_block = 256 / 32 * kStoreKeysPerHalfWave;
+  const int64_t keys_per_block = 256 / 4;
   const dim3 grid(static_cast<uint32_t>((a.n_keys + keys_per_block - 1) / keys_per_block));
   if (dtype == kBf16 && hadamard)
     hipLaunchKernelGGL((store_keys_kernel<kBf16, true>), grid, dim3(256), 0, stream, a);

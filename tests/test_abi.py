@@ -116,6 +116,9 @@ def test_store_validation(L):
     assert _store(L, eps=-1.0) == E_INVAL
     assert _store(L, eps=float("nan")) == E_INVAL
     assert _store(L, n_seq=-2) == E_INVAL
+    assert _store(L, x=ctypes.c_void_p(0x1008)) == E_INVAL               # x, gamma, kcache: 16-byte aligned
+    assert _store(L, gamma=ctypes.c_void_p(0x1004)) == E_INVAL
+    assert _store(L, kc=ctypes.c_void_p(0x1002)) == E_INVAL
     assert _store(L, n=0, x=None, kc=None) == E_OK        # empty store is a no-op
 
 
