@@ -55,7 +55,9 @@ DEFAULT = "prefill-22k-chunk8192-bf16"
 KERNEL_SOURCES = {
     "score_rows_bf16_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "score_rows_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
-    "score_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
+    # decode calls: the roofline and its traffic cover the scoring and the selection kernel
+    "score_kernel": ["csrc/score.hip", "csrc/topk.hip", "csrc/internal.h", "build.py"],
+    "store_keys_kernel": ["csrc/store.hip", "csrc/internal.h", "build.py"],
     "score_rows_fp8q_kernel": ["csrc/score.hip", "csrc/internal.h", "build.py"],
     "sparse_attn_kernel": ["csrc/attn.hip", "csrc/attn.h", "build.py"],
 }
@@ -211,6 +213,7 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
     key_bytes = KEY_BYTES[dtype]
     algo = wl.n_keys * (512 + 8 + key_bytes)
     achieved = algo / (kms * 1e-3) / 1e9
+    name = args.workload + ("-rotated" if args.rotate else "") + "-store-population"
     print(json.dumps({
         "metric": "keys stored/s (S1: RMSNorm + RoPE + " + ("Hadamard + " if args.rotate else "")
                   + "quantise + paged store)",
@@ -218,10 +221,10 @@ def store_population(args, wl, dtype, d, pool, ix, torch) -> int:
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": args.workload + ("-rotated" if args.rotate else "") + "-store-population",
-                   "keys": wl.n_keys, "kv_dtype": KV_NAMES[dtype]},
+        "config": {"workload": name, "keys": wl.n_keys, "kv_dtype": KV_NAMES[dtype]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": committed_traffic("store_keys_kernel", name),
                      "kernel": "store_keys_kernel", "kernel_ms": round(kms, 4)},
         "cpu_baseline": None}), flush=True)
     return 0
@@ -494,7 +497,7 @@ def main() -> int:
     # the bench's workload name (it names the cache dtype; the headline's equals wl.name)
     name = args.workload + ("-rotated" if args.rotate else "") + ("-fp8q" if args.fp8q else "")
     roof["traffic"] = committed_traffic(kernel, name)
-    roof["kernel"] = kernel
+    roof["kernel"] = kernel + (" + topk_hist_kernel" if decode and not args.fp8q else "")
 
     line = {
         "metric": "indexer keys scored/s (top-k queries/s alongside)",
