@@ -270,30 +270,33 @@ struct KeyBlock<kFp4> {
 
 // Scores of keys [c_begin, s_end) of query row i (sequence b): lane (m, g) holds key s0 + m of
 // each 32-key block; in histogram mode the lanes of group 0 also count their keys' scores.
-template <int DT, bool HIST>
-__device__ __forceinline__ void score_chunk(const ScoreArgs& a, int64_t i, int32_t b,
-                                            int32_t c_begin, int32_t s_end, float* out_row,
-                                            uint32_t* hist) {
+// A operand of query row i (q for two 32-head tiles, resident for the whole key loop) and the
+// head weights of the accumulator rows lane (m, g) holds: row = 8 (rr / 4) + 4 g + rr % 4.
+__device__ __forceinline__ void load_query(const ScoreArgs& a, int64_t i, Frag (&qa)[2][8],
+                                           float (&wv)[2][16]) {
   const int lane = threadIdx.x & 63;
-  const int m = lane & 31;      // MFMA row (A) / column (B, D) index
-  const int g = lane >> 5;      // lane group: which 64 dims of head_dim this lane feeds
-
-  // A operand: q[i] for two 32-head tiles, resident for the whole key loop.
+  const int m = lane & 31, g = lane >> 5;
   const uint16_t* qrow = a.q + i * (kHeads * kHeadDim);
-  Frag qa[2][8];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const u32x4* src = reinterpret_cast<const u32x4*>(qrow + (32 * ht + m) * kHeadDim + 64 * g);
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) qa[ht][jj].u = src[jj];
   }
-  // Head weights of the accumulator rows this lane holds: row = 8*(rr/4) + 4*g + rr%4.
-  float wv[2][16];
   const float* wrow = a.w + i * kHeads;
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) wv[ht][rr] = wrow[32 * ht + 8 * (rr >> 2) + 4 * g + (rr & 3)];
+}
+
+template <int DT, bool HIST>
+__device__ __forceinline__ void score_chunk(const ScoreArgs& a, int32_t b, int32_t c_begin,
+                                            int32_t s_end, float* out_row, uint32_t* hist,
+                                            const Frag (&qa)[2][8], const float (&wv)[2][16]) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31;      // MFMA row (A) / column (B, D) index
+  const int g = lane >> 5;      // lane group: which 64 dims of head_dim this lane feeds
 
   const int32_t* pt_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
   auto page_ok = [&](int32_t page) { return page >= 0 && page < a.n_pages_pool; };
@@ -379,6 +382,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     if (r >= a.n_rows) return;
   }
   const int64_t i = a.q_begin + r;
+  // q and the head weights depend on the row alone: requested first, they load while the
+  // sequence lookup below makes its round trip
+  Frag qa[2][8];
+  float wv[2][16];
+  load_query(a, i, qa, wv);
 
   // Query position and visible-key count.
   int32_t b, len = 0;
@@ -405,7 +413,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
   if (c_begin < s_end) {
     if (a.n_pages_pool > 0) {
-      score_chunk<DT, HIST>(a, i, b, c_begin, s_end, out_row, hist);
+      score_chunk<DT, HIST>(a, b, c_begin, s_end, out_row, hist, qa, wv);
     } else {   // no page in the pool: every visible key scores -inf
       for (int32_t s = c_begin + lane; s < s_end; s += 64) {
         out_row[s] = -INFINITY;

@@ -1017,9 +1017,6 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
   const int64_t r = (slot / a.n_seg) * kXcds + blockIdx.x % kXcds;
   const int32_t seg = static_cast<int32_t>(slot % a.n_seg);
   if (r >= a.n_rows) return;
-  int64_t len = a.row_nvis[r];
-  len = len < 0 ? 0 : (len > a.cols ? a.cols : len);
-  const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(len));
   const int32_t k = a.k;
   const float* row = a.scores + r * a.cols;
   int32_t* oi = a.out_idx + r * k;
@@ -1032,10 +1029,14 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
     info[2] = 0u;
     info[3] = 0u;
   }
+  // The row's visible count, its scores and its histograms are requested together: none of the
+  // loads depends on another, so they share one round trip.
+  const int32_t len_raw = a.row_nvis[r];
 
-  // scores of this thread (16-byte loads; the view ends at n rounded up to 4, inside the row, and
-  // slots at or past n are masked below; loads wholly past the view read 0)
-  const __amdgpu_buffer_rsrc_t view = buffer_view(row, (n + 3) & ~3);
+  // scores of this thread (16-byte loads through a view of the row's columns, rounded up to 4,
+  // which stays inside the workspace; loads wholly past the view read 0, and slots at or past
+  // the visible count are masked below)
+  const __amdgpu_buffer_rsrc_t view = buffer_view(row, static_cast<int32_t>((a.cols + 3) & ~3));
   uint32_t key[PER];
 #pragma unroll
   for (int j = 0; j < PER; j += 4) {
@@ -1045,22 +1046,6 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
     key[j + 1] = v.y;
     key[j + 2] = v.z;
     key[j + 3] = v.w;
-  }
-  if (n <= k) {   // every visible key is selected, then padding
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int32_t e = e0 + j;
-      if (e < n) {
-        oi[e] = e;
-        if (ov) ov[e] = key_value(score_order_key(__uint_as_float(key[j])));
-      }
-    }
-    if (seg == 0)
-      for (int32_t e = n + tid; e < k; e += kHistThreads) {
-        oi[e] = -1;
-        if (ov) ov[e] = -INFINITY;
-      }
-    return;
   }
 
   // 1. the row's histogram (bins 8 t .. 8 t + 7 here), and its part before this segment
@@ -1088,6 +1073,25 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
         prev[b] += before ? c[b] : 0u;
       }
     }
+  }
+
+  const int64_t len = len_raw < 0 ? 0 : (len_raw > a.cols ? a.cols : len_raw);
+  const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(len));
+  if (n <= k) {   // every visible key is selected, then padding
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      if (e < n) {
+        oi[e] = e;
+        if (ov) ov[e] = key_value(score_order_key(__uint_as_float(key[j])));
+      }
+    }
+    if (seg == 0)
+      for (int32_t e = n + tid; e < k; e += kHistThreads) {
+        oi[e] = -1;
+        if (ov) ov[e] = -INFINITY;
+      }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < PER; ++j)
