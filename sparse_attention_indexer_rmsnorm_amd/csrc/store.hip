@@ -321,6 +321,24 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c) k[i][c] = static_cast<float>(v[i][c]);
+  } else if constexpr (DT == kBf16) {
+    // bf16 needs no key-wide maximum: each chunk is rounded and stored as soon as it is computed,
+    // one chunk at a time, so that few values are live and three waves fit per SIMD
+    if (!ok) return;
+    uint8_t* dst = a.kcache + page * kBf16PageBytes + (s % kPageKeys) * (kHeadDim * 2) + 8 * l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      double y[4];
+      chunk(i, y);
+      const bf16x2 lo = __builtin_convertvector(
+          float2_v{static_cast<float>(y[0]), static_cast<float>(y[1])}, bf16x2);
+      const bf16x2 hi = __builtin_convertvector(
+          float2_v{static_cast<float>(y[2]), static_cast<float>(y[3])}, bf16x2);
+      *reinterpret_cast<uint2*>(dst + 32 * i) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
