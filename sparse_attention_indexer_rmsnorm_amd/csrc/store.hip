@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
   // The rotated store holds the whole key in fp64 for the transform; there each chunk converts
   // its x again (the empty asm hides the reuse), since keeping the norm sum's 32 fp64 values live
   // across the RoPE would cost a wave per SIMD: 150 registers and 3 waves instead of 182 and 2,
-  // 3% faster.  The plain store is faster with the reuse.
+  // 5-8% faster.  The plain store is faster with the reuse.
   auto chunk = [&](int i, double (&y)[4]) {
     float4 gi, xi = xv[i];
     if constexpr (HAD) {
@@ -339,7 +339,8 @@ __global__ __launch_bounds__(256) void store_keys_kernel(StoreArgs a) {
       for (int c = 0; c < 4; ++c) k[i][c] = static_cast<float>(v[i][c]);
   } else if constexpr (DT == kBf16) {
     // bf16 needs no key-wide maximum: each chunk is rounded and stored as soon as it is computed,
-    // one chunk at a time, so that few values are live and three waves fit per SIMD
+    // one chunk at a time, so that few values are live: 127 registers and 4 waves per SIMD
+    // instead of 182 and 2
     if (!ok) return;
     uint8_t* dst = a.kcache + page * kBf16PageBytes + (s % kPageKeys) * (kHeadDim * 2) + 8 * l;
 #pragma unroll
