@@ -535,7 +535,8 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int g = lane >> 5;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+  // rows in reverse, longest workgroups first (as in score_rows_bf16_kernel)
+  const int64_t r = (static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x) * 4 + wid;
   const bool row_ok = r < a.n_rows;
   const int64_t i = a.q_begin + (row_ok ? r : a.n_rows - 1);
 
@@ -756,7 +757,9 @@ void score_rows_bf16_kernel(ScoreArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int g = lane >> 5;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * W + wid;
+  // Workgroups take their rows in reverse: in a causal chunk the later rows see more keys, and
+  // dispatching the longest workgroups first leaves the short ones for the tail.
+  const int64_t r = (static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x) * W + wid;
   const bool row_ok = r < a.n_rows;
   const int64_t i = a.q_begin + (row_ok ? r : a.n_rows - 1);
 
@@ -991,7 +994,8 @@ void score_rows_fp8q_kernel(ScoreArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int g = lane >> 5;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * W + wid;
+  // rows in reverse, longest workgroups first (as in score_rows_bf16_kernel)
+  const int64_t r = (static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x) * W + wid;
   const bool row_ok = r < a.n_rows;
   const int64_t i = a.q_begin + (row_ok ? r : a.n_rows - 1);
 
