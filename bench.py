@@ -150,6 +150,23 @@ def ev_stats(pairs) -> dict:
             "mean": round(float(t.mean()), 5)}
 
 
+def spin_cycles(torch, us: float) -> int:
+    """Cycles of torch's spin kernel that keep the GPU busy for about `us` microseconds: queued
+    before a short timed call, the spin lets the host enqueue the call and its events before the
+    GPU reaches them, so the events bracket device work only (otherwise they also catch the
+    host's launch of the call whenever the GPU waits for it)."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 200000
+    torch.cuda._sleep(n)
+    e0.record(stream)
+    torch.cuda._sleep(n)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_us = n / max(e0.elapsed_time(e1) * 1e3, 1.0)
+    return max(1000, int(per_us * us))
+
+
 def ceilings(args, torch) -> int:
     """Context for the rooflines: the MFMA rate torch's GEMM reaches on this GPU, and the HBM read
     rate of a plain reduction, each the best of --steps runs."""
@@ -253,19 +270,28 @@ def attn_bench(args, cfg, ix, torch, W) -> int:
     def call():
         ix.sparse_attn(q, kv, kv_slot, cu_q, idx, a.scale, out=out, workspace=ws)
 
+    decode = cfg in (2, 4)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    # events in a second pass; decode calls are shorter than the host's launch of them, so a GPU
+    # spin before each puts the host ahead and the events bracket device work only
+    spin = spin_cycles(torch, 150.0) if decode else 0
     for e0, e1 in evs:
+        if spin:
+            torch.cuda._sleep(spin)
         e0.record(stream)
         call()
         e1.record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    kms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    decode = cfg in (2, 4)
+    kt = ev_stats(evs)
+    kms = kt["median"] if decode else kt["mean"]
     flops = 4.0 * H * 512 * n_list
     algo_bytes = n_list * 1024.0 + q.numel() * 2 + out.numel() * 2 + wl.n_q * H * 4 + idx.numel() * 4
     if decode:
@@ -280,7 +306,9 @@ def attn_bench(args, cfg, ix, torch, W) -> int:
     name = f"{name}-attn-h{H}"
     roof["traffic"] = committed_traffic("sparse_attn_kernel", name)
     roof["kernel"] = "sparse_attn_kernel" + (" + sparse_attn_merge_kernel" if ws_bytes else "")
-    roof["kernel_ms"] = round(kms, 4)
+    roof["kernel_ms"] = kt
+    roof["region"] = ("attention call (kernel and merge), median of HIP events" if decode else
+                      "attention call, mean of HIP events")
     line = {
         "metric": "sparse attention listed keys/s ((query, listed key) pairs, all heads)",
         "value": n_list / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
@@ -436,12 +464,16 @@ def main() -> int:
 
     decode = cfg in (2, 4)
 
-    def timed_loop(inner_events: bool):
+    spin = spin_cycles(torch, 150.0) if decode and flush is None else 0
+
+    def timed_loop(inner_events: bool, ahead: bool = False):
         for i in range(args.steps):
             if flush is not None:
                 # read, not write, the 512 MiB: written lines would be dirty in the MALL and
                 # every read of the step would then also pay for writing them back
                 flush_sink.copy_(flush.max())
+            elif ahead:
+                torch.cuda._sleep(spin)
             step_evs[i][0].record(stream)
             step(i, inner_events)
             step_evs[i][1].record(stream)
@@ -449,16 +481,22 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # decode calls are short: events inside the call would add their own packets to it, so the
-    # timed steps record none there, and a second pass times the scoring kernel alone
+    # The host clock times a plain pass.  Decode calls are shorter than the host's launch of
+    # them, so their events come from two more passes in which a GPU spin before every step puts
+    # the host ahead (the MALL flush does the same with --cold): one with events around the step
+    # and the call only (events inside the call would add their own packets to it), and one with
+    # events around the scoring kernel alone.
     t0 = time.perf_counter()
     timed_loop(inner_events=not decode)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if decode:
+        timed_loop(inner_events=False, ahead=True)
+        torch.cuda.synchronize()
     step_t = ev_stats(step_evs)
     call_t = ev_stats(call_evs)
     if decode:
-        timed_loop(inner_events=True)
+        timed_loop(inner_events=True, ahead=True)
         torch.cuda.synchronize()
 
     # the host clock times the loop (with --cold it also covers the flushes, so the step events
