@@ -179,9 +179,10 @@ int idx_logits_topk_plan(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t 
  * cu_q       device int32 [n_seq + 1], non-decreasing, cu_q[0] = 0, cu_q[n_seq] = n_q
  *            (a row outside every [cu_q[b], cu_q[b+1]) sees no key)
  * out_idx    device int32 [n_q, k];  out_val device fp32 [n_q, k] or NULL
- * workspace  device, workspace_bytes >= idx_logits_topk_min_workspace(...)
- * Errors: IDX_EINVAL (null pointer, n_q/n_seq/max_pages/n_pages_pool < 0, k < 1 or
- * k > IDX_MAX_TOPK), IDX_EUNSUPPORTED (n_heads != 64, unknown dtype), IDX_EWORKSPACE, IDX_EHIP.
+ * workspace  device, 16-byte aligned, workspace_bytes >= idx_logits_topk_min_workspace(...)
+ * Errors: IDX_EINVAL (null pointer, misaligned workspace, n_q/n_seq/max_pages/n_pages_pool < 0,
+ * k < 1 or k > IDX_MAX_TOPK), IDX_EUNSUPPORTED (n_heads != 64, unknown dtype), IDX_EWORKSPACE,
+ * IDX_EHIP.
  */
 int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype,
                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
@@ -283,12 +284,12 @@ int idx_logits_dense_fp8q(const void* q_codes, const float* q_scales, const floa
  * out_idx  device int32 [n_rows, k]: the column indices of the k largest values (ties to the lower
  *          index), in an unspecified order within the row, then -1; out_val (optional) device
  *          fp32 [n_rows, k] their values in the same order, then -inf.
- * workspace device, at least idx_topk_rows_workspace_size(n_rows, row_stride, k) bytes (that size
- *          is 0, and workspace may be NULL, when every row is selected in one pass: batches of at
- *          most 128 rows of at most 32768 scores, or rows of at most 6144 scores in batches large
- *          enough to fill the GPU).
- * Errors: IDX_EINVAL (null pointer, n_rows < 0, row_stride < 1, k < 1 or k > IDX_MAX_TOPK),
- * IDX_EWORKSPACE, IDX_EHIP.
+ * workspace device, 16-byte aligned, at least idx_topk_rows_workspace_size(n_rows, row_stride, k)
+ *          bytes (that size is 0, and workspace may be NULL, when every row is selected in one
+ *          pass: batches of at most 128 rows of at most 32768 scores, or rows of at most 6144
+ *          scores in batches large enough to fill the GPU).
+ * Errors: IDX_EINVAL (null pointer, misaligned workspace, n_rows < 0, row_stride < 1, k < 1 or
+ * k > IDX_MAX_TOPK), IDX_EWORKSPACE, IDX_EHIP.
  */
 size_t idx_topk_rows_workspace_size(int64_t n_rows, int64_t row_stride, int32_t k);
 int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const int32_t* row_len,
@@ -319,14 +320,13 @@ int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const
  * idx      device int32 [n_q, k], e.g. the output of idx_logits_topk (its -1 padding is skipped)
  * out      device bf16 [n_q, n_heads, 512], 16-byte aligned; out_lse device fp32 [n_q, n_heads]
  *          or NULL
- * workspace device, at least idx_sparse_attn_workspace_size(n_q, n_heads, k) bytes (0, and
- *          workspace may be NULL, when no list is split: batches of 256 rows or more with
- *          k <= 2048, or k <= 1024 with 32 heads)
+ * workspace device, 16-byte aligned, at least idx_sparse_attn_workspace_size(n_q, n_heads, k)
+ *          bytes (0, and workspace may be NULL, when no list is split: batches of 256 rows or
+ *          more with k <= 2048, or k <= 1024 with 32 heads)
  * n_heads is 32, 64 or 128.
- * Errors: IDX_EINVAL (null pointer, misaligned q / kv / out, n_q < 0, n_seq < 1, max_keys < 1,
- * n_slots < 0, k < 1, softmax_scale not finite and positive), IDX_EUNSUPPORTED (n_heads),
- * IDX_EWORKSPACE,
- * IDX_EHIP.
+ * Errors: IDX_EINVAL (null pointer, misaligned q / kv / out / workspace, n_q < 0, n_seq < 1,
+ * max_keys < 1, n_slots < 0, k < 1, softmax_scale not finite and positive), IDX_EUNSUPPORTED
+ * (n_heads), IDX_EWORKSPACE, IDX_EHIP.
  */
 #define IDX_LATENT_DIM 512
 size_t idx_sparse_attn_workspace_size(int64_t n_q, int32_t n_heads, int32_t k);

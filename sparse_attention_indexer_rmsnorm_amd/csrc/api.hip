@@ -25,6 +25,9 @@ constexpr int32_t kMinChunkKeys = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Workspaces hold 16-byte vectors and 8-byte atomics: the base must be 16-byte aligned.
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
 // Batches with several queries per sequence on average (prefill chunks) use the kernel whose
 // workgroups share key pages between 4 query rows; decode-shaped batches (about one query per
 // sequence) and small batches, where 4 rows per workgroup would leave most of the 256 CUs idle,
@@ -198,6 +201,7 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
   if (n_q > 0 && !out_idx) return IDX_EINVAL;
   if (n_q == 0) return IDX_OK;
   if (!workspace) return IDX_EWORKSPACE;
+  if (misaligned16(workspace)) return IDX_EINVAL;
   const bool q8 = q_scale != nullptr;
   const int64_t rows_per_chunk = rows_fitting(workspace_bytes, max_pages, k, n_q, n_seq, q8);
   if (rows_per_chunk < 1) return IDX_EWORKSPACE;
@@ -568,6 +572,7 @@ int idx_topk_rows(const float* scores, int64_t n_rows, int64_t row_stride, const
   if (!scores || !out_idx) return IDX_EINVAL;
   const size_t need = topk_workspace_bytes(n_rows, row_stride, k);
   if (need > 0 && (!workspace || workspace_bytes < need)) return IDX_EWORKSPACE;
+  if (need > 0 && misaligned16(workspace)) return IDX_EINVAL;
   return hip_status(run_topk(scores, row_stride, row_len, n_rows, k, out_idx, out_val, workspace,
                              static_cast<hipStream_t>(stream)));
 }
@@ -593,6 +598,7 @@ int idx_sparse_attn(const void* q, const void* kv, int64_t n_slots, const int32_
   if (n_q * a.n_split * 2 > INT32_MAX || n_q * n_heads > INT64_C(4) * INT32_MAX) return IDX_EINVAL;
   const size_t need = attn_workspace_bytes(n_q, n_heads, k);
   if (need > 0 && (!workspace || workspace_bytes < need)) return IDX_EWORKSPACE;
+  if (need > 0 && misaligned16(workspace)) return IDX_EINVAL;
   a.q = static_cast<const uint16_t*>(q);
   a.kv = static_cast<const uint16_t*>(kv);
   a.n_slots = n_slots;

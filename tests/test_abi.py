@@ -143,6 +143,7 @@ def test_logits_topk_validation(L):
     assert _topk(L, oi=None) == E_INVAL
     assert _topk(L, ws=None, ws_bytes=10 ** 9) == E_WS
     assert _topk(L, ws_bytes=100) == E_WS                    # < one row (256 + 128 * 4)
+    assert _topk(L, ws=ctypes.c_void_p(0x1008), ws_bytes=10 ** 9) == E_INVAL   # 16-byte aligned
     assert _topk(L, n_q=0, q=None, w=None, oi=None, ws=None) == E_OK
 
 
@@ -170,6 +171,8 @@ def test_topk_rows_validation(L):
     assert f(None, 0, 100, None, 10, None, None, None, 0, None) == E_OK
     # a two-pass selection without its workspace
     assert f(FAKE, 4, 40000, None, 1024, FAKE, None, None, 0, None) == E_WS
+    assert f(FAKE, 4, 40000, None, 1024, FAKE, None, ctypes.c_void_p(0x1004), 10 ** 9,
+             None) == E_INVAL                                                 # misaligned
 
 
 def test_sparse_attn_workspace_and_validation(L):
@@ -211,6 +214,7 @@ def test_sparse_attn_workspace_and_validation(L):
     assert call(out=MIS) == E_INVAL
     assert call(n_q=32, k=1024) == E_WS                              # split: needs a workspace
     assert call(n_q=32, k=1024, ws=F, ws_bytes=100) == E_WS
+    assert call(n_q=32, k=1024, ws=MIS, ws_bytes=10 ** 9) == E_INVAL       # misaligned workspace
 
 
 def test_binding_rejects_host_tensors():
