@@ -125,9 +125,10 @@ int idx_store_keys_rotated(const float* x, const float* gamma, float eps, const 
 /*
  * q for a rotated cache: each of n_vec 128-dim bf16 vectors (a [n_q, 64, 128] q is n_q * 64
  * vectors) multiplied by H / sqrt(128) in fp64, rounded to fp32 and then to bf16 (nearest-even).
- * q          device bf16 [n_vec, 128]
- * out        device bf16 [n_vec, 128]; may be q itself (in place)
- * Errors: IDX_EINVAL (null pointer with n_vec > 0, n_vec < 0), IDX_EHIP.  n_vec == 0 is a no-op.
+ * q          device bf16 [n_vec, 128], 16-byte aligned
+ * out        device bf16 [n_vec, 128], 16-byte aligned; may be q itself (in place)
+ * Errors: IDX_EINVAL (null or misaligned pointer with n_vec > 0, n_vec < 0), IDX_EHIP.  n_vec == 0
+ * is a no-op.
  */
 int idx_rotate_q(const void* q, void* out, int64_t n_vec, void* stream);
 
@@ -171,18 +172,18 @@ int idx_logits_topk_plan(int64_t n_q, int32_t n_seq, int32_t max_pages, int32_t 
  * logits in the same order, -inf for padding.
  * Keys whose page id lies outside [0, n_pages_pool) score -inf.
  *
- * q          device bf16 [n_q, 64, 128]
+ * q          device bf16 [n_q, 64, 128], 16-byte aligned
  * w          device fp32 [n_q, 64]
- * kcache     device pool as written by idx_store_keys with the same dtype
+ * kcache     device pool as written by idx_store_keys with the same dtype (16-byte aligned)
  * page_table device int32 [n_seq, max_pages]
  * seq_lens   device int32 [n_seq]
  * cu_q       device int32 [n_seq + 1], non-decreasing, cu_q[0] = 0, cu_q[n_seq] = n_q
  *            (a row outside every [cu_q[b], cu_q[b+1]) sees no key)
  * out_idx    device int32 [n_q, k];  out_val device fp32 [n_q, k] or NULL
  * workspace  device, 16-byte aligned, workspace_bytes >= idx_logits_topk_min_workspace(...)
- * Errors: IDX_EINVAL (null pointer, misaligned workspace, n_q/n_seq/max_pages/n_pages_pool < 0,
- * k < 1 or k > IDX_MAX_TOPK), IDX_EUNSUPPORTED (n_heads != 64, unknown dtype), IDX_EWORKSPACE,
- * IDX_EHIP.
+ * Errors: IDX_EINVAL (null pointer, misaligned q / kcache / workspace,
+ * n_q/n_seq/max_pages/n_pages_pool < 0, k < 1 or k > IDX_MAX_TOPK), IDX_EUNSUPPORTED (n_heads !=
+ * 64, unknown dtype), IDX_EWORKSPACE, IDX_EHIP.
  */
 int idx_logits_topk(const void* q, const float* w, const void* kcache, int dtype,
                     int64_t n_pages_pool, const int32_t* page_table, int32_t n_seq,
@@ -241,16 +242,16 @@ int idx_logits_dense(const void* q, const float* w, const void* kcache, int dtyp
  * idx_quantize_q: each 128-dim bf16 vector of q (one query head; a [n_q, 64, 128] q is n_q * 64
  * vectors) gets one fp32 scale = fp32(max_i |q_i| / 448) and e4m3fn codes = RNE, saturating, of
  * fp32(q_i / scale), the rule of the fp8 key store; an all-zero vector gets scale 0, codes 0.
- * q        device bf16 [n_vec, 128]
- * q_codes  device uint8 [n_vec, 128]
+ * q        device bf16 [n_vec, 128], 16-byte aligned
+ * q_codes  device uint8 [n_vec, 128], 16-byte aligned
  * q_scales device fp32 [n_vec]
- * Errors: IDX_EINVAL (null pointer with n_vec > 0, n_vec < 0), IDX_EHIP.
+ * Errors: IDX_EINVAL (null or misaligned pointer with n_vec > 0, n_vec < 0), IDX_EHIP.
  *
  * idx_logits_topk_fp8q / idx_logits_dense_fp8q: as idx_logits_topk / idx_logits_dense against an
  * fp8 cache (IDX_KV_FP8_E4M3; there is no dtype argument), with
  *   logit(i, s) = sum_h w[i,h] * max(0, sum_d (qc[i,h,d] * qs[i,h]) * (kc[s,d] * ks[s]))
  * accumulated in fp32 from the exact products of e4m3 values.  q_codes is uint8 [n_q, 64, 128]
- * and q_scales fp32 [n_q, 64] from idx_quantize_q (or any codes and non-negative scales).  The
+ * (16-byte aligned) and q_scales fp32 [n_q, 64] from idx_quantize_q (or any codes and non-negative scales).  The
  * workspace rules and errors are those of idx_logits_topk; _timed records the two events around
  * the scoring launches like idx_logits_topk_timed.
  */

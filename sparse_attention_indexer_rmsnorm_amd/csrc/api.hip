@@ -169,6 +169,8 @@ int validate_logits_common(const void* q, const float* w, const void* kcache, in
   if (n_q > 0 && (!q || !w || !cu_q || (n_seq > 0 && (!seq_lens || !page_table))))
     return IDX_EINVAL;
   if (n_q > 0 && n_seq > 0 && max_pages > 0 && n_pages_pool > 0 && !kcache) return IDX_EINVAL;
+  // q rows and key pages are read in 16-byte vectors
+  if (n_q > 0 && (misaligned16(q) || misaligned16(kcache))) return IDX_EINVAL;
   return IDX_OK;
 }
 
@@ -336,8 +338,7 @@ static int store_keys(const float* x, const float* gamma, float eps, const int32
   if (!dtype_ok(dtype)) return IDX_EUNSUPPORTED;
   if (n_keys == 0) return IDX_OK;
   if (!x || !gamma || !key_idx || !page_table || !kcache) return IDX_EINVAL;
-  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
-  if (misaligned(x) || misaligned(gamma) || misaligned(kcache)) return IDX_EINVAL;
+  if (misaligned16(x) || misaligned16(gamma) || misaligned16(kcache)) return IDX_EINVAL;
   if (n_keys > (static_cast<int64_t>(INT32_MAX) - 255) / 8 * 8) return IDX_EINVAL;
   StoreArgs a{};
   a.x = x;
@@ -375,6 +376,7 @@ int idx_rotate_q(const void* q, void* out, int64_t n_vec, void* stream) {
   if (n_vec < 0) return IDX_EINVAL;
   if (n_vec == 0) return IDX_OK;
   if (!q || !out) return IDX_EINVAL;
+  if (misaligned16(q) || misaligned16(out)) return IDX_EINVAL;
   if (n_vec > (static_cast<int64_t>(INT32_MAX) - 255) / 8) return IDX_EINVAL;
   return hip_status(launch_rotate_q(static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                                     n_vec, static_cast<hipStream_t>(stream)));
@@ -477,6 +479,7 @@ int idx_quantize_q(const void* q, void* q_codes, float* q_scales, int64_t n_vec,
   if (n_vec < 0) return IDX_EINVAL;
   if (n_vec == 0) return IDX_OK;
   if (!q || !q_codes || !q_scales) return IDX_EINVAL;
+  if (misaligned16(q) || misaligned16(q_codes)) return IDX_EINVAL;
   if (n_vec > (static_cast<int64_t>(INT32_MAX) - 255) / 8) return IDX_EINVAL;
   return hip_status(launch_quantize_q(static_cast<const uint16_t*>(q),
                                       static_cast<uint8_t*>(q_codes), q_scales, n_vec,
@@ -591,8 +594,7 @@ int idx_sparse_attn(const void* q, const void* kv, int64_t n_slots, const int32_
   if (n_heads != 32 && n_heads != 64 && n_heads != 128) return IDX_EUNSUPPORTED;
   if (n_q == 0) return IDX_OK;
   if (!q || !kv || !kv_slot || !cu_q || !idx || !out) return IDX_EINVAL;
-  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
-  if (misaligned(q) || misaligned(kv) || misaligned(out)) return IDX_EINVAL;
+  if (misaligned16(q) || misaligned16(kv) || misaligned16(out)) return IDX_EINVAL;
   AttnArgs a{};
   attn_plan(n_q, n_heads, k, &a.n_split, &a.split_keys);
   if (n_q * a.n_split * 2 > INT32_MAX || n_q * n_heads > INT64_C(4) * INT32_MAX) return IDX_EINVAL;

@@ -145,6 +145,29 @@ def test_logits_topk_validation(L):
     assert _topk(L, ws_bytes=100) == E_WS                    # < one row (256 + 128 * 4)
     assert _topk(L, ws=ctypes.c_void_p(0x1008), ws_bytes=10 ** 9) == E_INVAL   # 16-byte aligned
     assert _topk(L, n_q=0, q=None, w=None, oi=None, ws=None) == E_OK
+    assert _topk(L, q=ctypes.c_void_p(0x1008), ws_bytes=10 ** 9) == E_INVAL   # q, kcache: 16-byte
+    assert _topk(L, kc=ctypes.c_void_p(0x1004), ws_bytes=10 ** 9) == E_INVAL  # aligned
+
+
+def test_fp8q_rotate_quantize_validation(L):
+    MIS = ctypes.c_void_p(0x1008)
+
+    def fp8q(codes=FAKE, scales=FAKE, n_q=3, ws=FAKE, ws_bytes=10 ** 9):
+        return L.idx_logits_topk_fp8q(codes, scales, FAKE, FAKE, 4, FAKE, 1, 2, FAKE, FAKE, n_q,
+                                      64, 512, FAKE, None, ws, ws_bytes, None)
+    assert fp8q(scales=None) == E_INVAL
+    assert fp8q(codes=MIS) == E_INVAL
+    assert fp8q(ws=MIS) == E_INVAL
+    assert fp8q(n_q=0, codes=None, scales=None, ws=None) == E_OK
+    assert L.idx_rotate_q(FAKE, FAKE, -1, None) == E_INVAL
+    assert L.idx_rotate_q(None, None, 0, None) == E_OK
+    assert L.idx_rotate_q(None, FAKE, 4, None) == E_INVAL
+    assert L.idx_rotate_q(MIS, FAKE, 4, None) == E_INVAL
+    assert L.idx_rotate_q(FAKE, MIS, 4, None) == E_INVAL
+    assert L.idx_quantize_q(FAKE, FAKE, None, 4, None) == E_INVAL
+    assert L.idx_quantize_q(None, None, None, 0, None) == E_OK
+    assert L.idx_quantize_q(MIS, FAKE, FAKE, 4, None) == E_INVAL
+    assert L.idx_quantize_q(FAKE, MIS, FAKE, 4, None) == E_INVAL
 
 
 def test_logits_dense_validation(L):
