@@ -359,9 +359,16 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int32_t b, int32
 // One wave owns one (query row, chunk of chunk_keys keys) work item.  In histogram mode the four
 // waves of a workgroup own consecutive chunks of one row and count their scores into a shared
 // LDS histogram, which the workgroup writes out for the selection.
+// q rows staged in LDS for histogram mode: 16 chunks of 16 bytes per head, each head row padded
+// to 17 chunks so that the fragment reads (32 heads of one read 272 bytes apart) fall on distinct
+// banks.
+constexpr int kQRowChunks = kHeadDim * 2 / 16 + 1;   // 17
+
 template <int DT, bool HIST>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[HIST ? kHistBins : 1];
+  __shared__ __attribute__((aligned(16))) u32x4 qs[HIST ? kHeads * kQRowChunks : 1];
+  __shared__ float wsh[HIST ? kHeads : 1];
   const int lane = threadIdx.x & 63;
   // the wave index is uniform within a wave; say so, so that everything derived from it
   // (row, sequence, page-table row) lives in scalar registers
@@ -371,10 +378,6 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   if constexpr (HIST) {
     r = blockIdx.x / a.wg_per_row;
     chunk = static_cast<int32_t>(blockIdx.x % a.wg_per_row) * kHistChunks + wid;
-#pragma unroll
-    for (int c = 0; c < kHistBins / 1024; ++c)
-      reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * c] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
   } else {
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wid;
     r = wave / a.n_chunks;
@@ -383,16 +386,49 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
   const int64_t i = a.q_begin + r;
   // q and the head weights depend on the row alone: requested first, they load while the
-  // sequence lookup below makes its round trip
+  // sequence lookup below makes its round trip.  In histogram mode the four waves share the row,
+  // so the workgroup reads it once (each thread a quarter) and the waves take their operands
+  // from LDS: every wave reading the whole row made the start of the kernel a read of 16.5 KB
+  // per wave.
   Frag qa[2][8];
   float wv[2][16];
-  load_query(a, i, qa, wv);
+  u32x4 qv[4];
+  float wt = 0.0f;
+  if constexpr (HIST) {
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(a.q + i * (kHeads * kHeadDim));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qv[c] = qsrc[threadIdx.x + 256 * c];
+    if (threadIdx.x < kHeads) wt = a.w[i * kHeads + threadIdx.x];
+  } else {
+    load_query(a, i, qa, wv);
+  }
 
   // Query position and visible-key count.
   int32_t b, len = 0;
   int64_t q_len = 0, row_in_seq = 0;
   row_sequence(a.cu_q, a.seq_lens, a.n_seq, i, &b, &q_len, &row_in_seq, &len);
   b = __builtin_amdgcn_readfirstlane(b);
+  if constexpr (HIST) {
+#pragma unroll
+    for (int c = 0; c < kHistBins / 1024; ++c)
+      reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * c] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = threadIdx.x + 256 * c;          // chunk e of the row: head e / 16
+      qs[(e >> 4) * kQRowChunks + (e & 15)] = qv[c];
+    }
+    if (threadIdx.x < kHeads) wsh[threadIdx.x] = wt;
+    __syncthreads();
+    const int m = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) qa[ht][jj].u = qs[(32 * ht + m) * kQRowChunks + 8 * g + jj];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) wv[ht][rr] = wsh[32 * ht + 8 * (rr >> 2) + 4 * g + (rr & 3)];
+  }
   int64_t n_vis = 0;
   if (b >= 0) {
     const int64_t t = static_cast<int64_t>(len) - q_len + row_in_seq;
