@@ -73,6 +73,12 @@ HistPlan hist_plan(int64_t rows, int32_t cols) {
   int32_t ck, nc;
   plan_chunks(rows, cols, &ck, &nc);
   h.chunk_keys = ck >= 512 ? 512 : 256;
+  // batches too small for two 256-key work items per SIMD take 128-key chunks, where the row
+  // still fits the histogram selection
+  const int64_t fill = static_cast<int64_t>(cols) * rows / kMinWaves;
+  if (h.chunk_keys == 256 && fill < 256 &&
+      (cols + 128 * kHistChunks - 1) / (128 * kHistChunks) <= kMaxHistWgPerRow)
+    h.chunk_keys = 128;
   h.n_chunks = (cols + h.chunk_keys - 1) / h.chunk_keys;
   h.wg_per_row = (h.n_chunks + kHistChunks - 1) / kHistChunks;
   const int64_t segs4k = (static_cast<int64_t>(cols) + 4095) / 4096;
@@ -126,7 +132,8 @@ size_t workspace_upper(int64_t rows, int32_t max_pages, int32_t k) {
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
   const size_t cand = static_cast<size_t>(topk_cand_bound(static_cast<int64_t>(cols), k));
   const size_t passes_row = 2 * cand * 8;
-  const size_t wg_max = (cols + 4 * 256 - 1) / (4 * 256);   // histogram workgroups of 4 x 256 keys
+  // histogram workgroups of kHistChunks chunks of 128 keys at the least
+  const size_t wg_max = (cols + kHistChunks * 128 - 1) / (kHistChunks * 128);
   const size_t hist_row = wg_max * kHistBins * 2 + sizeof(int32_t) + cols * 8;
   const size_t sel_row = passes_row > hist_row ? passes_row : hist_row;
   return static_cast<size_t>(rows) * (sizeof(int32_t) + cols * sizeof(float) + sel_row) +
