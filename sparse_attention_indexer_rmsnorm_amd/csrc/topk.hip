@@ -1205,6 +1205,8 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
   // pass 1: bits 20..10 of the keys of bin B; pass 2: bits 9..0 of those in the chosen digit
   uint32_t want = k_rem;
   uint32_t prefix = B;
+  uint32_t T = 0u, eq_take = 0u;
+  bool resolved = false;
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
@@ -1225,9 +1227,22 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
     prefix = (prefix << width) | d;
     want -= gt;
     __syncthreads();   // sub is cleared again by the next pass
+    // Every key of the chosen digit is taken (the usual case: bin B's few hundred keys spread
+    // over 2048 digits): the winners are the keys whose top 21 bits are at least `prefix`, i.e.
+    // the keys above T = (prefix << 10) - 1 with no tie taken, and the second pass is not needed.
+    // (cnt and want come from the same LDS counts in every wave, so the exit is uniform; a zero
+    // prefix, only reachable by NaN keys, keeps the second pass.)
+    if (pass == 0 && cnt == want && prefix != 0u) {
+      T = (prefix << 10) - 1u;
+      eq_take = 0u;
+      resolved = true;
+      break;
+    }
   }
-  const uint32_t T = prefix;
-  const uint32_t eq_take = want;
+  if (!resolved) {
+    T = prefix;
+    eq_take = want;
+  }
 
   // candidates above T, then the lowest-indexed ones equal to T, after the higher-bin winners:
   // thread t visits a contiguous slice of the (index-ordered) list
