@@ -10,7 +10,7 @@ import torch
 
 import sparse_attention_indexer_rmsnorm_amd as ix
 import workloads as W
-from tests.helpers import check_logits, dev_inputs, oracle_rows, workload
+from tests.helpers import by_index, check_logits, dev_inputs, gpu_store, oracle_rows, workload
 
 pytestmark = pytest.mark.gpu
 FP8, BF16 = W.FP8, W.BF16
@@ -107,3 +107,38 @@ def test_dense_repeatable(oracle_mod):
     a = _dense(wl, d, pool, FP8)
     b = _dense(wl, d, pool, FP8)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("shape,dtype", [("decode", FP8), ("decode", BF16), ("decode", W.FP4),
+                                         ("prefill", BF16), ("prefill", FP8)])
+def test_page_placement_invariance(shape, dtype):
+    """The same keys stored through two page tables, one a random relabelling of the other's
+    pages, give bit-identical logits and selections: a score depends on the key's bytes, never on
+    where its page sits in the pool.  Decode rows go through the split kernel, the 1100-row
+    prefill batch through the rows kernels."""
+    if shape == "decode":
+        wl = W.make_workload("placement-decode", 70, [20000, 9000, 33000, 4100], [1, 1, 1, 1],
+                             512, permute_pages=True, extra_pages=2, dtypes=(dtype,))
+    else:
+        wl = W.make_workload("placement-prefill", 71, [9000, 6000], [700, 400], 512,
+                             permute_pages=True, extra_pages=2, dtypes=(dtype,))
+    d1 = dev_inputs(wl)
+    relabel = np.random.default_rng(72).permutation(wl.n_pages_pool).astype(np.int32)
+    pt2 = wl.page_table.copy()
+    ok = (pt2 >= 0) & (pt2 < wl.n_pages_pool)
+    pt2[ok] = relabel[pt2[ok]]
+    assert not np.array_equal(pt2, wl.page_table)
+    d2 = dict(d1)
+    d2["page_table"] = torch.from_numpy(pt2).cuda()
+    out = []
+    for d in (d1, d2):
+        pool = gpu_store(ix, wl, dtype, d)
+        dense = ix.logits_dense(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
+                                d["cu_q"], wl.max_keys)
+        gi, gv = ix.logits_topk(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
+                                d["cu_q"], wl.k, want_values=True)
+        out.append((dense, *by_index(gi, gv)))
+    (a, ai, av), (b, bi, bv) = out
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(ai, bi)
+    assert torch.equal(av.view(torch.int32), bv.view(torch.int32))
