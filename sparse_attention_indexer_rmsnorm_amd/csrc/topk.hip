@@ -1150,10 +1150,11 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
   uint32_t sc_pre[4], sc_tot[4];
   wg_excl_scan<4>({p_hi, p_eq, n_hi, n_eq}, red, lane, wid, sc_pre, sc_tot);
   uint64_t* cand = a.cand + r * a.cols;
-  {
-    // before this segment (totals of the earlier histograms' counts), then this thread's place
-    uint32_t at_hi = sc_tot[0] + sc_pre[2];
-    uint32_t at_eq = sc_tot[1] + sc_pre[3];
+  // before this segment (totals of the earlier histograms' counts), then this thread's place
+  const uint32_t hi0 = sc_tot[0] + sc_pre[2];
+  const uint32_t eq0 = sc_tot[1] + sc_pre[3];
+  if (all_win) {
+    uint32_t at_hi = hi0, at_eq = eq0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int32_t e = e0 + j;
@@ -1164,33 +1165,68 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
         oi[at_hi] = e;
         if (ov) ov[at_hi] = key_value(key[j]);
       }
-      if (eq && all_win && above + at_eq < static_cast<uint32_t>(k)) {
+      if (eq && above + at_eq < static_cast<uint32_t>(k)) {
         oi[above + at_eq] = e;
         if (ov) ov[above + at_eq] = key_value(key[j]);
-      } else if (eq && !all_win && at_eq < c_b) {
+      }
+      at_hi += hi ? 1u : 0u;
+      at_eq += eq ? 1u : 0u;
+    }
+    return;
+  }
+
+  // bin B's keys to the row's candidate list, which the row's last workgroup refines (3.)
+  {
+    uint32_t at_eq = eq0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      const bool eq = e < n && (key[j] >> kHistShift) == B;
+      if (eq && at_eq < c_b) {
         // an agent-scope store writes through to where every XCD's loads of it look
         __hip_atomic_store(cand + at_eq,
                            (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(e),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      at_hi += hi ? 1u : 0u;
       at_eq += eq ? 1u : 0u;
     }
   }
-  if (all_win) return;
 
   // 3. the row's last workgroup refines the threshold bin.  The hand-over needs no cache-wide
   //    write-back or invalidation (an agent-scope fence is both, on every XCD's L2): the
   //    candidates were stored with agent-scope atomic stores, each thread waits until its stores
   //    are acknowledged before the barrier, the counter is an agent-scope atomic, and the last
   //    workgroup reads the candidates with agent-scope atomic loads issued after the counter
-  //    returned.
+  //    returned.  The segment's higher-bin winners are stored after the counter is requested,
+  //    as a fixed number of buffer stores (a key that is not one writes past the output view,
+  //    which drops the store): the wait for the counter's value then leaves them in flight,
+  //    and they hold up neither the hand-over nor the workgroups that are not last.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
+  int32_t ticket = 0;
   if (tid == 0)
-    info[3] = static_cast<uint32_t>(__hip_atomic_fetch_add(a.row_ctr + r, 1, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
-  __syncthreads();
+    ticket = __hip_atomic_fetch_add(a.row_ctr + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {
+    const __amdgpu_buffer_rsrc_t vi = buffer_view(reinterpret_cast<const float*>(oi), k);
+    const __amdgpu_buffer_rsrc_t vv = buffer_view(ov, ov ? k : 0);
+    constexpr uint32_t kDrop = 0x40800000u;   // past every output view (k <= 2048 values)
+    uint32_t at_hi = hi0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      const bool hi = e < n && (key[j] >> kHistShift) > B;
+      const uint32_t at = (hi && at_hi < above) ? 4u * at_hi : kDrop;
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(e), vi, at, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key[j])), vv, at, 0, 0);
+      at_hi += hi ? 1u : 0u;
+    }
+  }
+  if (tid == 0) info[3] = static_cast<uint32_t>(ticket);
+  // LDS-only barrier: the winner stores stay in flight
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   if (info[3] != static_cast<uint32_t>(a.n_seg - 1)) return;
 
   auto load_cand = [&](uint32_t c) {
