@@ -1175,8 +1175,22 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
     return;
   }
 
-  // bin B's keys to the row's candidate list, which the row's last workgroup refines (3.)
-  {
+  // A row of one segment is this workgroup's alone: its candidates go to the LDS list, in
+  // index order, and the refinement below starts at once (c_b <= seg_len <= kHistCandLds).
+  const bool local = a.n_seg == 1;
+  if (local) {
+    uint32_t at_eq = eq0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      const bool eq = e < n && (key[j] >> kHistShift) == B;
+      if (eq && at_eq < c_b)
+        lcand[at_eq] = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(e);
+      at_eq += eq ? 1u : 0u;
+    }
+  }
+  // else bin B's keys to the row's candidate list, which the row's last workgroup refines (3.)
+  if (!local) {
     uint32_t at_eq = eq0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -1203,8 +1217,8 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
   //    and they hold up neither the hand-over nor the workgroups that are not last.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  int32_t ticket = 0;
-  if (tid == 0)
+  int32_t ticket = a.n_seg - 1;   // a local row's workgroup is its last
+  if (tid == 0 && !local)
     ticket = __hip_atomic_fetch_add(a.row_ctr + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   {
     const __amdgpu_buffer_rsrc_t vi = buffer_view(reinterpret_cast<const float*>(oi), k);
@@ -1233,7 +1247,7 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) 
     return __hip_atomic_load(cand + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   const bool listed = c_b <= static_cast<uint32_t>(kHistCandLds);
-  if (listed) {
+  if (listed && !local) {
     for (uint32_t c = tid; c < c_b; c += kHistThreads) lcand[c] = load_cand(c);
     __syncthreads();
   }
