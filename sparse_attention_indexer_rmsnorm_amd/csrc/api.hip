@@ -56,14 +56,12 @@ bool dtype_ok(int dtype) {
   return dtype == IDX_KV_FP8_E4M3 || dtype == IDX_KV_BF16 || dtype == IDX_KV_FP4_E2M1;
 }
 
-// Decode-shaped chunks (the split scoring kernel) are selected from per-workgroup histograms
-// (launch_topk_hist): the scoring kernel's workgroups cover 4 chunks of 256 or 512 keys of one
-// row, and a selection workgroup covers seg_len scores.  Rows of more than this many histogram
-// workgroups are selected in segments and passes instead (run_topk).
-constexpr int32_t kMaxHistWgPerRow = 64;
-
+// Decode-shaped chunks (the split scoring kernel) are selected from the per-workgroup histograms
+// and bucketed keys the scoring kernel writes (launch_topk_hist): its workgroups cover 4 chunks
+// of 128, 256 or 512 keys of one row.  Rows of more than kMaxHistWgPerRow such workgroups are
+// selected in segments and passes instead (run_topk).
 struct HistPlan {
-  int32_t chunk_keys, n_chunks, wg_per_row, seg_len, n_seg;
+  int32_t chunk_keys, n_chunks, wg_per_row;
 };
 
 void plan_chunks(int64_t n_rows, int32_t n_cols, int32_t* chunk_keys, int32_t* n_chunks);
@@ -81,9 +79,6 @@ HistPlan hist_plan(int64_t rows, int32_t cols) {
     h.chunk_keys = 128;
   h.n_chunks = (cols + h.chunk_keys - 1) / h.chunk_keys;
   h.wg_per_row = (h.n_chunks + kHistChunks - 1) / kHistChunks;
-  const int64_t segs4k = (static_cast<int64_t>(cols) + 4095) / 4096;
-  h.seg_len = rows * segs4k >= 256 ? 4096 : 2048;
-  h.n_seg = (cols + h.seg_len - 1) / h.seg_len;
   return h;
 }
 
@@ -95,12 +90,12 @@ bool use_hist(int64_t rows, int32_t n_seq, int32_t cols, bool q8) {
 }
 
 // Workspace layout for a chunk of `rows` query rows:
-//   [row_nvis int32 x rows | pad][scores fp32 rows x cols | pad] then either
-//   [selection candidates] (segments and passes), or
-//   [histograms u16 rows x wg_per_row x kHistBins | pad][row counters int32 x rows | pad]
-//   [candidates u64 rows x cols] (selection from histograms)
+//   [row_nvis int32 x rows | pad] then either
+//   [scores fp32 rows x cols | pad][selection candidates] (segments and passes), or
+//   [bucketed keys u64 rows x wg_per_row x wg_keys | pad][histograms u16 rows x wg_per_row x
+//    kHistBins | pad][bucket starts u16, the same] (selection from histograms)
 struct WsLayout {
-  size_t nvis, scores, topk, hist, ctr, cand, total;
+  size_t nvis, scores, topk, list, hist, off, total;
   bool hist_path;
 };
 
@@ -108,18 +103,19 @@ WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k, int32_t n_
   WsLayout L{};
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
   L.nvis = 0;
-  L.scores = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
-  L.topk = align_up(L.scores + static_cast<size_t>(rows) * cols * sizeof(float));
   L.hist_path = use_hist(rows, n_seq, static_cast<int32_t>(cols), q8);
   if (!L.hist_path) {
+    L.scores = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
+    L.topk = align_up(L.scores + static_cast<size_t>(rows) * cols * sizeof(float));
     L.total = L.topk + topk_workspace_bytes(rows, static_cast<int64_t>(cols), k);
     return L;
   }
   const HistPlan h = hist_plan(rows, static_cast<int32_t>(cols));
-  L.hist = L.topk;
-  L.ctr = align_up(L.hist + static_cast<size_t>(rows) * h.wg_per_row * kHistBins * 2);
-  L.cand = align_up(L.ctr + static_cast<size_t>(rows) * sizeof(int32_t));
-  L.total = L.cand + static_cast<size_t>(rows) * cols * 8;
+  const size_t lists = static_cast<size_t>(rows) * h.wg_per_row;
+  L.list = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
+  L.hist = align_up(L.list + lists * kHistChunks * h.chunk_keys * 8);
+  L.off = align_up(L.hist + lists * kHistBins * 2);
+  L.total = L.off + lists * kHistBins * 2;
   return L;
 }
 
@@ -131,13 +127,13 @@ WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k, int32_t n_
 size_t workspace_upper(int64_t rows, int32_t max_pages, int32_t k) {
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
   const size_t cand = static_cast<size_t>(topk_cand_bound(static_cast<int64_t>(cols), k));
-  const size_t passes_row = 2 * cand * 8;
-  // histogram workgroups of kHistChunks chunks of 128 keys at the least
+  const size_t passes_row = cols * sizeof(float) + 2 * cand * 8;
+  // histogram workgroups of kHistChunks chunks of 128 keys at the least; their keys cover the
+  // columns rounded up to one workgroup of the widest chunks
   const size_t wg_max = (cols + kHistChunks * 128 - 1) / (kHistChunks * 128);
-  const size_t hist_row = wg_max * kHistBins * 2 + sizeof(int32_t) + cols * 8;
+  const size_t hist_row = (cols + kHistWgKeysMax) * 8 + wg_max * kHistBins * 2 * 2;
   const size_t sel_row = passes_row > hist_row ? passes_row : hist_row;
-  return static_cast<size_t>(rows) * (sizeof(int32_t) + cols * sizeof(float) + sel_row) +
-         6 * kAlign;
+  return static_cast<size_t>(rows) * (sizeof(int32_t) + sel_row) + 6 * kAlign;
 }
 
 // Query rows per chunk for a workspace of `bytes`: all of them if they fit, else the largest
@@ -233,7 +229,7 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
     const int64_t rows = (n_q - q0 < rows_per_chunk) ? n_q - q0 : rows_per_chunk;
     const WsLayout L = workspace_layout(rows, max_pages, k, n_seq, q8);
     int32_t* nvis = reinterpret_cast<int32_t*>(ws + L.nvis);
-    float* scores = reinterpret_cast<float*>(ws + L.scores);
+    float* scores = L.hist_path ? nullptr : reinterpret_cast<float*>(ws + L.scores);
     sa.q_begin = q0;
     sa.n_rows = rows;
     sa.out = scores;
@@ -244,11 +240,14 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
       sa.chunk_keys = hp.chunk_keys;
       sa.n_chunks = hp.n_chunks;
       sa.wg_per_row = hp.wg_per_row;
+      sa.wg_list = reinterpret_cast<uint64_t*>(ws + L.list);
       sa.wg_hist = reinterpret_cast<uint16_t*>(ws + L.hist);
-      sa.row_ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
+      sa.wg_off = reinterpret_cast<uint16_t*>(ws + L.off);
+      sa.sel_k = k;
     } else {
+      sa.wg_list = nullptr;
       sa.wg_hist = nullptr;
-      sa.row_ctr = nullptr;
+      sa.wg_off = nullptr;
       sa.wg_per_row = 0;
       if (cols > 0) {
         plan_chunks(rows, cols, &sa.chunk_keys, &sa.n_chunks);
@@ -265,18 +264,15 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
       return IDX_EHIP;
     if (L.hist_path) {
       HistSelArgs h{};
-      h.scores = scores;
-      h.cols = cols;
+      h.wg_list = sa.wg_list;
+      h.wg_hist = sa.wg_hist;
+      h.wg_off = sa.wg_off;
       h.row_nvis = nvis;
+      h.cols = cols;
       h.n_rows = rows;
       h.k = k;
-      h.wg_hist = sa.wg_hist;
       h.wg_per_row = hp.wg_per_row;
       h.wg_keys = kHistChunks * hp.chunk_keys;
-      h.row_ctr = sa.row_ctr;
-      h.n_seg = hp.n_seg;
-      h.seg_len = hp.seg_len;
-      h.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
       h.out_idx = out_idx + q0 * k;
       h.out_val = out_val ? out_val + q0 * k : nullptr;
       if (launch_topk_hist(h, s) != hipSuccess) return IDX_EHIP;

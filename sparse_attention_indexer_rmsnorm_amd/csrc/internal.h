@@ -67,13 +67,21 @@ struct ScoreArgs {
   const uint8_t* q8;         // fp8 x fp8 scoring: q e4m3 codes [n_q, 64, 128], or null
   const float* q_scale;      // [n_q, 64] scales of q8
   // Histogram mode of the split kernel (set by the decode-shaped selection): workgroup
-  // (row r, j) scores chunks 4j .. 4j + 3 of row r and writes a kHistBins-bin histogram of its
-  // scores to wg_hist[(r * wg_per_row + j) * kHistBins ..] (16-bit counts); workgroup (r, 0)
-  // also zeroes row_ctr[r] for the selection.  Null wg_hist: plain mode (any four work items per
-  // workgroup).
+  // (row r, j) scores chunks 4j .. 4j + 3 of row r (keys [j * wg_keys, (j + 1) * wg_keys),
+  // wg_keys = 4 * chunk_keys) and writes, for list L = r * wg_per_row + j:
+  //   wg_hist[L * kHistBins + b]  its number of keys in histogram bin b (16-bit counts);
+  //   wg_off[L * kHistBins + b]   its number of keys in bins above b (16-bit);
+  //   wg_list[L * wg_keys + p]    its keys bucketed by bin, highest bin first: the keys of bin b
+  //                               at positions [wg_off[b], wg_off[b] + wg_hist[b]) in no set
+  //                               order, each as (order key << 32 | key index).  When the
+  //                               workgroup holds more than sel_k keys, the bins below its own
+  //                               sel_k-th largest key are counted but their keys not written.
+  // Null wg_hist: plain mode (any four work items per workgroup, scores to out).
   uint16_t* wg_hist;
-  int32_t* row_ctr;
+  uint16_t* wg_off;
+  uint64_t* wg_list;
   int32_t wg_per_row;
+  int32_t sel_k;
 };
 
 // Selection histogram: bins are the top kHistBits bits of a score's order-preserving key, so a
@@ -81,8 +89,15 @@ struct ScoreArgs {
 constexpr int kHistBits = 11;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
-// Chunks of one row per histogram workgroup (one per wave).
+// Chunks of one row per histogram workgroup (one per wave), and the most keys such a workgroup
+// covers (4 chunks of at most 512 keys).
 constexpr int kHistChunks = 4;
+constexpr int kXcds = 8;   // MI355X: 8 XCDs, each with its own L2
+constexpr int kHistWgKeysMax = 2048;
+// Most histogram workgroups per row (the selection keeps one entry per workgroup in LDS) and the
+// longest row that the selection covers (its winner bitmap is held in LDS).
+constexpr int kMaxHistWgPerRow = 64;
+constexpr int kHistMaxCols = kMaxHistWgPerRow * kHistWgKeysMax;
 
 // Order-preserving uint32 key of a score that is not a NaN: adding +0 turns -0 into +0 (fp32
 // denormals are kept), then the sign selects the mask.
@@ -124,25 +139,21 @@ struct TopkPlan {
   int64_t cand_elems;        // widest candidate row between passes
 };
 
-// Selection over a score matrix written by the split kernel in histogram mode (few long rows:
-// decode batches).  Row r is cut into n_seg segments of seg_len scores, one workgroup each; the
-// workgroup sums the row's histograms, finds the bin holding the k-th largest score, and writes
-// the keys of higher bins straight to their output positions (the histograms of the earlier
-// segments give the offset) and the threshold bin's keys to the row's candidate list; the last
-// workgroup of the row to finish refines the candidates to the exact threshold.
+// Selection from the bucketed lists the split kernel writes in histogram mode (few long rows:
+// decode batches), one workgroup per row: the sum of the row's histograms gives the bin B that
+// holds the k-th largest score; every key of a higher bin is a winner and is read from the front
+// of its list, bin B's keys are read from behind them and refined to the exact threshold, and a
+// bitmap of the winners' indices gives each its output position (the output is sorted by index).
 struct HistSelArgs {
-  const float* scores;       // [n_rows, cols]
-  int64_t cols;
+  const uint64_t* wg_list;   // [n_rows, wg_per_row, wg_keys]
+  const uint16_t* wg_hist;   // [n_rows, wg_per_row, kHistBins]
+  const uint16_t* wg_off;    // [n_rows, wg_per_row, kHistBins]
   const int32_t* row_nvis;   // [n_rows] visible keys per row
+  int64_t cols;              // key columns scored per row (<= kHistMaxCols)
   int64_t n_rows;
   int32_t k;
-  const uint16_t* wg_hist;   // [n_rows, wg_per_row, kHistBins]
-  int32_t wg_per_row;
-  int32_t wg_keys;           // scores per histogram workgroup; divides seg_len
-  int32_t* row_ctr;          // [n_rows], zero on entry
-  int32_t n_seg;
-  int32_t seg_len;           // 2048 or 4096
-  uint64_t* cand;            // [n_rows, cols] (order key << 32 | index), index order
+  int32_t wg_per_row;        // <= kMaxHistWgPerRow
+  int32_t wg_keys;           // keys per scoring workgroup (<= kHistWgKeysMax)
   int32_t* out_idx;          // [n_rows, k]
   float* out_val;            // [n_rows, k] or null
 };

@@ -123,6 +123,23 @@ __device__ __forceinline__ void row_sequence(const int32_t* cu_q, const int32_t*
   *len_out = lb;
 }
 
+// Inclusive sum over the lanes of a wave with DPP (no LDS round trips): row_shr 1, 2, 4, 8 within
+// each 16-lane row, then row_bcast 15 and 31 across rows.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_add_scan(uint32_t x) {
+  x += dpp_or_zero<0x111, 0xF>(x);
+  x += dpp_or_zero<0x112, 0xF>(x);
+  x += dpp_or_zero<0x114, 0xF>(x);
+  x += dpp_or_zero<0x118, 0xF>(x);
+  x += dpp_or_zero<0x142, 0xA>(x);
+  x += dpp_or_zero<0x143, 0xC>(x);
+  return x;
+}
+
 // ReLU of a finite float as one integer max: a set sign bit makes the pattern a negative int32,
 // which max(., 0) maps to +0; non-negative floats are unchanged.  (A float max would first have
 // to quieten NaNs in IEEE mode, costing a second instruction.)
@@ -293,6 +310,7 @@ __device__ __forceinline__ void load_query(const ScoreArgs& a, int64_t i, Frag (
 template <int DT, bool HIST>
 __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int32_t b, int32_t c_begin,
                                             int32_t s_end, float* out_row, uint32_t* hist,
+                                            float* sc, int32_t wg_begin,
                                             const Frag (&qa)[2][8], const float (&wv)[2][16]) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 31;      // MFMA row (A) / column (B, D) index
@@ -338,8 +356,12 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int32_t b, int32
     const int32_t s = s0 + m;
     const float v = ok_cur ? tot : -INFINITY;
     if (g == 0 && s < s_end) {
-      out_row[s] = v;
-      if constexpr (HIST) atomicAdd(&hist[score_order_key(v) >> kHistShift], 1u);
+      if constexpr (HIST) {
+        sc[s - wg_begin] = v;
+        atomicAdd(&hist[score_order_key(v) >> kHistShift], 1u);
+      } else {
+        out_row[s] = v;
+      }
     }
   };
   pid[0] = pg_of(c_begin);
@@ -369,15 +391,26 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[HIST ? kHistBins : 1];
   __shared__ __attribute__((aligned(16))) u32x4 qs[HIST ? kHeads * kQRowChunks : 1];
   __shared__ float wsh[HIST ? kHeads : 1];
+  __shared__ float sc[HIST ? kHistWgKeysMax : 1];   // the workgroup's scores, by key
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t blo_sh;
   const int lane = threadIdx.x & 63;
   // the wave index is uniform within a wave; say so, so that everything derived from it
   // (row, sequence, page-table row) lives in scalar registers
   const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int64_t r;
   int32_t chunk;
+  int32_t wg_j = 0;   // histogram mode: which of its row's workgroups this is
   if constexpr (HIST) {
-    r = blockIdx.x / a.wg_per_row;
-    chunk = static_cast<int32_t>(blockIdx.x % a.wg_per_row) * kHistChunks + wid;
+    // Workgroups go to the 8 XCDs in turn (workgroup b to XCD b % 8): every workgroup of row r
+    // is given to XCD r % 8, the XCD that the selection's workgroup for the row runs on, so
+    // that the row's q is read into one L2 and its buckets are written into the L2 they are
+    // read from.  The grid covers the rows rounded up to a multiple of 8.
+    const int32_t slot = static_cast<int32_t>(blockIdx.x / kXcds);
+    r = static_cast<int64_t>(slot / a.wg_per_row) * kXcds + blockIdx.x % kXcds;
+    wg_j = slot % a.wg_per_row;
+    if (r >= a.n_rows) return;   // the whole workgroup, before any barrier
+    chunk = wg_j * kHistChunks + wid;
   } else {
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wid;
     r = wave / a.n_chunks;
@@ -412,6 +445,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int c = 0; c < kHistBins / 1024; ++c)
       reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * c] = u32x4{0u, 0u, 0u, 0u};
+    if (threadIdx.x == 0) blo_sh = 0u;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int e = threadIdx.x + 256 * c;          // chunk e of the row: head e / 16
@@ -443,31 +477,93 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int32_t c_begin = chunk * a.chunk_keys;
   const int32_t c_end = min(c_begin + a.chunk_keys, a.n_cols);
   const int32_t s_end = static_cast<int32_t>(min<int64_t>(c_end, n_vis));
-  float* out_row = a.out + r * a.out_stride;
-  if (a.fill_invisible) {
+  // histogram mode: keys [wg_begin, wg_begin + 4 * chunk_keys) of the row are this workgroup's
+  const int32_t wg_begin = HIST ? wg_j * kHistChunks * a.chunk_keys : 0;
+  float* out_row = HIST ? nullptr : a.out + r * a.out_stride;
+  if (!HIST && a.fill_invisible) {
     for (int32_t s = max(c_begin, s_end) + lane; s < c_end; s += 64) out_row[s] = -INFINITY;
   }
   if (c_begin < s_end) {
     if (a.n_pages_pool > 0) {
-      score_chunk<DT, HIST>(a, b, c_begin, s_end, out_row, hist, qa, wv);
+      score_chunk<DT, HIST>(a, b, c_begin, s_end, out_row, hist, sc, wg_begin, qa, wv);
     } else {   // no page in the pool: every visible key scores -inf
       for (int32_t s = c_begin + lane; s < s_end; s += 64) {
-        out_row[s] = -INFINITY;
-        if constexpr (HIST) atomicAdd(&hist[score_order_key(-INFINITY) >> kHistShift], 1u);
+        if constexpr (HIST) {
+          sc[s - wg_begin] = -INFINITY;
+          atomicAdd(&hist[score_order_key(-INFINITY) >> kHistShift], 1u);
+        } else {
+          out_row[s] = -INFINITY;
+        }
       }
     }
   }
 
   if constexpr (HIST) {
+    // The workgroup's keys, bucketed by histogram bin (a counting sort in LDS): the histogram,
+    // then for every bin the number of keys in higher bins (where its bucket starts), then each
+    // key to the next free place of its bucket.  The selection reads only the buckets at and
+    // above the bin of the row's k-th largest key; that bin is at or above the bin of this
+    // workgroup's own k-th largest key whenever the workgroup holds more than k keys (the row
+    // holds those k keys too), so the keys of lower bins are never read and are not written.
     __syncthreads();
-    // bins 8 t .. 8 t + 7 of thread t as 16-bit counts (at most 4 x 512 scores per workgroup)
-    const u32x4 lo = reinterpret_cast<const u32x4*>(hist)[2 * threadIdx.x];
-    const u32x4 hi = reinterpret_cast<const u32x4*>(hist)[2 * threadIdx.x + 1];
-    const u32x4 packed = {lo.x | (lo.y << 16), lo.z | (lo.w << 16), hi.x | (hi.y << 16),
-                          hi.z | (hi.w << 16)};
-    reinterpret_cast<u32x4*>(a.wg_hist + static_cast<int64_t>(blockIdx.x) * kHistBins)
-        [threadIdx.x] = packed;
-    if (threadIdx.x == 0 && blockIdx.x % a.wg_per_row == 0) a.row_ctr[r] = 0;
+    const int tid = threadIdx.x;
+    const int64_t list = r * a.wg_per_row + wg_j;
+    // bins 8 t .. 8 t + 7 of thread t
+    const u32x4 lo = reinterpret_cast<const u32x4*>(hist)[2 * tid];
+    const u32x4 hi = reinterpret_cast<const u32x4*>(hist)[2 * tid + 1];
+    const uint32_t c[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    // 16-bit counts: at most 4 x 512 keys per workgroup
+    reinterpret_cast<u32x4*>(a.wg_hist + list * kHistBins)[tid] =
+        u32x4{c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+    uint32_t mine = 0;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) mine += c[bb];
+    const uint32_t incl = wave_add_scan(mine);
+    if (lane == 63) wsum[threadIdx.x >> 6] = incl;
+    __syncthreads();
+    // keys above thread t's bins: those of the later lanes of its wave and of the later waves
+    const int wv_id = threadIdx.x >> 6;
+    uint32_t later = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63)) - incl;
+    uint32_t total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      total += wsum[w];
+      later += w > wv_id ? wsum[w] : 0u;
+    }
+    uint32_t e[8];
+    e[7] = later;
+#pragma unroll
+    for (int bb = 6; bb >= 0; --bb) e[bb] = e[bb + 1] + c[bb + 1];
+    const uint32_t k = static_cast<uint32_t>(a.sel_k);
+    if (total > k) {
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+        if (e[bb] < k && e[bb] + c[bb] >= k) blo_sh = 8 * tid + bb;
+    }
+    reinterpret_cast<u32x4*>(a.wg_off + list * kHistBins)[tid] =
+        u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+    reinterpret_cast<u32x4*>(hist)[2 * tid] = u32x4{e[0], e[1], e[2], e[3]};
+    reinterpret_cast<u32x4*>(hist)[2 * tid + 1] = u32x4{e[4], e[5], e[6], e[7]};
+    __syncthreads();
+    const uint32_t blo = blo_sh;
+    const int32_t wg_keys = kHistChunks * a.chunk_keys;
+    const int64_t wg_end =
+        min<int64_t>(min<int64_t>(wg_begin + static_cast<int64_t>(wg_keys), a.n_cols), n_vis);
+    const int32_t n_valid = wg_end > wg_begin ? static_cast<int32_t>(wg_end - wg_begin) : 0;
+    uint64_t* lst = a.wg_list + list * wg_keys;
+#pragma unroll
+    for (int u = 0; u < kHistWgKeysMax / 256; ++u) {
+      const int32_t el = tid + 256 * u;
+      if (el < n_valid) {
+        const uint32_t key = score_order_key(sc[el]);
+        const uint32_t bin = key >> kHistShift;
+        if (bin >= blo) {
+          const uint32_t slot = atomicAdd(&hist[bin], 1u);
+          if (slot < static_cast<uint32_t>(wg_keys))
+            lst[slot] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(wg_begin + el);
+        }
+      }
+    }
   }
 }
 
@@ -1254,7 +1350,12 @@ hipError_t launch_score_fp8q(const ScoreArgs& a, hipStream_t stream) {
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
   int64_t blocks;
   if (a.wg_hist) {
-    blocks = a.n_rows * a.wg_per_row;
+    // the workgroup's scores and bucket offsets live in LDS arrays of kHistWgKeysMax keys
+    if (!a.wg_off || !a.wg_list || a.chunk_keys <= 0 ||
+        kHistChunks * a.chunk_keys > kHistWgKeysMax || a.wg_per_row <= 0 || a.sel_k < 1 ||
+        static_cast<int64_t>(a.wg_per_row) * kHistChunks * a.chunk_keys < a.n_cols)
+      return hipErrorInvalidValue;
+    blocks = (a.n_rows + kXcds - 1) / kXcds * kXcds * a.wg_per_row;
   } else {
     const int64_t waves = a.n_rows * a.n_chunks;
     blocks = (waves + 3) / 4;

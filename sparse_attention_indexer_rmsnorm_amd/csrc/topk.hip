@@ -950,29 +950,35 @@ __global__ __launch_bounds__(64 * kBlockWaves) void topk_block_kernel(TopkArgs a
   }
 }
 
-// ---- selection from per-workgroup histograms (decode-shaped batches) ----------------------------
+// ---- selection from bucketed lists (decode-shaped batches) -------------------------------------
 //
-// Workgroup (row r, segment g) of 256 threads, thread t owning scores e0 .. e0 + PER - 1 of the
-// segment (e0 = g * seg_len + PER t) and histogram bins 8 t .. 8 t + 7:
-//   1. the row's histogram is the sum of its score workgroups' histograms; the bin B holding the
-//      k-th largest score, the count `above` of higher bins and B's count c_B follow from a
-//      descending scan.  The histograms of the score workgroups before this segment give the
-//      numbers of higher-bin and of bin-B keys that precede it in the row;
-//   2. every key of a higher bin is a winner and goes straight to its output position (in index
-//      order, after the winners of earlier segments); bin B's keys go to the row's candidate list
-//      at their position in index order;
-//   3. if bin B's keys all win, they go straight to the output instead and nothing more is
-//      needed; otherwise the row's last workgroup to finish (one atomic counter per row, zeroed
-//      by the score kernel) refines the candidates with two radix passes (11 and 10 bits) to the
-//      exact k-th largest key T and how many keys equal to T are taken, then writes the
-//      candidates above T and the lowest-indexed ones equal to T after the higher-bin winners.
-// The output is deterministic: higher-bin winners in index order, then the threshold bin's.
-// Scanning the whole row for bin B in every workgroup instead (no hand-over) was measured slower:
-// the scan is bound by issuing per-score work, repeated by every workgroup of the row.
-constexpr int kHistWaves = 4;
+// One workgroup of 1024 threads per row.  The scoring kernel left, for each of its workgroups j
+// of the row, a histogram of the order keys' top 11 bits, the start of every bin's bucket, and
+// the keys bucketed by bin, highest bin first (see ScoreArgs).  Thread t owns bins 2 t, 2 t + 1:
+//   1. the row's histogram is the sum of its workgroups'; a descending scan gives the bin B that
+//      holds the k-th largest key, the count `above` of higher bins and B's count c_B;
+//   2. list j holds hi_j keys of higher bins at its front and bin B's eq_j keys behind them
+//      (two 16-bit loads per list); prefix sums over the lists place them: the `above` winners
+//      and bin B's keys are loaded into registers;
+//   3. unless bin B's keys all win, two radix passes over them (bits 20..10, then 9..0) give the
+//      exact k-th largest key T and how many keys equal to T win; when they are only some of
+//      the keys equal to T, a bitmap of those keys' indices gives the index of the last one
+//      taken (ties go to the lower index);
+//   4. a bitmap of the winners' indices and its running popcount give every winner its output
+//      position: each row comes out sorted by index, and the result is deterministic although
+//      the buckets are filled in no set order.
+// The scoring kernel writes no bucket below its workgroup's own k-th largest key; every read
+// here is of a bucket at or above B, which lies at or above each of those.
+constexpr int kHistWaves = 16;         // 1024 threads: 4 waves per SIMD on the row's CU
 constexpr int kHistThreads = 64 * kHistWaves;
-constexpr int kXcds = 8;               // MI355X: 8 XCDs, each with its own L2
-constexpr int kHistCandLds = 4096;     // candidates refined from LDS; more are read from memory
+constexpr int kBinsPer = kHistBins / kHistThreads;   // histogram bins per thread
+constexpr int kListCandLds = 4096;     // bin B's keys held in registers; more are read from the lists
+constexpr int kSpec = 6;               // list positions each thread reads before the threshold is known
+constexpr int kBitWords = kHistMaxCols / 32;
+constexpr int kWordsPerThread = kBitWords / kHistThreads;
+static_assert(kWordsPerThread * kHistThreads == kBitWords && kWordsPerThread % 4 == 0,
+              "bitmap words per thread");
+static_assert(kBitWords * 2 <= kHistBins * 4, "16-bit word ranks fit the digit counts' area");
 
 // Exclusive prefixes over the workgroup (thread order) of N counts, and their totals (one pair
 // of barriers for all N).
@@ -1002,323 +1008,405 @@ __device__ __forceinline__ void wg_excl_scan(const uint32_t (&v)[N], uint32_t (*
   __syncthreads();   // red is reused by the next scan
 }
 
-template <int PER>
-__global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) {
+// The lists holding entries f[0..N) of a run laid out list after list: for each, the largest
+// j < n with off[j] <= f (off non-decreasing from off[0] = 0, so empty lists are passed over).
+// A branch-free search of fixed depth (n <= kMaxHistWgPerRow), so that the N searches' LDS reads
+// are in flight together.
+template <int N>
+__device__ __forceinline__ void lists_of(const uint32_t* off, int n, const uint32_t (&f)[N],
+                                         int (&j)[N]) {
+  static_assert(kMaxHistWgPerRow == 64, "six halving steps");
+#pragma unroll
+  for (int u = 0; u < N; ++u) j[u] = 0;
+#pragma unroll
+  for (int step = 32; step >= 1; step >>= 1) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int mid = min(j[u] + step, n - 1);
+      j[u] = off[mid] <= f[u] ? mid : j[u];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kHistThreads) void topk_list_kernel(HistSelArgs a) {
   __shared__ uint32_t red[4][kHistWaves];
-  __shared__ uint32_t info[4];
-  __shared__ __attribute__((aligned(16))) uint32_t sub[kHistBins];
-  __shared__ __attribute__((aligned(16))) uint64_t lcand[kHistCandLds];
+  __shared__ uint32_t info[8];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_l[kHistBins];   // the row's histogram
+  __shared__ __attribute__((aligned(16))) uint32_t sub[kHistBins];      // digit counts, then ranks
+  __shared__ __attribute__((aligned(16))) uint32_t bits[kBitWords];
+  __shared__ uint32_t lhoff[kMaxHistWgPerRow], leoff[kMaxHistWgPerRow], lhi[kMaxHistWgPerRow];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Workgroups go to the 8 XCDs in turn (workgroup b to XCD b % 8): every segment of a row is
-  // given to the same XCD, so the row's histograms and scores are read into one L2 and hit there.
-  const int64_t slot = blockIdx.x / kXcds;
-  const int64_t r = (slot / a.n_seg) * kXcds + blockIdx.x % kXcds;
-  const int32_t seg = static_cast<int32_t>(slot % a.n_seg);
+  const int64_t r = blockIdx.x;
   if (r >= a.n_rows) return;
+  static_assert(kHistBins == 2 * kHistThreads, "two digit counters per thread");
   const int32_t k = a.k;
-  const float* row = a.scores + r * a.cols;
+  const int32_t wpr = a.wg_per_row;
+  const int32_t wk = a.wg_keys;
+  const uint64_t* lrow = a.wg_list + r * wpr * static_cast<int64_t>(wk);
   int32_t* oi = a.out_idx + r * k;
   float* ov = a.out_val ? a.out_val + r * k : nullptr;
-  const int32_t seg_begin = seg * a.seg_len;
-  const int32_t e0 = seg_begin + PER * tid;
-  if (tid == 0) {   // defined even if no thread finds the threshold bin below
-    info[0] = 0u;
-    info[1] = 0u;
-    info[2] = 0u;
-    info[3] = 0u;
+  if (tid < 8) info[tid] = 0u;
+  reinterpret_cast<u32x4*>(bits)[tid] = u32x4{0u, 0u, 0u, 0u};
+  reinterpret_cast<uint2*>(sub)[tid] = uint2{0u, 0u};
+  reinterpret_cast<uint2*>(hist_l)[tid] = uint2{0u, 0u};
+  // The front of every list, read before anything about the row is known: thread t reads
+  // positions q + tpl u (u < kSpec) of list t / tpl, tpl = 1024 / wg_per_row threads per list,
+  // within the first min(kSpec tpl, k) positions.  A list's keys of bin B and above lie at its
+  // front; they are usually all inside this window, which is then all that is read.
+  // (info: [5] keys in the window, [7] one above the highest bin at which the window cuts a list.)
+  const int tpl = kHistThreads / wpr;
+  const int sj = tid / tpl, sq = tid % tpl;
+  const int32_t swin = min(min(kSpec * tpl, k), wk);
+  uint64_t spec[kSpec];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int32_t p = sq + tpl * u;
+    spec[u] = sj < wpr && p < swin ? lrow[static_cast<int64_t>(sj) * wk + p] : 0ull;
   }
-  // The row's visible count, its scores and its histograms are requested together: none of the
-  // loads depends on another, so they share one round trip.
   const int32_t len_raw = a.row_nvis[r];
-
-  // scores of this thread (16-byte loads through a view of the row's columns, rounded up to 4,
-  // which stays inside the workspace; loads wholly past the view read 0, and slots at or past
-  // the visible count are masked below)
-  const __amdgpu_buffer_rsrc_t view = buffer_view(row, static_cast<int32_t>((a.cols + 3) & ~3));
-  uint32_t key[PER];
-#pragma unroll
-  for (int j = 0; j < PER; j += 4) {
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  view, (e0 + j) * 4, 0, 0));
-    key[j] = v.x;
-    key[j + 1] = v.y;
-    key[j + 2] = v.z;
-    key[j + 3] = v.w;
-  }
-
-  // 1. the row's histogram (bins 8 t .. 8 t + 7 here), and its part before this segment
-  uint32_t tot[8], prev[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) tot[b] = prev[b] = 0u;
-  const int32_t w0 = seg * (a.seg_len / a.wg_keys);
-  const uint16_t* hrow = a.wg_hist + r * static_cast<int64_t>(a.wg_per_row) * kHistBins + 8 * tid;
-  // 16 histograms per round, all requested before the first is summed
-  for (int32_t wr = 0; wr < a.wg_per_row; wr += 16) {
-    u32x4 h[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      h[q] = wr + q < a.wg_per_row
-                 ? *reinterpret_cast<const u32x4*>(hrow + static_cast<int64_t>(wr + q) * kHistBins)
-                 : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint32_t c[8] = {h[q].x & 0xFFFFu, h[q].x >> 16, h[q].y & 0xFFFFu, h[q].y >> 16,
-                             h[q].z & 0xFFFFu, h[q].z >> 16, h[q].w & 0xFFFFu, h[q].w >> 16};
-      const bool before = wr + q < w0;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        tot[b] += c[b];
-        prev[b] += before ? c[b] : 0u;
-      }
-    }
-  }
-
   const int64_t len = len_raw < 0 ? 0 : (len_raw > a.cols ? a.cols : len_raw);
   const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(len));
-  if (n <= k) {   // every visible key is selected, then padding
+  if (n <= k) {
+    // Every visible key is selected.  No workgroup of the row holds more than k keys, so every
+    // list is written in full, and the lists' n entries lie at the front of the row's area.
+    // All of a thread's entries are requested before any is stored.
+    constexpr int kPer = kMaxTopk / kHistThreads;
+    uint64_t e[kPer];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int32_t e = e0 + j;
-      if (e < n) {
-        oi[e] = e;
-        if (ov) ov[e] = key_value(score_order_key(__uint_as_float(key[j])));
+    for (int u = 0; u < kPer; ++u) {
+      const int32_t f = tid + kHistThreads * u;
+      e[u] = f < n ? lrow[f] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t idx = static_cast<uint32_t>(e[u]);
+      if (tid + kHistThreads * u < n && idx < static_cast<uint32_t>(k)) {
+        oi[idx] = static_cast<int32_t>(idx);
+        if (ov) ov[idx] = key_value(static_cast<uint32_t>(e[u] >> 32));
       }
     }
-    if (seg == 0)
-      for (int32_t e = n + tid; e < k; e += kHistThreads) {
-        oi[e] = -1;
-        if (ov) ov[e] = -INFINITY;
-      }
+    for (int32_t f = n + tid; f < k; f += kHistThreads) {
+      oi[f] = -1;
+      if (ov) ov[f] = -INFINITY;
+    }
     return;
   }
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    key[j] = e0 + j < n ? score_order_key(__uint_as_float(key[j])) : 0u;
 
-  // descending scan: thread t's bins lie above those of every lower thread
-  uint32_t mine = 0;
-#pragma unroll
-  for (int b = 0; b < 8; ++b) mine += tot[b];
+  // 1. The bin B holding the k-th largest key, from an LDS histogram of the window.  A position
+  //    below min(the workgroup's key count, k) always holds one of its keys (the scoring kernel
+  //    leaves out only keys below its own k-th largest), and a list is bucketed from its highest
+  //    bin down, so the window holds all of a list's keys of every bin above the bin of its last
+  //    window entry.  When the bin where the window's count from the top reaches k lies above
+  //    every such cut, it is the row's B, and the window holds every key of B and above.
+  //    Otherwise the workgroups' histograms give B and the lists are read in full (below).
+  __syncthreads();   // the LDS counters cleared above are zero before any thread adds to them
+  const int64_t cnt_l =
+      sj < wpr ? min<int64_t>(max<int64_t>(n - static_cast<int64_t>(sj) * wk, 0), wk) : 0;
+  const int32_t lim = static_cast<int32_t>(min<int64_t>(cnt_l, swin));
   {
-    const uint32_t incl = wave_incl_scan(mine, 0u, [](uint32_t p, uint32_t q) { return p + q; });
-    if (lane == 63) red[0][wid] = incl;
-    __syncthreads();
-    uint32_t higher = lane_value(incl, 63) - incl;      // later lanes of this wave
+    // The lanes of a wave hold consecutive positions of a list (for each u), and a list's
+    // buckets are runs of positions, so equal bins sit in runs of lanes: the first lane of each
+    // run adds the run's length (one LDS add per bin instead of one per key; the window's keys
+    // crowd into a few bins).
+    uint32_t nv = 0;
 #pragma unroll
-    for (int w = 0; w < kHistWaves; ++w)
-      if (w > wid) higher += red[0][w];
-    if (higher < static_cast<uint32_t>(k) && higher + mine >= static_cast<uint32_t>(k)) {
-      uint32_t acc = higher;
+    for (int u = 0; u < kSpec; ++u) {
+      const int32_t p = sq + tpl * u;
+      const bool in = p < lim;
+      const uint32_t bin = in ? static_cast<uint32_t>(spec[u] >> 32) >> kHistShift : 0xFFFFFFFFu;
+      // the previous lane's bin (DPP wave_shr:1); lane 0 has none
+      const uint32_t prev = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+          static_cast<int>(0xFFFFFFFEu), static_cast<int>(bin), 0x138, 0xF, 0xF, false));
+      const bool head = in && (sq == 0 || prev != bin);
+      const uint64_t ends = __ballot(head) | __ballot(!in);   // a run stops before these lanes
+      if (head) {
+        const uint64_t later = lane == 63 ? 0ull : ends >> (lane + 1);
+        const uint32_t run = later ? static_cast<uint32_t>(__builtin_ctzll(later)) + 1u
+                                   : static_cast<uint32_t>(64 - lane);
+        atomicAdd(&hist_l[bin], run);
+      }
+      nv += in ? 1u : 0u;
+      if (in && p == lim - 1 && lim < cnt_l) atomicMax(&info[7], bin + 1u);   // the list is cut here
+    }
+    nv = wave_incl_scan(nv, 0u, [](uint32_t p, uint32_t q) { return p + q; });
+    if (lane == 63) atomicAdd(&info[5], nv);
+  }
+  __syncthreads();
+  uint32_t B, above_raw, count_b;
+  wave_find_bin32<kHistBins>(hist_l, static_cast<uint32_t>(k), lane, &B, &above_raw, &count_b);
+  // Every bin above B lies above every cut when B is at or above the highest cut bin: then B
+  // and the count above it are the row's.  Bin B itself is whole in the window only when B lies
+  // above every cut.
+  const bool b_ok = info[5] >= static_cast<uint32_t>(k) && B + 1u >= info[7];
+  const bool fast = b_ok && B >= info[7];
+  if (!b_ok) {
+    // the row's histogram: the sum of its workgroups' (thread t: bins 2 t, 2 t + 1)
+    static_assert(kBinsPer == 2, "two 16-bit counts per thread and list");
+    uint32_t tot[kBinsPer] = {0u, 0u};
+    const uint32_t* hrow = reinterpret_cast<const uint32_t*>(
+        a.wg_hist + r * static_cast<int64_t>(wpr) * kHistBins + kBinsPer * tid);
+    for (int32_t wr = 0; wr < wpr; wr += 16) {   // 16 histograms requested before any is summed
+      uint32_t h[16];
 #pragma unroll
-      for (int b = 7; b >= 0; --b) {
-        if (acc < static_cast<uint32_t>(k) && acc + tot[b] >= static_cast<uint32_t>(k)) {
-          info[0] = 8 * tid + b;
-          info[1] = acc;
-          info[2] = tot[b];
-        }
-        acc += tot[b];
+      for (int q = 0; q < 16; ++q)
+        h[q] = wr + q < wpr ? hrow[static_cast<int64_t>(wr + q) * (kHistBins / 2)] : 0u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        tot[0] += h[q] & 0xFFFFu;
+        tot[1] += h[q] >> 16;
       }
     }
+    __syncthreads();   // every wave has read the window's histogram
+    reinterpret_cast<uint2*>(hist_l)[tid] = uint2{tot[0], tot[1]};
+    __syncthreads();
+    wave_find_bin32<kHistBins>(hist_l, static_cast<uint32_t>(k), lane, &B, &above_raw, &count_b);
+  }
+  if (!fast) {
+    // list j holds hi_j keys of higher bins at its front and bin B's eq_j keys behind them (two
+    // 16-bit loads per list); prefix sums over the lists place them, and their total of bin B
+    // is B's count
+    uint32_t hj = 0, ej = 0;
+    if (tid < wpr) {
+      const int64_t L = (r * wpr + tid) * static_cast<int64_t>(kHistBins) + B;
+      hj = a.wg_off[L];
+      ej = a.wg_hist[L];
+    }
+    uint32_t pre[2], sums[2];
+    wg_excl_scan<2>({hj, ej}, red, lane, wid, pre, sums);
+    if (tid < wpr) {
+      lhoff[tid] = pre[0];
+      leoff[tid] = pre[1];
+      lhi[tid] = hj;
+    }
+    count_b = sums[1];
     __syncthreads();
   }
-  const uint32_t B = info[0];
-  const uint32_t above = min(info[1], static_cast<uint32_t>(k));
-  const uint32_t c_b = min(info[2], static_cast<uint32_t>(n));
+  const uint32_t above = min(above_raw, static_cast<uint32_t>(k));
+  const uint32_t c_b = min(count_b, static_cast<uint32_t>(n));
   const uint32_t k_rem = static_cast<uint32_t>(k) - above;   // 1 <= k_rem <= c_b
   const bool all_win = c_b == k_rem;
-  // Every store below is also bounded by its array (k outputs), whatever the counts: they agree
-  // with the scores by construction (the scoring kernel counted exactly the values it wrote),
-  // and the bounds only keep a broken invariant from writing out of range.
+  // Every access below is also bounded by its array, whatever the counts: they agree with the
+  // lists by construction (the scoring kernel counted exactly the keys it bucketed), and the
+  // bounds only keep a broken invariant from reading or writing out of range.
 
-  // 2. higher-bin winners (and, when bin B wins whole, its keys) of this segment
-  uint32_t p_hi = 0, p_eq = 0;
+  // 2. The window's keys of higher bins (winners) and of bin B (candidates), and the
+  //    candidates' first radix digits (bits 20..10).
+  uint32_t hm = 0u, em = 0u;   // bit u: spec[u] is a higher-bin key / a bin-B key
+  if (fast) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const uint32_t bin = 8 * tid + b;
-    p_hi += bin > B ? prev[b] : 0u;
-    p_eq += bin == B ? prev[b] : 0u;
-  }
-  uint32_t n_hi = 0, n_eq = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const uint32_t bin = key[j] >> kHistShift;
-    n_hi += (e0 + j < n && bin > B) ? 1u : 0u;
-    n_eq += (e0 + j < n && bin == B) ? 1u : 0u;
-  }
-  uint32_t sc_pre[4], sc_tot[4];
-  wg_excl_scan<4>({p_hi, p_eq, n_hi, n_eq}, red, lane, wid, sc_pre, sc_tot);
-  uint64_t* cand = a.cand + r * a.cols;
-  // before this segment (totals of the earlier histograms' counts), then this thread's place
-  const uint32_t hi0 = sc_tot[0] + sc_pre[2];
-  const uint32_t eq0 = sc_tot[1] + sc_pre[3];
-  if (all_win) {
-    uint32_t at_hi = hi0, at_eq = eq0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int32_t e = e0 + j;
-      const uint32_t bin = key[j] >> kHistShift;
-      const bool hi = e < n && bin > B;
-      const bool eq = e < n && bin == B;
-      if (hi && at_hi < above) {
-        oi[at_hi] = e;
-        if (ov) ov[at_hi] = key_value(key[j]);
-      }
-      if (eq && above + at_eq < static_cast<uint32_t>(k)) {
-        oi[above + at_eq] = e;
-        if (ov) ov[above + at_eq] = key_value(key[j]);
-      }
-      at_hi += hi ? 1u : 0u;
-      at_eq += eq ? 1u : 0u;
+    for (int u = 0; u < kSpec; ++u) {
+      const uint32_t kk = static_cast<uint32_t>(spec[u] >> 32);
+      const uint32_t bin = kk >> kHistShift;
+      const bool in = sq + tpl * u < lim;
+      const bool h = in && bin > B, e = in && bin == B;
+      hm |= h ? 1u << u : 0u;
+      em |= e ? 1u << u : 0u;
+      if (e && !all_win) atomicAdd(&sub[(kk >> 10) & (kHistBins - 1)], 1u);
     }
-    return;
+    __syncthreads();
   }
-
-  // A row of one segment is this workgroup's alone: its candidates go to the LDS list, in
-  // index order, and the refinement below starts at once (c_b <= seg_len <= kHistCandLds).
-  const bool local = a.n_seg == 1;
-  if (local) {
-    uint32_t at_eq = eq0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int32_t e = e0 + j;
-      const bool eq = e < n && (key[j] >> kHistShift) == B;
-      if (eq && at_eq < c_b)
-        lcand[at_eq] = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(e);
-      at_eq += eq ? 1u : 0u;
-    }
-  }
-  // else bin B's keys to the row's candidate list, which the row's last workgroup refines (3.)
-  if (!local) {
-    uint32_t at_eq = eq0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int32_t e = e0 + j;
-      const bool eq = e < n && (key[j] >> kHistShift) == B;
-      if (eq && at_eq < c_b) {
-        // an agent-scope store writes through to where every XCD's loads of it look
-        __hip_atomic_store(cand + at_eq,
-                           (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(e),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      at_eq += eq ? 1u : 0u;
-    }
-  }
-
-  // 3. the row's last workgroup refines the threshold bin.  The hand-over needs no cache-wide
-  //    write-back or invalidation (an agent-scope fence is both, on every XCD's L2): the
-  //    candidates were stored with agent-scope atomic stores, each thread waits until its stores
-  //    are acknowledged before the barrier, the counter is an agent-scope atomic, and the last
-  //    workgroup reads the candidates with agent-scope atomic loads issued after the counter
-  //    returned.  The segment's higher-bin winners are stored after the counter is requested,
-  //    as a fixed number of buffer stores (a key that is not one writes past the output view,
-  //    which drops the store): the wait for the counter's value then leaves them in flight,
-  //    and they hold up neither the hand-over nor the workgroups that are not last.
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
-  int32_t ticket = a.n_seg - 1;   // a local row's workgroup is its last
-  if (tid == 0 && !local)
-    ticket = __hip_atomic_fetch_add(a.row_ctr + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  {
-    const __amdgpu_buffer_rsrc_t vi = buffer_view(reinterpret_cast<const float*>(oi), k);
-    const __amdgpu_buffer_rsrc_t vv = buffer_view(ov, ov ? k : 0);
-    constexpr uint32_t kDrop = 0x40800000u;   // past every output view (k <= 2048 values)
-    uint32_t at_hi = hi0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int32_t e = e0 + j;
-      const bool hi = e < n && (key[j] >> kHistShift) > B;
-      const uint32_t at = (hi && at_hi < above) ? 4u * at_hi : kDrop;
-      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(e), vi, at, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key[j])), vv, at, 0, 0);
-      at_hi += hi ? 1u : 0u;
-    }
-  }
-  if (tid == 0) info[3] = static_cast<uint32_t>(ticket);
-  // LDS-only barrier: the winner stores stay in flight
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  if (info[3] != static_cast<uint32_t>(a.n_seg - 1)) return;
-
-  auto load_cand = [&](uint32_t c) {
-    return __hip_atomic_load(cand + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Otherwise every list's keys of bin B and above are read in full, from the places found
+  // above: kMaxTopk / 1024 winners and kListCandLds / 1024 candidates per thread (candidates
+  // beyond that are read from the lists where needed).
+  constexpr int kHiPer = kMaxTopk / kHistThreads;
+  constexpr int kEqPer = kListCandLds / kHistThreads;
+  static_assert(kHiPer + kEqPer <= kSpec, "the searched path reuses the window's registers");
+  const bool listed = fast || c_b <= static_cast<uint32_t>(kListCandLds);
+  auto entry = [&](int j, uint32_t p) -> uint64_t {
+    return p < static_cast<uint32_t>(wk) ? lrow[static_cast<int64_t>(j) * wk + p] : 0ull;
   };
-  const bool listed = c_b <= static_cast<uint32_t>(kHistCandLds);
-  if (listed && !local) {
-    for (uint32_t c = tid; c < c_b; c += kHistThreads) lcand[c] = load_cand(c);
-    __syncthreads();
-  }
-  auto cand_at = [&](uint32_t c) { return listed ? lcand[c] : load_cand(c); };
-  // pass 1: bits 20..10 of the keys of bin B; pass 2: bits 9..0 of those in the chosen digit
-  uint32_t want = k_rem;
-  uint32_t prefix = B;
-  uint32_t T = 0u, eq_take = 0u;
-  bool resolved = false;
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    const int width = pass == 0 ? 11 : 10;
-    const int nb = 1 << width;
-    for (int c = tid; c < nb; c += kHistThreads) sub[c] = 0u;
-    __syncthreads();
-    for (uint32_t c = tid; c < c_b; c += kHistThreads) {
-      const uint32_t kk = static_cast<uint32_t>(cand_at(c) >> 32);
-      if ((kk >> (shift + width)) == prefix) atomicAdd(&sub[(kk >> shift) & (nb - 1)], 1u);
+  auto cand_mem = [&](uint32_t f) -> uint64_t {
+    uint32_t ff[1] = {f};
+    int j[1];
+    lists_of<1>(leoff, wpr, ff, j);
+    return entry(j[0], lhi[j[0]] + f - leoff[j[0]]);
+  };
+  // fn(e) for every key of bin B
+  auto for_cand = [&](auto fn) {
+    if (listed) {
+#pragma unroll
+      for (int u = 0; u < kSpec; ++u)
+        if (em & (1u << u)) fn(spec[u]);
+    } else {
+      for (uint32_t c = tid; c < c_b; c += kHistThreads) fn(cand_mem(c));
     }
-    __syncthreads();
-    uint32_t d, gt, cnt;
-    if (pass == 0)
-      wave_find_bin32<2048>(sub, want, lane, &d, &gt, &cnt);
-    else
-      wave_find_bin32<1024>(sub, want, lane, &d, &gt, &cnt);
-    prefix = (prefix << width) | d;
-    want -= gt;
-    __syncthreads();   // sub is cleared again by the next pass
-    // Every key of the chosen digit is taken (the usual case: bin B's few hundred keys spread
-    // over 2048 digits): the winners are the keys whose top 21 bits are at least `prefix`, i.e.
-    // the keys above T = (prefix << 10) - 1 with no tie taken, and the second pass is not needed.
-    // (cnt and want come from the same LDS counts in every wave, so the exit is uniform; a zero
-    // prefix, only reachable by NaN keys, keeps the second pass.)
-    if (pass == 0 && cnt == want && prefix != 0u) {
-      T = (prefix << 10) - 1u;
-      eq_take = 0u;
-      resolved = true;
-      break;
+  };
+  if (!fast) {
+    hm = 0u;
+    em = 0u;
+    uint32_t fh[kHiPer], fe[kEqPer];
+    int jh[kHiPer], je[kEqPer];
+#pragma unroll
+    for (int u = 0; u < kHiPer; ++u) fh[u] = tid + kHistThreads * u;
+#pragma unroll
+    for (int u = 0; u < kEqPer; ++u) fe[u] = tid + kHistThreads * u;
+    lists_of<kHiPer>(lhoff, wpr, fh, jh);
+    lists_of<kEqPer>(leoff, wpr, fe, je);
+#pragma unroll
+    for (int u = 0; u < kHiPer; ++u) {
+      const bool h = fh[u] < above;
+      spec[u] = h ? entry(jh[u], fh[u] - lhoff[jh[u]]) : 0ull;
+      hm |= h ? 1u << u : 0u;
     }
-  }
-  if (!resolved) {
-    T = prefix;
-    eq_take = want;
+#pragma unroll
+    for (int u = 0; u < kEqPer; ++u) {
+      const bool e = listed && fe[u] < c_b;
+      spec[kHiPer + u] = e ? entry(je[u], lhi[je[u]] + fe[u] - leoff[je[u]]) : 0ull;
+      em |= e ? 1u << (kHiPer + u) : 0u;
+    }
+    if (!all_win) {   // the first digits again, over every candidate
+      for (int c = tid; c < kHistBins; c += kHistThreads) sub[c] = 0u;
+      __syncthreads();
+      for_cand([&](uint64_t e) {
+        atomicAdd(&sub[(static_cast<uint32_t>(e >> 32) >> 10) & (kHistBins - 1)], 1u);
+      });
+      __syncthreads();
+    }
   }
 
-  // candidates above T, then the lowest-indexed ones equal to T, after the higher-bin winners:
-  // thread t visits a contiguous slice of the (index-ordered) list
-  const uint32_t per_t = (c_b + kHistThreads - 1) / kHistThreads;
-  const uint32_t c_lo = min(c_b, per_t * tid), c_hi = min(c_b, c_lo + per_t);
-  uint32_t m_gt = 0, m_eq = 0;
-  for (uint32_t c = c_lo; c < c_hi; ++c) {
-    const uint32_t kk = static_cast<uint32_t>(cand_at(c) >> 32);
-    m_gt += kk > T ? 1u : 0u;
-    m_eq += kk == T ? 1u : 0u;
-  }
-  uint32_t o_pre[2], o_tot[2];
-  wg_excl_scan<2>({m_gt, m_eq}, red, lane, wid, o_pre, o_tot);
-  uint32_t g_before = o_pre[0], e_before = o_pre[1];
-  for (uint32_t c = c_lo; c < c_hi; ++c) {
-    const uint64_t ce = cand_at(c);
-    const uint32_t kk = static_cast<uint32_t>(ce >> 32);
-    uint32_t pos = 0xFFFFFFFFu;
-    if (kk > T) pos = g_before + min(e_before, eq_take);
-    else if (kk == T && e_before < eq_take) pos = g_before + e_before;
-    if (pos < k_rem) {
-      oi[above + pos] = static_cast<int32_t>(static_cast<uint32_t>(ce));
-      if (ov) ov[above + pos] = key_value(kk);
+  // 3. the exact threshold T among bin B's keys, and which keys equal to T win.  Every key of
+  //    the chosen first digit usually wins (bin B's few hundred keys spread over 2048 digits):
+  //    then the winners are the keys above T = (prefix << 10) - 1, no tie taken, and the second
+  //    digit (bits 9..0) is not needed.  (The digit counts are the same LDS values in every
+  //    wave, so every branch here is uniform; a zero prefix, only reachable by NaN keys, takes
+  //    the second digit.)
+  uint32_t T = 0u, eq_take = 0u;
+  bool ties_all = true;   // every key equal to T that is a candidate wins
+  if (!all_win) {
+    uint32_t d, gt, cnt;
+    wave_find_bin32<kHistBins>(sub, k_rem, lane, &d, &gt, &cnt);
+    const uint32_t prefix = (B << 11) | d;
+    uint32_t want = k_rem - gt;
+    if (cnt == want && prefix != 0u) {
+      T = (prefix << 10) - 1u;
+    } else {
+      __syncthreads();   // every wave has read the first digits' counts
+      for (int c = tid; c < 1024; c += kHistThreads) sub[c] = 0u;
+      __syncthreads();
+      for_cand([&](uint64_t e) {
+        const uint32_t kk = static_cast<uint32_t>(e >> 32);
+        if ((kk >> 10) == prefix) atomicAdd(&sub[kk & 1023u], 1u);
+      });
+      __syncthreads();
+      uint32_t d2, gt2, cnt2;
+      wave_find_bin32<1024>(sub, want, lane, &d2, &gt2, &cnt2);
+      want -= gt2;
+      T = (prefix << 10) | d2;
+      eq_take = want;
+      ties_all = cnt2 == want;
     }
-    g_before += kk > T ? 1u : 0u;
-    e_before += kk == T ? 1u : 0u;
+  }
+  auto wins = [&](uint32_t kk, uint32_t idx, uint32_t cut) {
+    return all_win || kk > T || (kk == T && eq_take > 0u && (ties_all || idx <= cut));
+  };
+  auto set_bit = [&](uint32_t idx) {
+    if (idx < static_cast<uint32_t>(kHistMaxCols)) atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+  };
+  // Thread t owns bitmap words 4 t .. 4 t + 3: the set bits before each of them (after the
+  // barrier the caller provides once every bit is set), using partial-sum slot `slot` of red.
+  auto word_ranks = [&](int slot, uint32_t (&pre)[4]) {
+    static_assert(kWordsPerThread == 4, "one 16-byte word group per thread");
+    const u32x4 x = reinterpret_cast<const u32x4*>(bits)[tid];
+    pre[0] = 0u;
+    pre[1] = __popc(x.x);
+    pre[2] = pre[1] + __popc(x.y);
+    pre[3] = pre[2] + __popc(x.z);
+    const uint32_t mine = pre[3] + __popc(x.w);
+    const uint32_t incl = wave_incl_scan(mine, 0u, [](uint32_t p, uint32_t q) { return p + q; });
+    if (lane == 63) red[slot][wid] = incl;
+    __syncthreads();
+    uint32_t base = incl - mine;
+#pragma unroll
+    for (int w = 0; w < kHistWaves; ++w) base += w < wid ? red[slot][w] : 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pre[c] += base;
+  };
+  uint32_t cut = 0xFFFFFFFFu;
+  if (!ties_all) {
+    // some of the keys equal to T win: the eq_take lowest-indexed ones, up to index `cut`
+    for_cand([&](uint64_t e) {
+      if (static_cast<uint32_t>(e >> 32) == T) set_bit(static_cast<uint32_t>(e));
+    });
+    __syncthreads();
+    uint32_t pre[4];
+    word_ranks(2, pre);
+    const u32x4 x = reinterpret_cast<const u32x4*>(bits)[tid];
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t cnt = __popc(w4[c]);
+      if (pre[c] < eq_take && pre[c] + cnt >= eq_take) {
+        uint32_t y = w4[c];
+        for (uint32_t i = pre[c] + 1; i < eq_take; ++i) y &= y - 1u;   // drop the lower bits taken
+        info[4] = 32u * (4 * tid + c) + static_cast<uint32_t>(__builtin_ctz(y));
+      }
+    }
+    __syncthreads();
+    reinterpret_cast<u32x4*>(bits)[tid] = u32x4{0u, 0u, 0u, 0u};
+    cut = info[4];
+    __syncthreads();
+  }
+
+  // 4. output positions from the bitmap of the winners' indices
+  uint32_t wm = hm;   // bit u: spec[u] wins
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u)
+    if ((em & (1u << u)) &&
+        wins(static_cast<uint32_t>(spec[u] >> 32), static_cast<uint32_t>(spec[u]), cut))
+      wm |= 1u << u;
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u)
+    if (wm & (1u << u)) set_bit(static_cast<uint32_t>(spec[u]));
+  if (!listed) {
+    for (uint32_t c = tid; c < c_b; c += kHistThreads) {
+      const uint64_t e = cand_mem(c);
+      if (wins(static_cast<uint32_t>(e >> 32), static_cast<uint32_t>(e), cut))
+        set_bit(static_cast<uint32_t>(e));
+    }
+  }
+  __syncthreads();
+  uint16_t* rank16 = reinterpret_cast<uint16_t*>(sub);   // output position of each word's first
+  {
+    uint32_t pre[4];
+    word_ranks(3, pre);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rank16[4 * tid + c] = static_cast<uint16_t>(pre[c]);
+  }
+  __syncthreads();
+  auto pos_of = [&](uint32_t idx, uint32_t rank_w, uint32_t word) {
+    return rank_w + __popc(word & ((1u << (idx & 31)) - 1u));
+  };
+  auto put = [&](uint64_t e, uint32_t pos) {
+    if (pos < static_cast<uint32_t>(k)) {
+      oi[pos] = static_cast<int32_t>(static_cast<uint32_t>(e));
+      if (ov) ov[pos] = key_value(static_cast<uint32_t>(e >> 32));
+    }
+  };
+  {
+    // every word read first, then the stores
+    uint32_t rw[kSpec], bw[kSpec];
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u) {
+      const uint32_t idx = static_cast<uint32_t>(spec[u]);
+      const uint32_t w =
+          (wm & (1u << u)) && idx < static_cast<uint32_t>(kHistMaxCols) ? idx >> 5 : 0u;
+      rw[u] = rank16[w];
+      bw[u] = bits[w];
+    }
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u)
+      if ((wm & (1u << u)) && static_cast<uint32_t>(spec[u]) < static_cast<uint32_t>(kHistMaxCols))
+        put(spec[u], pos_of(static_cast<uint32_t>(spec[u]), rw[u], bw[u]));
+  }
+  if (!listed) {
+    for (uint32_t c = tid; c < c_b; c += kHistThreads) {
+      const uint64_t e = cand_mem(c);
+      const uint32_t idx = static_cast<uint32_t>(e);
+      if (wins(static_cast<uint32_t>(e >> 32), idx, cut) && idx < static_cast<uint32_t>(kHistMaxCols))
+        put(e, pos_of(idx, rank16[idx >> 5], bits[idx >> 5]));
+    }
   }
 }
 
@@ -1391,15 +1479,12 @@ int32_t seg_len_for(int64_t cols, int32_t n_seg) {
 
 hipError_t launch_topk_hist(const HistSelArgs& a, hipStream_t stream) {
   if (a.n_rows <= 0) return hipSuccess;
-  // rows rounded up to a multiple of the XCD count (see the row mapping in the kernel)
-  const int64_t rows8 = (a.n_rows + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid(static_cast<uint32_t>(rows8 * a.n_seg)), block(64 * kHistWaves);
-  if (a.seg_len == 16 * kHistThreads)
-    hipLaunchKernelGGL(topk_hist_kernel<16>, grid, block, 0, stream, a);
-  else if (a.seg_len == 8 * kHistThreads)
-    hipLaunchKernelGGL(topk_hist_kernel<8>, grid, block, 0, stream, a);
-  else
+  if (a.k < 1 || a.k > kMaxTopk || a.cols > kHistMaxCols || a.wg_per_row < 1 ||
+      a.wg_per_row > kMaxHistWgPerRow || a.wg_keys < 1 || a.wg_keys > kHistWgKeysMax ||
+      static_cast<int64_t>(a.wg_per_row) * a.wg_keys < a.cols)
     return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_list_kernel, dim3(static_cast<uint32_t>(a.n_rows)), dim3(kHistThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -42,13 +42,12 @@ def test_page_bytes(L):
 
 
 def test_workspace_sizes(L):
-    # decode batch of 32 queries over 512 pages: visible counts, a row of 32768 fp32 scores each,
-    # then the histogram selection's 16 workgroup histograms of 2048 16-bit bins per row, one
-    # counter per row and a candidate list of 32768 (key, index) pairs per row
-    scores = 256 + 32 * 32768 * 4
+    # decode batch of 32 queries over 512 pages: visible counts, then per row the keys of its 16
+    # scoring workgroups bucketed by histogram bin (32768 (key, index) pairs) and the 16
+    # workgroups' histograms and bucket starts (2048 16-bit bins each)
+    lists = 256 + 32 * 32768 * 8
     hist = 32 * 16 * 2048 * 2
-    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == scores + hist + 256 + \
-        32 * 32768 * 8
+    assert L.idx_logits_topk_workspace_size(32, 32, 512, 1024) == lists + hist + hist
     # 256 such rows go through the segmented two-pass selection: two candidate buffers of
     # 6 segments x k (index, value) pairs per row
     cand = 2 * (256 * 6 * 1024 * 8 + 256)
@@ -72,7 +71,7 @@ def test_chunk_plan_fits_workspace(L):
     """Every query chunk of idx_logits_topk fits the workspace it is given: the planner's row
     bound must cover the segmented selection's candidate buffers, which a batch of more than 128
     long rows needs even where a single row is selected with none, and the histogram selection's
-    histograms and candidate lists (decode-shaped batches)."""
+    histograms, bucket starts and bucketed keys (decode-shaped batches)."""
     for max_pages in (1, 16, 97, 128, 192, 256, 384, 512, 640, 2048):  # 64 .. 131072 key columns
         for k in (512, 1024, 2048):
             mins = ix.min_workspace(1, max_pages, k)
