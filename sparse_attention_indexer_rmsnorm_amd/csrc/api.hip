@@ -56,12 +56,20 @@ bool dtype_ok(int dtype) {
   return dtype == IDX_KV_FP8_E4M3 || dtype == IDX_KV_BF16 || dtype == IDX_KV_FP4_E2M1;
 }
 
-// Decode-shaped chunks (the split scoring kernel) are selected from the per-workgroup histograms
-// and bucketed keys the scoring kernel writes (launch_topk_hist): its workgroups cover 4 chunks
-// of 128, 256 or 512 keys of one row.  Rows of more than kMaxHistWgPerRow such workgroups are
-// selected in segments and passes instead (run_topk).
+// Decode-shaped chunks (the split scoring kernel) are selected with the per-workgroup histograms
+// the scoring kernel writes: its workgroups cover 4 chunks of 128, 256 or 512 keys of one row.
+// Rows of at least kBucketMinCols key columns are selected from the workgroups' keys bucketed by
+// bin (launch_topk_list: the selection reads little more than its winners, at the cost of a
+// sort in every scoring workgroup), shorter ones from the scores in segments (launch_topk_hist:
+// the scoring workgroups only count, and a selection workgroup covers seg_len scores).  Rows of
+// more than kMaxHistWgPerRow such workgroups are selected in segments and passes (run_topk).
+// (Measured, one box: 32 rows of 32768 keys 41.5 -> 39.0 us with the lists (fp8), 64 rows of
+// 1024..5632 keys 25.3 -> 27.4 us.)
+constexpr int32_t kBucketMinCols = 16384;
+
 struct HistPlan {
-  int32_t chunk_keys, n_chunks, wg_per_row;
+  int32_t chunk_keys, n_chunks, wg_per_row, seg_len, n_seg;
+  bool bucket;
 };
 
 void plan_chunks(int64_t n_rows, int32_t n_cols, int32_t* chunk_keys, int32_t* n_chunks);
@@ -79,6 +87,10 @@ HistPlan hist_plan(int64_t rows, int32_t cols) {
     h.chunk_keys = 128;
   h.n_chunks = (cols + h.chunk_keys - 1) / h.chunk_keys;
   h.wg_per_row = (h.n_chunks + kHistChunks - 1) / kHistChunks;
+  const int64_t segs4k = (static_cast<int64_t>(cols) + 4095) / 4096;
+  h.seg_len = rows * segs4k >= 256 ? 4096 : 2048;
+  h.n_seg = (cols + h.seg_len - 1) / h.seg_len;
+  h.bucket = cols >= kBucketMinCols;
   return h;
 }
 
@@ -90,13 +102,15 @@ bool use_hist(int64_t rows, int32_t n_seq, int32_t cols, bool q8) {
 }
 
 // Workspace layout for a chunk of `rows` query rows:
-//   [row_nvis int32 x rows | pad] then either
-//   [scores fp32 rows x cols | pad][selection candidates] (segments and passes), or
-//   [bucketed keys u64 rows x wg_per_row x wg_keys | pad][histograms u16 rows x wg_per_row x
-//    kHistBins | pad][bucket starts u16, the same] (selection from histograms)
+//   [row_nvis int32 x rows | pad] then one of
+//   [scores fp32 rows x cols | pad][selection candidates] (segments and passes);
+//   [scores fp32 rows x cols | pad][histograms u16 rows x wg_per_row x kHistBins | pad]
+//     [row counters int32 x rows | pad][candidates u64 rows x cols] (histograms and scores);
+//   [bucketed keys u64 rows x wg_per_row x wg_keys | pad][histograms | pad][bucket starts u16,
+//     like the histograms] (histograms and bucketed keys)
 struct WsLayout {
-  size_t nvis, scores, topk, list, hist, off, total;
-  bool hist_path;
+  size_t nvis, scores, topk, hist, ctr, cand, list, off, total;
+  bool hist_path, bucket;
 };
 
 WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k, int32_t n_seq, bool q8) {
@@ -104,22 +118,30 @@ WsLayout workspace_layout(int64_t rows, int32_t max_pages, int32_t k, int32_t n_
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
   L.nvis = 0;
   L.hist_path = use_hist(rows, n_seq, static_cast<int32_t>(cols), q8);
+  const HistPlan h = L.hist_path ? hist_plan(rows, static_cast<int32_t>(cols)) : HistPlan{};
+  L.bucket = L.hist_path && h.bucket;
+  const size_t lists = static_cast<size_t>(rows) * h.wg_per_row;
+  if (L.bucket) {
+    L.list = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
+    L.hist = align_up(L.list + lists * kHistChunks * h.chunk_keys * 8);
+    L.off = align_up(L.hist + lists * kHistBins * 2);
+    L.total = L.off + lists * kHistBins * 2;
+    return L;
+  }
+  L.scores = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
+  L.topk = align_up(L.scores + static_cast<size_t>(rows) * cols * sizeof(float));
   if (!L.hist_path) {
-    L.scores = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
-    L.topk = align_up(L.scores + static_cast<size_t>(rows) * cols * sizeof(float));
     L.total = L.topk + topk_workspace_bytes(rows, static_cast<int64_t>(cols), k);
     return L;
   }
-  const HistPlan h = hist_plan(rows, static_cast<int32_t>(cols));
-  const size_t lists = static_cast<size_t>(rows) * h.wg_per_row;
-  L.list = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
-  L.hist = align_up(L.list + lists * kHistChunks * h.chunk_keys * 8);
-  L.off = align_up(L.hist + lists * kHistBins * 2);
-  L.total = L.off + lists * kHistBins * 2;
+  L.hist = L.topk;
+  L.ctr = align_up(L.hist + lists * kHistBins * 2);
+  L.cand = align_up(L.ctr + static_cast<size_t>(rows) * sizeof(int32_t));
+  L.total = L.cand + static_cast<size_t>(rows) * cols * 8;
   return L;
 }
 
-// A bound on workspace_layout(n).total for every n <= rows, every n_seq and both selections,
+// A bound on workspace_layout(n).total for every n <= rows, every n_seq and every selection,
 // that never decreases with `rows`: the exact size is not monotone (a batch of few rows is
 // selected by one workgroup per row with no candidates, more rows in segments with candidate
 // buffers, decode-shaped chunks from histograms), so every row reserves the most any of them
@@ -128,11 +150,14 @@ size_t workspace_upper(int64_t rows, int32_t max_pages, int32_t k) {
   const size_t cols = static_cast<size_t>(max_pages) * IDX_PAGE_KEYS;
   const size_t cand = static_cast<size_t>(topk_cand_bound(static_cast<int64_t>(cols), k));
   const size_t passes_row = cols * sizeof(float) + 2 * cand * 8;
-  // histogram workgroups of kHistChunks chunks of 128 keys at the least; their keys cover the
+  // histogram workgroups of kHistChunks chunks of 128 keys at the least; bucketed keys cover the
   // columns rounded up to one workgroup of the widest chunks
   const size_t wg_max = (cols + kHistChunks * 128 - 1) / (kHistChunks * 128);
-  const size_t hist_row = (cols + kHistWgKeysMax) * 8 + wg_max * kHistBins * 2 * 2;
-  const size_t sel_row = passes_row > hist_row ? passes_row : hist_row;
+  const size_t scores_row = cols * sizeof(float) + wg_max * kHistBins * 2 + sizeof(int32_t) +
+                            cols * 8;
+  const size_t bucket_row = (cols + kHistWgKeysMax) * 8 + wg_max * kHistBins * 2 * 2;
+  size_t sel_row = passes_row > scores_row ? passes_row : scores_row;
+  sel_row = sel_row > bucket_row ? sel_row : bucket_row;
   return static_cast<size_t>(rows) * (sizeof(int32_t) + sel_row) + 6 * kAlign;
 }
 
@@ -229,32 +254,35 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
     const int64_t rows = (n_q - q0 < rows_per_chunk) ? n_q - q0 : rows_per_chunk;
     const WsLayout L = workspace_layout(rows, max_pages, k, n_seq, q8);
     int32_t* nvis = reinterpret_cast<int32_t*>(ws + L.nvis);
-    float* scores = L.hist_path ? nullptr : reinterpret_cast<float*>(ws + L.scores);
+    float* scores = L.bucket ? nullptr : reinterpret_cast<float*>(ws + L.scores);
     sa.q_begin = q0;
     sa.n_rows = rows;
     sa.out = scores;
     sa.row_nvis = nvis;
+    sa.wg_hist = nullptr;
+    sa.row_ctr = nullptr;
+    sa.wg_off = nullptr;
+    sa.wg_list = nullptr;
+    sa.wg_per_row = 0;
+    sa.sel_k = k;
     HistPlan hp{};
     if (L.hist_path) {
       hp = hist_plan(rows, cols);
       sa.chunk_keys = hp.chunk_keys;
       sa.n_chunks = hp.n_chunks;
       sa.wg_per_row = hp.wg_per_row;
-      sa.wg_list = reinterpret_cast<uint64_t*>(ws + L.list);
       sa.wg_hist = reinterpret_cast<uint16_t*>(ws + L.hist);
-      sa.wg_off = reinterpret_cast<uint16_t*>(ws + L.off);
-      sa.sel_k = k;
-    } else {
-      sa.wg_list = nullptr;
-      sa.wg_hist = nullptr;
-      sa.wg_off = nullptr;
-      sa.wg_per_row = 0;
-      if (cols > 0) {
-        plan_chunks(rows, cols, &sa.chunk_keys, &sa.n_chunks);
+      if (L.bucket) {
+        sa.wg_list = reinterpret_cast<uint64_t*>(ws + L.list);
+        sa.wg_off = reinterpret_cast<uint16_t*>(ws + L.off);
       } else {
-        sa.chunk_keys = 32;
-        sa.n_chunks = 1;
+        sa.row_ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
       }
+    } else if (cols > 0) {
+      plan_chunks(rows, cols, &sa.chunk_keys, &sa.n_chunks);
+    } else {
+      sa.chunk_keys = 32;
+      sa.n_chunks = 1;
     }
     if (ev_begin && q0 == 0 && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess)
       return IDX_EHIP;
@@ -262,8 +290,8 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
     if (ev_end && q0 + rows >= n_q &&
         hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
       return IDX_EHIP;
-    if (L.hist_path) {
-      HistSelArgs h{};
+    if (L.bucket) {
+      ListSelArgs h{};
       h.wg_list = sa.wg_list;
       h.wg_hist = sa.wg_hist;
       h.wg_off = sa.wg_off;
@@ -273,6 +301,23 @@ int logits_topk_impl(const void* q, const float* q_scale, const float* w, const 
       h.k = k;
       h.wg_per_row = hp.wg_per_row;
       h.wg_keys = kHistChunks * hp.chunk_keys;
+      h.out_idx = out_idx + q0 * k;
+      h.out_val = out_val ? out_val + q0 * k : nullptr;
+      if (launch_topk_list(h, s) != hipSuccess) return IDX_EHIP;
+    } else if (L.hist_path) {
+      HistSelArgs h{};
+      h.scores = scores;
+      h.cols = cols;
+      h.row_nvis = nvis;
+      h.n_rows = rows;
+      h.k = k;
+      h.wg_hist = sa.wg_hist;
+      h.wg_per_row = hp.wg_per_row;
+      h.wg_keys = kHistChunks * hp.chunk_keys;
+      h.row_ctr = sa.row_ctr;
+      h.n_seg = hp.n_seg;
+      h.seg_len = hp.seg_len;
+      h.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
       h.out_idx = out_idx + q0 * k;
       h.out_val = out_val ? out_val + q0 * k : nullptr;
       if (launch_topk_hist(h, s) != hipSuccess) return IDX_EHIP;

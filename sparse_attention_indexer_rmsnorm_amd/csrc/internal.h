@@ -66,18 +66,22 @@ struct ScoreArgs {
   int32_t* row_nvis;         // [n_rows] visible-key count per row, or null
   const uint8_t* q8;         // fp8 x fp8 scoring: q e4m3 codes [n_q, 64, 128], or null
   const float* q_scale;      // [n_q, 64] scales of q8
-  // Histogram mode of the split kernel (set by the decode-shaped selection): workgroup
+  // Histogram modes of the split kernel (set by the decode-shaped selections): workgroup
   // (row r, j) scores chunks 4j .. 4j + 3 of row r (keys [j * wg_keys, (j + 1) * wg_keys),
-  // wg_keys = 4 * chunk_keys) and writes, for list L = r * wg_per_row + j:
-  //   wg_hist[L * kHistBins + b]  its number of keys in histogram bin b (16-bit counts);
-  //   wg_off[L * kHistBins + b]   its number of keys in bins above b (16-bit);
-  //   wg_list[L * wg_keys + p]    its keys bucketed by bin, highest bin first: the keys of bin b
-  //                               at positions [wg_off[b], wg_off[b] + wg_hist[b]) in no set
-  //                               order, each as (order key << 32 | key index).  When the
-  //                               workgroup holds more than sel_k keys, the bins below its own
-  //                               sel_k-th largest key are counted but their keys not written.
+  // wg_keys = 4 * chunk_keys) and writes a kHistBins-bin histogram of their scores (16-bit
+  // counts) to wg_hist[L * kHistBins ..], L = r * wg_per_row + j.  Then either
+  //   - scores mode (wg_list null): the scores go to out like plain mode, and workgroup (r, 0)
+  //     zeroes row_ctr[r] for the selection; or
+  //   - bucket mode (wg_list set): nothing goes to out; the workgroup writes
+  //       wg_off[L * kHistBins + b]  its number of keys in bins above b (16-bit), and
+  //       wg_list[L * wg_keys + p]   its keys bucketed by bin, highest bin first: the keys of
+  //                                  bin b at positions [wg_off[b], wg_off[b] + count) in no
+  //                                  set order, each as (order key << 32 | key index).  When
+  //                                  the workgroup holds more than sel_k keys, the bins below
+  //                                  its own sel_k-th largest key are counted, not written.
   // Null wg_hist: plain mode (any four work items per workgroup, scores to out).
   uint16_t* wg_hist;
+  int32_t* row_ctr;
   uint16_t* wg_off;
   uint64_t* wg_list;
   int32_t wg_per_row;
@@ -139,12 +143,38 @@ struct TopkPlan {
   int64_t cand_elems;        // widest candidate row between passes
 };
 
-// Selection from the bucketed lists the split kernel writes in histogram mode (few long rows:
-// decode batches), one workgroup per row: the sum of the row's histograms gives the bin B that
-// holds the k-th largest score; every key of a higher bin is a winner and is read from the front
-// of its list, bin B's keys are read from behind them and refined to the exact threshold, and a
-// bitmap of the winners' indices gives each its output position (the output is sorted by index).
+// Selection over a score matrix written by the split kernel in scores mode (few rows of moderate
+// length: decode batches).  Row r is cut into n_seg segments of seg_len scores, one workgroup
+// each; the workgroup sums the row's histograms, finds the bin holding the k-th largest score,
+// and writes the keys of higher bins straight to their output positions (the histograms of the
+// earlier segments give the offset) and the threshold bin's keys to the row's candidate list;
+// the last workgroup of the row to finish refines the candidates to the exact threshold.
 struct HistSelArgs {
+  const float* scores;       // [n_rows, cols]
+  int64_t cols;
+  const int32_t* row_nvis;   // [n_rows] visible keys per row
+  int64_t n_rows;
+  int32_t k;
+  const uint16_t* wg_hist;   // [n_rows, wg_per_row, kHistBins]
+  int32_t wg_per_row;
+  int32_t wg_keys;           // scores per histogram workgroup; divides seg_len
+  int32_t* row_ctr;          // [n_rows], zero on entry
+  int32_t n_seg;
+  int32_t seg_len;           // 2048 or 4096
+  uint64_t* cand;            // [n_rows, cols] (order key << 32 | index), index order
+  int32_t* out_idx;          // [n_rows, k]
+  float* out_val;            // [n_rows, k] or null
+};
+
+hipError_t launch_topk_hist(const HistSelArgs& a, hipStream_t stream);
+
+// Selection from the bucketed lists the split kernel writes in bucket mode (few long rows: long-
+// context decode batches), one workgroup per row: the sum of the row's histograms gives the bin
+// B that holds the k-th largest score; every key of a higher bin is a winner and is read from
+// the front of its list, bin B's keys are read from behind them and refined to the exact
+// threshold, and a bitmap of the winners' indices gives each its output position (the output
+// is sorted by index).
+struct ListSelArgs {
   const uint64_t* wg_list;   // [n_rows, wg_per_row, wg_keys]
   const uint16_t* wg_hist;   // [n_rows, wg_per_row, kHistBins]
   const uint16_t* wg_off;    // [n_rows, wg_per_row, kHistBins]
@@ -158,7 +188,7 @@ struct HistSelArgs {
   float* out_val;            // [n_rows, k] or null
 };
 
-hipError_t launch_topk_hist(const HistSelArgs& a, hipStream_t stream);
+hipError_t launch_topk_list(const ListSelArgs& a, hipStream_t stream);
 
 TopkPlan topk_plan(int64_t n_rows, int64_t cols, int32_t k);
 // Workspace the selection of n_rows rows of `cols` scores needs (0 for one pass).

@@ -307,7 +307,13 @@ __device__ __forceinline__ void load_query(const ScoreArgs& a, int64_t i, Frag (
     for (int rr = 0; rr < 16; ++rr) wv[ht][rr] = wrow[32 * ht + 8 * (rr >> 2) + 4 * g + (rr & 3)];
 }
 
-template <int DT, bool HIST>
+// Modes of the split kernel: scores to out only; scores to out and per-workgroup histograms;
+// histograms and the workgroup's keys bucketed by bin (see ScoreArgs).
+constexpr int kModePlain = 0;
+constexpr int kModeHist = 1;
+constexpr int kModeBucket = 2;
+
+template <int DT, int MODE>
 __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int32_t b, int32_t c_begin,
                                             int32_t s_end, float* out_row, uint32_t* hist,
                                             float* sc, int32_t wg_begin,
@@ -356,12 +362,12 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int32_t b, int32
     const int32_t s = s0 + m;
     const float v = ok_cur ? tot : -INFINITY;
     if (g == 0 && s < s_end) {
-      if constexpr (HIST) {
+      if constexpr (MODE == kModeBucket) {
         sc[s - wg_begin] = v;
-        atomicAdd(&hist[score_order_key(v) >> kHistShift], 1u);
       } else {
         out_row[s] = v;
       }
+      if constexpr (MODE != kModePlain) atomicAdd(&hist[score_order_key(v) >> kHistShift], 1u);
     }
   };
   pid[0] = pg_of(c_begin);
@@ -386,12 +392,14 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, int32_t b, int32
 // banks.
 constexpr int kQRowChunks = kHeadDim * 2 / 16 + 1;   // 17
 
-template <int DT, bool HIST>
+template <int DT, int MODE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  constexpr bool HIST = MODE != kModePlain;
+  constexpr bool BUCKET = MODE == kModeBucket;
   __shared__ __attribute__((aligned(16))) uint32_t hist[HIST ? kHistBins : 1];
   __shared__ __attribute__((aligned(16))) u32x4 qs[HIST ? kHeads * kQRowChunks : 1];
   __shared__ float wsh[HIST ? kHeads : 1];
-  __shared__ float sc[HIST ? kHistWgKeysMax : 1];   // the workgroup's scores, by key
+  __shared__ float sc[BUCKET ? kHistWgKeysMax : 1];   // the workgroup's scores, by key
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t blo_sh;
   const int lane = threadIdx.x & 63;
@@ -400,16 +408,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int64_t r;
   int32_t chunk;
-  int32_t wg_j = 0;   // histogram mode: which of its row's workgroups this is
+  int32_t wg_j = 0;   // histogram modes: which of its row's workgroups this is
   if constexpr (HIST) {
-    // Workgroups go to the 8 XCDs in turn (workgroup b to XCD b % 8): every workgroup of row r
-    // is given to XCD r % 8, the XCD that the selection's workgroup for the row runs on, so
-    // that the row's q is read into one L2 and its buckets are written into the L2 they are
-    // read from.  The grid covers the rows rounded up to a multiple of 8.
-    const int32_t slot = static_cast<int32_t>(blockIdx.x / kXcds);
-    r = static_cast<int64_t>(slot / a.wg_per_row) * kXcds + blockIdx.x % kXcds;
-    wg_j = slot % a.wg_per_row;
-    if (r >= a.n_rows) return;   // the whole workgroup, before any barrier
+    r = blockIdx.x / a.wg_per_row;
+    wg_j = static_cast<int32_t>(blockIdx.x % a.wg_per_row);
     chunk = wg_j * kHistChunks + wid;
   } else {
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + wid;
@@ -479,26 +481,37 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int32_t s_end = static_cast<int32_t>(min<int64_t>(c_end, n_vis));
   // histogram mode: keys [wg_begin, wg_begin + 4 * chunk_keys) of the row are this workgroup's
   const int32_t wg_begin = HIST ? wg_j * kHistChunks * a.chunk_keys : 0;
-  float* out_row = HIST ? nullptr : a.out + r * a.out_stride;
+  float* out_row = BUCKET ? nullptr : a.out + r * a.out_stride;
   if (!HIST && a.fill_invisible) {
     for (int32_t s = max(c_begin, s_end) + lane; s < c_end; s += 64) out_row[s] = -INFINITY;
   }
   if (c_begin < s_end) {
     if (a.n_pages_pool > 0) {
-      score_chunk<DT, HIST>(a, b, c_begin, s_end, out_row, hist, sc, wg_begin, qa, wv);
+      score_chunk<DT, MODE>(a, b, c_begin, s_end, out_row, hist, sc, wg_begin, qa, wv);
     } else {   // no page in the pool: every visible key scores -inf
       for (int32_t s = c_begin + lane; s < s_end; s += 64) {
-        if constexpr (HIST) {
+        if constexpr (BUCKET) {
           sc[s - wg_begin] = -INFINITY;
-          atomicAdd(&hist[score_order_key(-INFINITY) >> kHistShift], 1u);
         } else {
           out_row[s] = -INFINITY;
         }
+        if constexpr (HIST) atomicAdd(&hist[score_order_key(-INFINITY) >> kHistShift], 1u);
       }
     }
   }
 
-  if constexpr (HIST) {
+  if constexpr (MODE == kModeHist) {
+    __syncthreads();
+    // bins 8 t .. 8 t + 7 of thread t as 16-bit counts (at most 4 x 512 scores per workgroup)
+    const u32x4 lo = reinterpret_cast<const u32x4*>(hist)[2 * threadIdx.x];
+    const u32x4 hi = reinterpret_cast<const u32x4*>(hist)[2 * threadIdx.x + 1];
+    const u32x4 packed = {lo.x | (lo.y << 16), lo.z | (lo.w << 16), hi.x | (hi.y << 16),
+                          hi.z | (hi.w << 16)};
+    reinterpret_cast<u32x4*>(a.wg_hist + static_cast<int64_t>(blockIdx.x) * kHistBins)
+        [threadIdx.x] = packed;
+    if (threadIdx.x == 0 && wg_j == 0) a.row_ctr[r] = 0;
+  }
+  if constexpr (BUCKET) {
     // The workgroup's keys, bucketed by histogram bin (a counting sort in LDS): the histogram,
     // then for every bin the number of keys in higher bins (where its bucket starts), then each
     // key to the next free place of its bucket.  The selection reads only the buckets at and
@@ -551,18 +564,30 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         min<int64_t>(min<int64_t>(wg_begin + static_cast<int64_t>(wg_keys), a.n_cols), n_vis);
     const int32_t n_valid = wg_end > wg_begin ? static_cast<int32_t>(wg_end - wg_begin) : 0;
     uint64_t* lst = a.wg_list + list * wg_keys;
+    // every score read, then every bucket place taken, then every store: no LDS round trip
+    // waits on another
+    constexpr int kPer = kHistWgKeysMax / 256;
+    const int32_t upto = (n_valid + 255) / 256;   // groups of 256 keys the workgroup holds
+    uint32_t key[kPer], slot[kPer];
+    bool take[kPer];
 #pragma unroll
-    for (int u = 0; u < kHistWgKeysMax / 256; ++u) {
+    for (int u = 0; u < kPer; ++u) {
       const int32_t el = tid + 256 * u;
-      if (el < n_valid) {
-        const uint32_t key = score_order_key(sc[el]);
-        const uint32_t bin = key >> kHistShift;
-        if (bin >= blo) {
-          const uint32_t slot = atomicAdd(&hist[bin], 1u);
-          if (slot < static_cast<uint32_t>(wg_keys))
-            lst[slot] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(wg_begin + el);
-        }
+      key[u] = 0u;
+      take[u] = false;
+      if (u < upto) {   // uniform
+        key[u] = score_order_key(sc[el]);
+        take[u] = el < n_valid && (key[u] >> kHistShift) >= blo;
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      slot[u] = take[u] ? atomicAdd(&hist[key[u] >> kHistShift], 1u) : 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (take[u] && slot[u] < static_cast<uint32_t>(wg_keys))
+        lst[slot[u]] =
+            (static_cast<uint64_t>(key[u]) << 32) | static_cast<uint32_t>(wg_begin + tid + 256 * u);
     }
   }
 }
@@ -1347,36 +1372,45 @@ hipError_t launch_score_fp8q(const ScoreArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+namespace {
+
+template <int MODE>
+void launch_score_mode(const ScoreArgs& a, int dtype, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  if (dtype == kBf16)
+    hipLaunchKernelGGL((score_kernel<kBf16, MODE>), grid, block, 0, stream, a);
+  else if (dtype == kFp4)
+    hipLaunchKernelGGL((score_kernel<kFp4, MODE>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((score_kernel<kFp8, MODE>), grid, block, 0, stream, a);
+}
+
+}  // namespace
+
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
   int64_t blocks;
+  const bool bucket = a.wg_hist && a.wg_list;
   if (a.wg_hist) {
-    // the workgroup's scores and bucket offsets live in LDS arrays of kHistWgKeysMax keys
-    if (!a.wg_off || !a.wg_list || a.chunk_keys <= 0 ||
-        kHistChunks * a.chunk_keys > kHistWgKeysMax || a.wg_per_row <= 0 || a.sel_k < 1 ||
+    // a histogram workgroup covers 4 chunks of one row; in bucket mode its scores and bucket
+    // starts live in LDS arrays of kHistWgKeysMax keys
+    if (a.chunk_keys <= 0 || kHistChunks * a.chunk_keys > kHistWgKeysMax ||
+        a.wg_per_row <= 0 ||
         static_cast<int64_t>(a.wg_per_row) * kHistChunks * a.chunk_keys < a.n_cols)
       return hipErrorInvalidValue;
-    blocks = (a.n_rows + kXcds - 1) / kXcds * kXcds * a.wg_per_row;
+    if (bucket ? (!a.wg_off || a.sel_k < 1) : (!a.out || !a.row_ctr)) return hipErrorInvalidValue;
+    blocks = a.n_rows * a.wg_per_row;
   } else {
     const int64_t waves = a.n_rows * a.n_chunks;
     blocks = (waves + 3) / 4;
   }
   if (blocks <= 0) return hipSuccess;
-  const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
-  if (a.wg_hist) {
-    if (dtype == kBf16)
-      hipLaunchKernelGGL((score_kernel<kBf16, true>), grid, block, 0, stream, a);
-    else if (dtype == kFp4)
-      hipLaunchKernelGGL((score_kernel<kFp4, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((score_kernel<kFp8, true>), grid, block, 0, stream, a);
-  } else {
-    if (dtype == kBf16)
-      hipLaunchKernelGGL((score_kernel<kBf16, false>), grid, block, 0, stream, a);
-    else if (dtype == kFp4)
-      hipLaunchKernelGGL((score_kernel<kFp4, false>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((score_kernel<kFp8, false>), grid, block, 0, stream, a);
-  }
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (bucket)
+    launch_score_mode<kModeBucket>(a, dtype, grid, stream);
+  else if (a.wg_hist)
+    launch_score_mode<kModeHist>(a, dtype, grid, stream);
+  else
+    launch_score_mode<kModePlain>(a, dtype, grid, stream);
   return hipGetLastError();
 }
 

@@ -950,7 +950,384 @@ __global__ __launch_bounds__(64 * kBlockWaves) void topk_block_kernel(TopkArgs a
   }
 }
 
-// ---- selection from bucketed lists (decode-shaped batches) -------------------------------------
+namespace seg {
+
+// ---- selection from per-workgroup histograms and scores (decode batches of moderate rows) --------
+//
+// Workgroup (row r, segment g) of 256 threads, thread t owning scores e0 .. e0 + PER - 1 of the
+// segment (e0 = g * seg_len + PER t) and histogram bins 8 t .. 8 t + 7:
+//   1. the row's histogram is the sum of its score workgroups' histograms; the bin B holding the
+//      k-th largest score, the count `above` of higher bins and B's count c_B follow from a
+//      descending scan.  The histograms of the score workgroups before this segment give the
+//      numbers of higher-bin and of bin-B keys that precede it in the row;
+//   2. every key of a higher bin is a winner and goes straight to its output position (in index
+//      order, after the winners of earlier segments); bin B's keys go to the row's candidate list
+//      at their position in index order;
+//   3. if bin B's keys all win, they go straight to the output instead and nothing more is
+//      needed; otherwise the row's last workgroup to finish (one atomic counter per row, zeroed
+//      by the score kernel) refines the candidates with two radix passes (11 and 10 bits) to the
+//      exact k-th largest key T and how many keys equal to T are taken, then writes the
+//      candidates above T and the lowest-indexed ones equal to T after the higher-bin winners.
+// The output is deterministic: higher-bin winners in index order, then the threshold bin's.
+// Scanning the whole row for bin B in every workgroup instead (no hand-over) was measured slower:
+// the scan is bound by issuing per-score work, repeated by every workgroup of the row.
+constexpr int kHistWaves = 4;
+constexpr int kHistThreads = 64 * kHistWaves;
+constexpr int kHistCandLds = 4096;     // candidates refined from LDS; more are read from memory
+
+// Exclusive prefixes over the workgroup (thread order) of N counts, and their totals (one pair
+// of barriers for all N).
+template <int N>
+__device__ __forceinline__ void wg_excl_scan(const uint32_t (&v)[N], uint32_t (*red)[kHistWaves],
+                                             int lane, int wid, uint32_t (&pre)[N],
+                                             uint32_t (&tot)[N]) {
+  uint32_t inc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    inc[i] = wave_incl_scan(v[i], 0u, [](uint32_t p, uint32_t q) { return p + q; });
+    if (lane == 63) red[i][wid] = inc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    uint32_t o = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < kHistWaves; ++w) {
+      const uint32_t x = red[i][w];
+      o += w < wid ? x : 0u;
+      t += x;
+    }
+    pre[i] = o + inc[i] - v[i];
+    tot[i] = t;
+  }
+  __syncthreads();   // red is reused by the next scan
+}
+
+template <int PER>
+__global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(HistSelArgs a) {
+  __shared__ uint32_t red[4][kHistWaves];
+  __shared__ uint32_t info[4];
+  __shared__ __attribute__((aligned(16))) uint32_t sub[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint64_t lcand[kHistCandLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroups go to the 8 XCDs in turn (workgroup b to XCD b % 8): every segment of a row is
+  // given to the same XCD, so the row's histograms and scores are read into one L2 and hit there.
+  const int64_t slot = blockIdx.x / kXcds;
+  const int64_t r = (slot / a.n_seg) * kXcds + blockIdx.x % kXcds;
+  const int32_t seg = static_cast<int32_t>(slot % a.n_seg);
+  if (r >= a.n_rows) return;
+  const int32_t k = a.k;
+  const float* row = a.scores + r * a.cols;
+  int32_t* oi = a.out_idx + r * k;
+  float* ov = a.out_val ? a.out_val + r * k : nullptr;
+  const int32_t seg_begin = seg * a.seg_len;
+  const int32_t e0 = seg_begin + PER * tid;
+  if (tid == 0) {   // defined even if no thread finds the threshold bin below
+    info[0] = 0u;
+    info[1] = 0u;
+    info[2] = 0u;
+    info[3] = 0u;
+  }
+  // The row's visible count, its scores and its histograms are requested together: none of the
+  // loads depends on another, so they share one round trip.
+  const int32_t len_raw = a.row_nvis[r];
+
+  // scores of this thread (16-byte loads through a view of the row's columns, rounded up to 4,
+  // which stays inside the workspace; loads wholly past the view read 0, and slots at or past
+  // the visible count are masked below)
+  const __amdgpu_buffer_rsrc_t view = buffer_view(row, static_cast<int32_t>((a.cols + 3) & ~3));
+  uint32_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; j += 4) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  view, (e0 + j) * 4, 0, 0));
+    key[j] = v.x;
+    key[j + 1] = v.y;
+    key[j + 2] = v.z;
+    key[j + 3] = v.w;
+  }
+
+  // 1. the row's histogram (bins 8 t .. 8 t + 7 here), and its part before this segment
+  uint32_t tot[8], prev[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) tot[b] = prev[b] = 0u;
+  const int32_t w0 = seg * (a.seg_len / a.wg_keys);
+  const uint16_t* hrow = a.wg_hist + r * static_cast<int64_t>(a.wg_per_row) * kHistBins + 8 * tid;
+  // 16 histograms per round, all requested before the first is summed
+  for (int32_t wr = 0; wr < a.wg_per_row; wr += 16) {
+    u32x4 h[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      h[q] = wr + q < a.wg_per_row
+                 ? *reinterpret_cast<const u32x4*>(hrow + static_cast<int64_t>(wr + q) * kHistBins)
+                 : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t c[8] = {h[q].x & 0xFFFFu, h[q].x >> 16, h[q].y & 0xFFFFu, h[q].y >> 16,
+                             h[q].z & 0xFFFFu, h[q].z >> 16, h[q].w & 0xFFFFu, h[q].w >> 16};
+      const bool before = wr + q < w0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        tot[b] += c[b];
+        prev[b] += before ? c[b] : 0u;
+      }
+    }
+  }
+
+  const int64_t len = len_raw < 0 ? 0 : (len_raw > a.cols ? a.cols : len_raw);
+  const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(len));
+  if (n <= k) {   // every visible key is selected, then padding
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      if (e < n) {
+        oi[e] = e;
+        if (ov) ov[e] = key_value(score_order_key(__uint_as_float(key[j])));
+      }
+    }
+    if (seg == 0)
+      for (int32_t e = n + tid; e < k; e += kHistThreads) {
+        oi[e] = -1;
+        if (ov) ov[e] = -INFINITY;
+      }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    key[j] = e0 + j < n ? score_order_key(__uint_as_float(key[j])) : 0u;
+
+  // descending scan: thread t's bins lie above those of every lower thread
+  uint32_t mine = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) mine += tot[b];
+  {
+    const uint32_t incl = wave_incl_scan(mine, 0u, [](uint32_t p, uint32_t q) { return p + q; });
+    if (lane == 63) red[0][wid] = incl;
+    __syncthreads();
+    uint32_t higher = lane_value(incl, 63) - incl;      // later lanes of this wave
+#pragma unroll
+    for (int w = 0; w < kHistWaves; ++w)
+      if (w > wid) higher += red[0][w];
+    if (higher < static_cast<uint32_t>(k) && higher + mine >= static_cast<uint32_t>(k)) {
+      uint32_t acc = higher;
+#pragma unroll
+      for (int b = 7; b >= 0; --b) {
+        if (acc < static_cast<uint32_t>(k) && acc + tot[b] >= static_cast<uint32_t>(k)) {
+          info[0] = 8 * tid + b;
+          info[1] = acc;
+          info[2] = tot[b];
+        }
+        acc += tot[b];
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t B = info[0];
+  const uint32_t above = min(info[1], static_cast<uint32_t>(k));
+  const uint32_t c_b = min(info[2], static_cast<uint32_t>(n));
+  const uint32_t k_rem = static_cast<uint32_t>(k) - above;   // 1 <= k_rem <= c_b
+  const bool all_win = c_b == k_rem;
+  // Every store below is also bounded by its array (k outputs), whatever the counts: they agree
+  // with the scores by construction (the scoring kernel counted exactly the values it wrote),
+  // and the bounds only keep a broken invariant from writing out of range.
+
+  // 2. higher-bin winners (and, when bin B wins whole, its keys) of this segment
+  uint32_t p_hi = 0, p_eq = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint32_t bin = 8 * tid + b;
+    p_hi += bin > B ? prev[b] : 0u;
+    p_eq += bin == B ? prev[b] : 0u;
+  }
+  uint32_t n_hi = 0, n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t bin = key[j] >> kHistShift;
+    n_hi += (e0 + j < n && bin > B) ? 1u : 0u;
+    n_eq += (e0 + j < n && bin == B) ? 1u : 0u;
+  }
+  uint32_t sc_pre[4], sc_tot[4];
+  wg_excl_scan<4>({p_hi, p_eq, n_hi, n_eq}, red, lane, wid, sc_pre, sc_tot);
+  uint64_t* cand = a.cand + r * a.cols;
+  // before this segment (totals of the earlier histograms' counts), then this thread's place
+  const uint32_t hi0 = sc_tot[0] + sc_pre[2];
+  const uint32_t eq0 = sc_tot[1] + sc_pre[3];
+  if (all_win) {
+    uint32_t at_hi = hi0, at_eq = eq0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      const uint32_t bin = key[j] >> kHistShift;
+      const bool hi = e < n && bin > B;
+      const bool eq = e < n && bin == B;
+      if (hi && at_hi < above) {
+        oi[at_hi] = e;
+        if (ov) ov[at_hi] = key_value(key[j]);
+      }
+      if (eq && above + at_eq < static_cast<uint32_t>(k)) {
+        oi[above + at_eq] = e;
+        if (ov) ov[above + at_eq] = key_value(key[j]);
+      }
+      at_hi += hi ? 1u : 0u;
+      at_eq += eq ? 1u : 0u;
+    }
+    return;
+  }
+
+  // A row of one segment is this workgroup's alone: its candidates go to the LDS list, in
+  // index order, and the refinement below starts at once (c_b <= seg_len <= kHistCandLds).
+  const bool local = a.n_seg == 1;
+  if (local) {
+    uint32_t at_eq = eq0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      const bool eq = e < n && (key[j] >> kHistShift) == B;
+      if (eq && at_eq < c_b)
+        lcand[at_eq] = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(e);
+      at_eq += eq ? 1u : 0u;
+    }
+  }
+  // else bin B's keys to the row's candidate list, which the row's last workgroup refines (3.)
+  if (!local) {
+    uint32_t at_eq = eq0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      const bool eq = e < n && (key[j] >> kHistShift) == B;
+      if (eq && at_eq < c_b) {
+        // an agent-scope store writes through to where every XCD's loads of it look
+        __hip_atomic_store(cand + at_eq,
+                           (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(e),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      at_eq += eq ? 1u : 0u;
+    }
+  }
+
+  // 3. the row's last workgroup refines the threshold bin.  The hand-over needs no cache-wide
+  //    write-back or invalidation (an agent-scope fence is both, on every XCD's L2): the
+  //    candidates were stored with agent-scope atomic stores, each thread waits until its stores
+  //    are acknowledged before the barrier, the counter is an agent-scope atomic, and the last
+  //    workgroup reads the candidates with agent-scope atomic loads issued after the counter
+  //    returned.  The segment's higher-bin winners are stored after the counter is requested,
+  //    as a fixed number of buffer stores (a key that is not one writes past the output view,
+  //    which drops the store): the wait for the counter's value then leaves them in flight,
+  //    and they hold up neither the hand-over nor the workgroups that are not last.
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  int32_t ticket = a.n_seg - 1;   // a local row's workgroup is its last
+  if (tid == 0 && !local)
+    ticket = __hip_atomic_fetch_add(a.row_ctr + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {
+    const __amdgpu_buffer_rsrc_t vi = buffer_view(reinterpret_cast<const float*>(oi), k);
+    const __amdgpu_buffer_rsrc_t vv = buffer_view(ov, ov ? k : 0);
+    constexpr uint32_t kDrop = 0x40800000u;   // past every output view (k <= 2048 values)
+    uint32_t at_hi = hi0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = e0 + j;
+      const bool hi = e < n && (key[j] >> kHistShift) > B;
+      const uint32_t at = (hi && at_hi < above) ? 4u * at_hi : kDrop;
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(e), vi, at, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key[j])), vv, at, 0, 0);
+      at_hi += hi ? 1u : 0u;
+    }
+  }
+  if (tid == 0) info[3] = static_cast<uint32_t>(ticket);
+  // LDS-only barrier: the winner stores stay in flight
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (info[3] != static_cast<uint32_t>(a.n_seg - 1)) return;
+
+  auto load_cand = [&](uint32_t c) {
+    return __hip_atomic_load(cand + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  const bool listed = c_b <= static_cast<uint32_t>(kHistCandLds);
+  if (listed && !local) {
+    for (uint32_t c = tid; c < c_b; c += kHistThreads) lcand[c] = load_cand(c);
+    __syncthreads();
+  }
+  auto cand_at = [&](uint32_t c) { return listed ? lcand[c] : load_cand(c); };
+  // pass 1: bits 20..10 of the keys of bin B; pass 2: bits 9..0 of those in the chosen digit
+  uint32_t want = k_rem;
+  uint32_t prefix = B;
+  uint32_t T = 0u, eq_take = 0u;
+  bool resolved = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const int width = pass == 0 ? 11 : 10;
+    const int nb = 1 << width;
+    for (int c = tid; c < nb; c += kHistThreads) sub[c] = 0u;
+    __syncthreads();
+    for (uint32_t c = tid; c < c_b; c += kHistThreads) {
+      const uint32_t kk = static_cast<uint32_t>(cand_at(c) >> 32);
+      if ((kk >> (shift + width)) == prefix) atomicAdd(&sub[(kk >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t d, gt, cnt;
+    if (pass == 0)
+      wave_find_bin32<2048>(sub, want, lane, &d, &gt, &cnt);
+    else
+      wave_find_bin32<1024>(sub, want, lane, &d, &gt, &cnt);
+    prefix = (prefix << width) | d;
+    want -= gt;
+    __syncthreads();   // sub is cleared again by the next pass
+    // Every key of the chosen digit is taken (the usual case: bin B's few hundred keys spread
+    // over 2048 digits): the winners are the keys whose top 21 bits are at least `prefix`, i.e.
+    // the keys above T = (prefix << 10) - 1 with no tie taken, and the second pass is not needed.
+    // (cnt and want come from the same LDS counts in every wave, so the exit is uniform; a zero
+    // prefix, only reachable by NaN keys, keeps the second pass.)
+    if (pass == 0 && cnt == want && prefix != 0u) {
+      T = (prefix << 10) - 1u;
+      eq_take = 0u;
+      resolved = true;
+      break;
+    }
+  }
+  if (!resolved) {
+    T = prefix;
+    eq_take = want;
+  }
+
+  // candidates above T, then the lowest-indexed ones equal to T, after the higher-bin winners:
+  // thread t visits a contiguous slice of the (index-ordered) list
+  const uint32_t per_t = (c_b + kHistThreads - 1) / kHistThreads;
+  const uint32_t c_lo = min(c_b, per_t * tid), c_hi = min(c_b, c_lo + per_t);
+  uint32_t m_gt = 0, m_eq = 0;
+  for (uint32_t c = c_lo; c < c_hi; ++c) {
+    const uint32_t kk = static_cast<uint32_t>(cand_at(c) >> 32);
+    m_gt += kk > T ? 1u : 0u;
+    m_eq += kk == T ? 1u : 0u;
+  }
+  uint32_t o_pre[2], o_tot[2];
+  wg_excl_scan<2>({m_gt, m_eq}, red, lane, wid, o_pre, o_tot);
+  uint32_t g_before = o_pre[0], e_before = o_pre[1];
+  for (uint32_t c = c_lo; c < c_hi; ++c) {
+    const uint64_t ce = cand_at(c);
+    const uint32_t kk = static_cast<uint32_t>(ce >> 32);
+    uint32_t pos = 0xFFFFFFFFu;
+    if (kk > T) pos = g_before + min(e_before, eq_take);
+    else if (kk == T && e_before < eq_take) pos = g_before + e_before;
+    if (pos < k_rem) {
+      oi[above + pos] = static_cast<int32_t>(static_cast<uint32_t>(ce));
+      if (ov) ov[above + pos] = key_value(kk);
+    }
+    g_before += kk > T ? 1u : 0u;
+    e_before += kk == T ? 1u : 0u;
+  }
+}
+
+}  // namespace seg
+
+namespace lst {
+
+// ---- selection from bucketed lists (decode batches of long rows) --------------------------------
 //
 // One workgroup of 1024 threads per row.  The scoring kernel left, for each of its workgroups j
 // of the row, a histogram of the order keys' top 11 bits, the start of every bin's bucket, and
@@ -1028,7 +1405,7 @@ __device__ __forceinline__ void lists_of(const uint32_t* off, int n, const uint3
   }
 }
 
-__global__ __launch_bounds__(kHistThreads) void topk_list_kernel(HistSelArgs a) {
+__global__ __launch_bounds__(kHistThreads) void topk_list_kernel(ListSelArgs a) {
   __shared__ uint32_t red[4][kHistWaves];
   __shared__ uint32_t info[8];
   __shared__ __attribute__((aligned(16))) uint32_t hist_l[kHistBins];   // the row's histogram
@@ -1410,6 +1787,8 @@ __global__ __launch_bounds__(kHistThreads) void topk_list_kernel(HistSelArgs a) 
   }
 }
 
+}  // namespace lst
+
 bool use_block(int64_t n_rows, int64_t cols) {
   return n_rows <= kBlockRowsMax && cols <= static_cast<int64_t>(kBlockWaves) * 64 * kBlockMaxE;
 }
@@ -1479,11 +1858,25 @@ int32_t seg_len_for(int64_t cols, int32_t n_seg) {
 
 hipError_t launch_topk_hist(const HistSelArgs& a, hipStream_t stream) {
   if (a.n_rows <= 0) return hipSuccess;
+  // rows rounded up to a multiple of the XCD count (see the row mapping in the kernel)
+  const int64_t rows8 = (a.n_rows + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid(static_cast<uint32_t>(rows8 * a.n_seg)), block(64 * seg::kHistWaves);
+  if (a.seg_len == 16 * seg::kHistThreads)
+    hipLaunchKernelGGL(seg::topk_hist_kernel<16>, grid, block, 0, stream, a);
+  else if (a.seg_len == 8 * seg::kHistThreads)
+    hipLaunchKernelGGL(seg::topk_hist_kernel<8>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_list(const ListSelArgs& a, hipStream_t stream) {
+  if (a.n_rows <= 0) return hipSuccess;
   if (a.k < 1 || a.k > kMaxTopk || a.cols > kHistMaxCols || a.wg_per_row < 1 ||
       a.wg_per_row > kMaxHistWgPerRow || a.wg_keys < 1 || a.wg_keys > kHistWgKeysMax ||
       static_cast<int64_t>(a.wg_per_row) * a.wg_keys < a.cols)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_list_kernel, dim3(static_cast<uint32_t>(a.n_rows)), dim3(kHistThreads), 0,
+  hipLaunchKernelGGL(lst::topk_list_kernel, dim3(static_cast<uint32_t>(a.n_rows)), dim3(lst::kHistThreads), 0,
                      stream, a);
   return hipGetLastError();
 }

@@ -182,6 +182,34 @@ def test_decode_selection_matches_dense_then_select(dtype, k):
     assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
 
 
+@pytest.mark.parametrize("dtype,k", [(FP8, 64), (BF16, 512), (FP8, 1024), (BF16, 2048)])
+def test_long_row_selection_matches_dense_then_select(dtype, k):
+    """Rows of more than 16384 key columns, which are selected from each scoring workgroup's keys
+    bucketed by histogram bin: the front of every list, or, when the threshold bin reaches past
+    it (small k), the lists read in full.  Ragged rows up to 37,500 keys, rows shorter than k and
+    just above it, and keys on an invalid page included; the result must equal the selection
+    over the dense logits, bit for bit."""
+    r = np.random.default_rng(90 + k)
+    lens = r.integers(8, 150000, 12).astype(np.int32)
+    lens[:3] = [12, 4 * k - 4, 4 * k + 8]             # n_vis < k, just below and above k
+    lens[3] = 150000
+    wl = W.make_workload("decode-long-ragged", 91 + k, lens, np.ones(lens.size, np.int32), k,
+                         permute_pages=True, max_pages=600)
+    wl.page_table[3, 40] = wl.n_pages_pool + 7          # keys 2560..2623 of row 3 score -inf
+    d = dev_inputs(wl)
+    pool = gpu_store(ix, wl, dtype, d)
+    gi, gv = _gpu_topk(wl, d, pool, dtype, want_values=True)
+    dense = ix.logits_dense(d["q"], d["w"], pool, dtype, d["page_table"], d["seq_lens"],
+                            d["cu_q"], wl.max_keys)
+    t = query_positions(wl)
+    nv = torch.from_numpy(np.minimum((t + 1) // 4, wl.max_keys).astype(np.int32)).cuda()
+    si, sv = ix.topk_rows(dense, wl.k, nv)
+    gi, gv = by_index(gi, gv)
+    si, sv = by_index(si, sv)
+    assert torch.equal(gi, si)
+    assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
+
+
 @pytest.mark.parametrize("budget", ["min", 4 << 20, 11 << 20, "recommended"])
 def test_workspace_guard_bytes(budget):
     """More than 128 rows of more than 6144 keys go through the segmented selection, whose
