@@ -535,7 +535,10 @@ def main() -> int:
     # the bench's workload name (it names the cache dtype; the headline's equals wl.name)
     name = args.workload + ("-rotated" if args.rotate else "") + ("-fp8q" if args.fp8q else "")
     roof["traffic"] = committed_traffic(kernel, name)
-    roof["kernel"] = kernel + (" + topk_list_kernel" if decode and not args.fp8q else "")
+    # decode rows of at least 16384 key columns are selected from bucketed keys, shorter ones from
+    # the scores in segments
+    sel = "topk_list_kernel" if wl.max_pages * 64 >= 16384 else "topk_hist_kernel"
+    roof["kernel"] = kernel + (" + " + sel if decode and not args.fp8q else "")
 
     line = {
         "metric": "indexer keys scored/s (top-k queries/s alongside)",
