@@ -85,3 +85,48 @@ def test_multiseq_topk(oracle_mod, dtype, k):
     assert torch.equal(gi, si)
     assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
     assert (nv < wl.k).any() and (nv > wl.k).any()        # padded and selected rows both occur
+
+
+@pytest.mark.parametrize("k,want_values", [(512, False), (2048, True), (1, True), (100, False)])
+def test_prefill_selection_ties_match_dense_then_select(k, want_values):
+    """Prefill-shaped bf16 batches go through the rows scoring kernel and the whole-row
+    selection (one wave per row).  Rows whose scores tie massively (a sequence of all-zero keys:
+    every score 0, so the threshold bin holds the whole row, more than a wave lists in LDS; a
+    sequence whose keys take three values), rows shorter than k, rows that see no key and long
+    plain rows (5632 keys) must give the selection made over the dense logits, bit for bit, with
+    and without values, for k from 1 to 2048."""
+    seq_lens = [22528, 3000, 2500, 900, 40, 12000]
+    q_lens = [420, 250, 301, 151, 9, 110]           # 1241 rows
+    wl = W.make_workload("prefill-ties", 640 + k, seq_lens, q_lens, k, permute_pages=True,
+                         extra_pages=2, dtypes=(BF16,))
+    assert wl.n_q >= 1024 and wl.n_q >= 4 * wl.n_seq and wl.max_keys <= 6144
+    x = wl.x.copy()
+    x[wl.key_seq == 1] = 0.0
+    rows2 = np.nonzero(wl.key_seq == 2)[0]
+    x[rows2] = x[rows2[np.arange(rows2.size) % 3]]
+    x[rows2, 64:] = 0.0
+    d = dev_inputs(wl, x)
+    pool = gpu_store(ix, wl, BF16, d)
+    gi, gv = ix.logits_topk(d["q"], d["w"], pool, BF16, d["page_table"], d["seq_lens"],
+                            d["cu_q"], wl.k, want_values=want_values)
+    assert (gv is not None) == want_values
+    dense = ix.logits_dense(d["q"], d["w"], pool, BF16, d["page_table"], d["seq_lens"],
+                            d["cu_q"], wl.max_keys)
+    t = query_positions(wl)
+    nvis = torch.from_numpy(np.minimum((t + 1) // 4, wl.max_keys).astype(np.int32)).cuda()
+    si, sv = ix.topk_rows(dense, wl.k, nvis)
+    si, sv = by_index(si, sv)
+    if want_values:
+        gi, gv = by_index(gi, gv)
+        assert torch.equal(gv.view(torch.int32), sv.view(torch.int32))
+    else:
+        gi = by_index(gi)
+    assert torch.equal(gi, si)
+    # sequence 1 scores 0 everywhere: its rows take their first k keys (ties to the lower index)
+    r1 = np.nonzero((np.arange(wl.n_q) >= wl.cu_q[1]) & (np.arange(wl.n_q) < wl.cu_q[2]))[0]
+    nv1 = nvis[torch.from_numpy(r1).cuda()].cpu().numpy()
+    full = r1[nv1 >= k]
+    assert full.size > 0 or k > nv1.max()
+    if full.size:
+        want = torch.arange(k, dtype=torch.int32).expand(full.size, k)
+        assert torch.equal(gi[torch.from_numpy(full).cuda(), :k].cpu(), want)
