@@ -162,3 +162,32 @@ def test_store_repeatable():
     a = gpu_store(ix, wl, FP8, d)
     b = gpu_store(ix, wl, FP8, d)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,rotate", [(FP8, False), (BF16, False), (W.FP4, False),
+                                          (FP8, True)])
+def test_store_far_positions(oracle_mod, dtype, rotate):
+    """Keys at positions that reach every part of the RoPE angle (key index s = m0 + 256 m1 +
+    65536 m2, each part's cosine and sine combined by angle addition) and past 2^24 keys (the
+    direct sincos): the boundaries of every part, and 3000 keys spread up to 2^24 + 2^15, stored
+    bit-identical to the oracle's cos and sin of the whole angle."""
+    r = np.random.default_rng([77, dtype, int(rotate)])
+    edges = [0, 1, 2, 255, 256, 257, 511, 65535, 65536, 65537, 131071, 1 << 20, (1 << 20) + 77,
+             (1 << 23) + 5, (1 << 24) - 1, 1 << 24, (1 << 24) + 1, (1 << 24) + 300]
+    key_idx = np.unique(np.concatenate([edges, r.integers(0, (1 << 24) + (1 << 15), 3000)]))
+    key_idx = key_idx.astype(np.int32)
+    max_pages = ((1 << 24) + (1 << 15)) // 64
+    pages = np.unique(key_idx // 64)
+    pt = np.full((1, max_pages), -1, np.int32)
+    pt[0, pages] = r.permutation(pages.size).astype(np.int32)
+    x = (r.standard_normal((key_idx.size, 128)) * r.choice([1e-2, 1.0, 30.0],
+                                                           (key_idx.size, 1))).astype(np.float32)
+    gamma = (1 + 0.1 * r.standard_normal(128)).astype(np.float32)
+    dev = "cuda"
+    pool = ix.new_cache(pages.size, dtype)
+    ix.store_keys(torch.from_numpy(x).to(dev), torch.from_numpy(gamma).to(dev),
+                  torch.from_numpy(key_idx).to(dev), torch.from_numpy(pt).to(dev), pool, dtype,
+                  eps=1e-6, rotate=rotate)
+    pool_o = oracle_mod.new_pool(pages.size, dtype)
+    oracle_mod.store_keys(x, gamma, 1e-6, key_idx, None, pt, dtype, pool_o, hadamard=rotate)
+    _compare(pool.cpu().numpy(), pool_o, dtype, f"far positions dtype={dtype} rotate={rotate}")
