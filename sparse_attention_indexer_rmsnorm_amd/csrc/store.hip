@@ -36,35 +36,33 @@ __device__ __forceinline__ double fma_const(double a, double b, double c) {
 
 // cos and sin of a RoPE angle th = 4 s f_j, exact in fp64 (0 <= th < 2^26 rad for s < 2^24):
 // Cody-Waite reduction by pi/2 (th - n pi/2 with pi/2 split into two 27-bit parts, whose
-// products with n < 2^26 are exact, and a 53-bit third), then the Taylor polynomials of sin and
-// cos to degree 17 and 18 on [-pi/4, pi/4] (the first omitted term is below 2^-62 of the result)
-// and the quadrant n mod 4.  The result is within about 2 ulp of the exact cosine and sine.
+// products with n < 2^26 are exact, and a 53-bit third), then polynomials in z = r^2 on
+// [-pi/4, pi/4] and the quadrant n mod 4.  The polynomials interpolate (sin r - r) / r^3 and
+// (cos r - 1) / z at Chebyshev nodes on [0, (pi/4)^2], solved in 80-digit arithmetic
+// (rope_poly.py): near-minimax, their error is below 2^-56 of r and 2^-62 respectively.  The
+// result is within about 2 ulp of the exact cosine and sine.
 __device__ __forceinline__ void rope_sincos(double th, double* sn, double* cs) {
   const double n = __builtin_rint(th * 0x1.45f306dc9c883p-1);   // th * 2/pi
   double r = fma(-n, 0x1.921fb54000000p+0, th);
   r = fma(-n, 0x1.10b4610000000p-30, r);
   r = fma(-n, 0x1.a62633145c06ep-58, r);
   const double z = r * r;
-  // sin r = r + r^3 P(z), P(z) = sum_k (-1)^(k+1) z^(k-1) / (2k+1)!, k = 1..8
-  double ps = 0x1.952c77030ad4ap-49;          // 1/17!
-  ps = fma_const(ps, z, -0x1.ae7f3e733b81fp-41);    // 1/15!
-  ps = fma_const(ps, z, 0x1.6124613a86d09p-33);     // 1/13!
-  ps = fma_const(ps, z, -0x1.ae64567f544e4p-26);    // 1/11!
-  ps = fma_const(ps, z, 0x1.71de3a556c734p-19);     // 1/9!
-  ps = fma_const(ps, z, -0x1.a01a01a01a01ap-13);    // 1/7!
-  ps = fma_const(ps, z, 0x1.1111111111111p-7);      // 1/5!
-  ps = fma_const(ps, z, -0x1.5555555555555p-3);     // 1/3!
+  // sin r = r + r^3 P(z)
+  double ps = 0x1.5e0b19f8b1451p-33;
+  ps = fma_const(ps, z, -0x1.ae600b02b6262p-26);
+  ps = fma_const(ps, z, 0x1.71de37968a100p-19);
+  ps = fma_const(ps, z, -0x1.a01a019e83aaep-13);
+  ps = fma_const(ps, z, 0x1.1111111110bb2p-7);
+  ps = fma_const(ps, z, -0x1.5555555555555p-3);
   const double sr = fma(r * z, ps, r);
-  // cos r = 1 + z Q(z), Q(z) = sum_k (-1)^k z^(k-1) / (2k)!, k = 1..9
-  double pc = -0x1.6827863b97d97p-53;         // 1/18!
-  pc = fma_const(pc, z, 0x1.ae7f3e733b81fp-45);     // 1/16!
-  pc = fma_const(pc, z, -0x1.93974a8c07c9dp-37);    // 1/14!
-  pc = fma_const(pc, z, 0x1.1eed8eff8d898p-29);     // 1/12!
-  pc = fma_const(pc, z, -0x1.27e4fb7789f5cp-22);    // 1/10!
-  pc = fma_const(pc, z, 0x1.a01a01a01a01ap-16);     // 1/8!
-  pc = fma_const(pc, z, -0x1.6c16c16c16c17p-10);    // 1/6!
-  pc = fma_const(pc, z, 0x1.5555555555555p-5);      // 1/4!
-  pc = fma_const(pc, z, -0x1.0000000000000p-1);     // 1/2!
+  // cos r = 1 + z Q(z)
+  double pc = -0x1.8ff9d439a204ap-37;
+  pc = fma_const(pc, z, 0x1.1eea7f259b344p-29);
+  pc = fma_const(pc, z, -0x1.27e4f8e4a2e74p-22);
+  pc = fma_const(pc, z, 0x1.a01a019de131fp-16);
+  pc = fma_const(pc, z, -0x1.6c16c16c15d79p-10);
+  pc = fma_const(pc, z, 0x1.5555555555551p-5);
+  pc = fma_const(pc, z, -0x1.0000000000000p-1);
   const double cr = fma(z, pc, 1.0);
   // th = n pi/2 + r: (sin, cos) th = (s, c), (c, -s), (-s, -c), (-c, s) for n = 0, 1, 2, 3 mod 4
   const int q = static_cast<int>(n) & 3;
